@@ -1,0 +1,168 @@
+/*
+ * attn.h - softmax attention with online (flash) softmax for AMD Instinct MI355X (gfx950).
+ *
+ * C ABI of libattn.so.  Every pointer argument named q, k, v, o, *_pages, *_scales,
+ * page_table, kv_lens and workspace is a DEVICE pointer; every call is asynchronous on
+ * `stream` (a hipStream_t; NULL means the null stream) and returns as soon as the kernels
+ * are queued.
+ *
+ * Problem statement.  The arguments follow the attention parameter block of
+ * doppler (@simulatte/doppler 0.1.9->0.2.0, gpu/kernels/attention.js,
+ * createAttentionUniformBuffer / executeAttention): numHeads, numKVHeads, headDim, kvLen,
+ * seqLen, scale, causal, attnSoftcap, slidingWindow, pageSize, a page table and a
+ * device-side kv length.  For one query row i at absolute position p_i, query head h,
+ * KV head kvh = h / (num_heads / num_kv_heads) (contiguous groups):
+ *
+ *     visible(j)  =  j < kv_len  and  (!causal or j <= p_i)  and  (W == 0 or p_i - j < W)
+ *     s_j         =  scale * <q_i, k_j>;   if attn_softcap > 0:  s_j = c * tanh(s_j / c)
+ *     o_i         =  sum_{visible j} exp(s_j - m) v_j  /  sum_{visible j} exp(s_j - m)
+ *
+ * with m the row maximum.  A window of W keys includes the query's own position (doppler
+ * run.js 0.1.0 clips kvLen to the window and sets kvStart = total - kvLen).  W = 0 and
+ * c = 0 disable the window and the cap ("0 = disabled").  A row that sees no key cannot
+ * occur for in-contract arguments; it would be written as zeros.
+ *
+ * Ownership.  All buffers are owned by the caller.  The library allocates nothing, frees
+ * nothing, never synchronises and keeps no pointer after returning.  The caller keeps
+ * every buffer alive until the queued work has completed on `stream`.
+ *
+ * Errors.  Each entry point returns ATTN_OK (0) or a negative attn_status.  Argument
+ * errors are detected on the host BEFORE any HIP call, so nothing is queued and no output
+ * is touched.  ATTN_ERR_LAUNCH reports a failed kernel launch (hipGetLastError).  A
+ * message for the last failure of the calling thread is returned by attn_last_error().
+ * Faults during kernel execution surface at the caller's next synchronisation.
+ *
+ * Threading.  Re-entrant: the only mutable library state is thread-local (the error
+ * string and the decode split override).  Concurrent calls on different streams must
+ * use different workspaces.
+ */
+#ifndef TA03_ATTN_H
+#define TA03_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    ATTN_OK = 0,
+    ATTN_ERR_INVALID_ARG = -1,   /* null/misaligned pointer, inconsistent sizes, bad value */
+    ATTN_ERR_UNSUPPORTED = -2,   /* valid attention, but not a head_dim/dtype built here   */
+    ATTN_ERR_WORKSPACE = -3,     /* workspace missing or smaller than required             */
+    ATTN_ERR_LAUNCH = -4         /* the HIP runtime refused the launch                     */
+} attn_status;
+
+typedef enum {
+    ATTN_F32 = 0,                /* q, k, v, o in float32                                  */
+    ATTN_F16 = 1                 /* q, k, v, o in IEEE float16                             */
+} attn_dtype;
+
+/*
+ * Causal / sliding-window / bidirectional prefill with grouped KV heads and an optional
+ * logit softcap (doppler attention.js, executeAttention with seqLen > 1; the tiled
+ * prefill variants prefill, prefill_f16).
+ *
+ *   q, o : [seq_len, num_heads, head_dim]        token-major, dtype (doppler run.js:
+ *   k, v : [kv_len, num_kv_heads, head_dim]      Q is [numTokens, numHeads*headDim], the
+ *                                                cache is [kvLen, numKVHeads*headDim])
+ *   Query row i sits at absolute position kv_len - seq_len + i (startPos = kvLen - seqLen).
+ *   causal          : 0 or 1
+ *   sliding_window  : W >= 0 keys including the query's own position; 0 = off
+ *   attn_softcap    : c >= 0, finite; 0 = off
+ *   scale           : finite, > 0 (doppler: 1/sqrt(headDim) or 1/sqrt(queryPreAttnScalar))
+ *   head_dim        : 64, 128 or 256 (others: ATTN_ERR_UNSUPPORTED)
+ *   Requires 1 <= seq_len <= kv_len, num_heads % num_kv_heads == 0, 16-byte aligned
+ *   pointers.  f32 accumulation; the output is written in `dtype`.
+ */
+int attn_prefill(const void *q, const void *k, const void *v, void *o, int dtype,
+                 int seq_len, int kv_len, int num_heads, int num_kv_heads, int head_dim,
+                 int causal, int sliding_window, float attn_softcap, float scale,
+                 void *stream);
+
+/*
+ * Bidirectional vision-tower self-attention (rullama 0.5.0, src/backend/dispatch/
+ * attention.rs, vision_attention_chained and the head-major flash variant
+ * vision_attention_flash_sub_hpd_chained): no mask, every patch sees every patch.
+ *
+ *   q, k, v, o : float16 [num_heads, num_patches, head_dim]   (head-major, "HPD")
+ *   head_dim   : 64, 128 or 256;  num_patches >= 1;  scale finite > 0.
+ *   f32 accumulation, float16 output.
+ */
+int attn_vision(const void *q, const void *k, const void *v, void *o,
+                int num_patches, int num_heads, int head_dim, float scale, void *stream);
+
+/*
+ * Single-token decode over a contiguous float16 KV cache with float32 query (doppler
+ * attention.js: decode is seqLen == 1; the _f16kv variants take f32 Q with f16 K/V).
+ *
+ *   q, o : float32 [num_heads, head_dim]
+ *   k, v : float16 [num_kv_heads, kv_len, head_dim]   (head-major cache)
+ *   The query sits at position kv_len - 1 and sees keys [max(0, kv_len - W), kv_len - 1].
+ *   workspace : device memory of at least attn_decode_workspace_bytes(1, num_heads,
+ *               num_kv_heads, head_dim, kv_len) bytes, 256-byte aligned, ZERO-FILLED by the
+ *               caller once when allocated; the kernels leave it zeroed again on completion
+ *               (self-resetting arrival counters), so it can be reused call after call on
+ *               one stream.  One workspace per stream that runs decode concurrently.
+ */
+int attn_decode(const float *q, const void *k, const void *v, float *o,
+                int num_heads, int num_kv_heads, int head_dim, int kv_len,
+                int sliding_window, float attn_softcap, float scale,
+                void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Batched single-token decode over a paged, symmetric-int8 KV cache with float32 query
+ * (doppler attention.js: kvLayout paged with pageSize and kvPageTable, kvLenSource = 1
+ * reading kvLen from a buffer; executeAttentionTieredQuant: packed int8 K/V with separate
+ * K and V scale buffers, f32 Q required).
+ *
+ *   q, o        : float32 [batch, num_heads, head_dim]
+ *   k_pages,
+ *   v_pages     : int8    [num_pages, page_size, num_kv_heads, head_dim]
+ *   k_scales,
+ *   v_scales    : float32 [num_pages, page_size, num_kv_heads]; value = q8 * scale
+ *   page_table  : int32   [batch, max_pages_per_seq]; logical page -> physical page
+ *   kv_lens     : int32   [batch], in DEVICE memory
+ *   page_size   : 16
+ *   Device-data contract: 1 <= kv_lens[b] <= max_pages_per_seq * page_size and
+ *   page_table[b][0 .. ceil(kv_lens[b]/16) - 1] in [0, num_pages).  Entries past that are
+ *   never read.  A kv_lens[b] outside its range makes row b of o NaN (nothing is read for
+ *   it); page-table entries out of range are clamped into [0, num_pages) so a bad table
+ *   gives wrong numbers, never an out-of-bounds access.
+ *   workspace: as for attn_decode, sized by attn_decode_workspace_bytes(batch, num_heads,
+ *   num_kv_heads, head_dim, max_pages_per_seq * page_size).
+ */
+int attn_decode_paged_q8(const float *q, const int8_t *k_pages, const int8_t *v_pages,
+                         const float *k_scales, const float *v_scales,
+                         const int32_t *page_table, const int32_t *kv_lens, float *o,
+                         int batch, int num_heads, int num_kv_heads, int head_dim,
+                         int page_size, int num_pages, int max_pages_per_seq,
+                         int sliding_window, float attn_softcap, float scale,
+                         void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Workspace bytes needed by attn_decode (batch = 1) and attn_decode_paged_q8 for the
+ * given shape (split partials and arrival counters).  Returns 0 for invalid sizes.
+ * Honours the calling thread's split override (attn_set_decode_split).
+ */
+size_t attn_decode_workspace_bytes(int batch, int num_heads, int num_kv_heads, int head_dim,
+                                   int max_kv_len);
+
+/*
+ * Test and tuning hook: force the number of KV tokens each decode workgroup handles
+ * (a positive multiple of 16), for the calling thread; 0 restores the built-in plan.
+ * Split-KV results agree within rounding for every split size.
+ * Returns ATTN_OK or ATTN_ERR_INVALID_ARG.
+ */
+int attn_set_decode_split(int tokens_per_split);
+
+/* Message for the calling thread's last failed call ("" if none).  Valid until the next
+ * call on this thread. */
+const char *attn_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TA03_ATTN_H */

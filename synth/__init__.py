@@ -19,7 +19,10 @@ Generator (counter based, so any slice can be drawn independently):
 """
 from __future__ import annotations
 
+import ctypes
 import math
+import os
+import subprocess
 
 import numpy as np
 
@@ -53,8 +56,52 @@ def uniform(seed: int, n: int, start: int = 0) -> np.ndarray:
     return (splitmix64(seed, start, n) >> np.uint64(11)).astype(np.float64) * (2.0 ** -53)
 
 
-def normal(seed: int, n: int) -> np.ndarray:
-    """n standard normals (float64) from stream `seed`, Box-Muller on pairs."""
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_CLIB = os.path.join(_HERE, "libsynth.so")
+_clib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile synth.c (the threaded generator loop) with gcc into libsynth.so."""
+    if force or not os.path.exists(_CLIB):
+        tmp = _CLIB + ".tmp%d" % os.getpid()
+        subprocess.check_call(["gcc", "-O2", "-fPIC", "-shared", "-std=c11", "-Wall", "-o", tmp,
+                               os.path.join(_HERE, "synth.c"), "-lm", "-lpthread"])
+        os.replace(tmp, _CLIB)
+    return _CLIB
+
+
+def _c():
+    global _clib
+    if _clib is None:
+        if not os.path.exists(_CLIB):
+            build(force=True)
+        L = ctypes.CDLL(_CLIB)
+        L.synth_normal_f32.argtypes = [ctypes.c_uint64, ctypes.c_uint64, ctypes.c_uint64,
+                                       ctypes.c_void_p, ctypes.c_int]
+        L.synth_normal_f32.restype = None
+        L.synth_uniform.argtypes = [ctypes.c_uint64, ctypes.c_uint64, ctypes.c_uint64,
+                                    ctypes.c_void_p]
+        L.synth_uniform.restype = None
+        _clib = L
+    return _clib
+
+
+def _threads() -> int:
+    return max(1, min(32, len(os.sched_getaffinity(0))))
+
+
+def normal_f32_stream(seed: int, start: int, n: int) -> np.ndarray:
+    """Normals with stream indices start .. start+n-1, rounded to float32 (C loop)."""
+    out = np.empty(int(n), dtype=np.float32)
+    if n:
+        _c().synth_normal_f32(int(seed) & 0xFFFFFFFFFFFFFFFF, int(start), int(n),
+                              out.ctypes.data, _threads())
+    return out
+
+
+def normal_numpy(seed: int, n: int) -> np.ndarray:
+    """The same normals in float64, evaluated with numpy (a cross-check of the C loop)."""
     out = np.empty(n, dtype=np.float64)
     npair = (n + 1) // 2
     for p0 in range(0, npair, _CHUNK):
@@ -72,7 +119,7 @@ def normal(seed: int, n: int) -> np.ndarray:
 
 def normal_f32(seed: int, shape) -> np.ndarray:
     n = int(np.prod(shape))
-    return normal(seed, n).astype(np.float32).reshape(shape)
+    return normal_f32_stream(seed, 0, n).reshape(shape)
 
 
 def normal_f16(seed: int, shape) -> np.ndarray:
@@ -118,17 +165,7 @@ def ragged_normal_f32(seed: int, kv_lens, hkv: int, d: int):
     out, start = [], 0
     for L in kv_lens:
         n = int(L) * hkv * d
-        # counter-based: draw the pairs covering [start, start + n)
-        p0 = start // 2
-        p1 = (start + n + 1) // 2
-        u = uniform(seed, 2 * (p1 - p0), start=2 * p0)
-        r = np.sqrt(-2.0 * np.log1p(-u[0::2]))
-        th = (2.0 * math.pi) * u[1::2]
-        pair = np.empty(2 * (p1 - p0), dtype=np.float64)
-        pair[0::2] = r * np.cos(th)
-        pair[1::2] = r * np.sin(th)
-        off = start - 2 * p0
-        out.append(pair[off: off + n].astype(np.float32).reshape(int(L), hkv, d))
+        out.append(normal_f32_stream(seed, start, n).reshape(int(L), hkv, d))
         start += n
     return out
 

@@ -1,0 +1,169 @@
+"""The C ABI without a GPU: the library loads, exports every entry point the header
+declares, and rejects invalid arguments on the host (before any HIP call) with the
+documented status codes and messages."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import transformer_attention_03_amd as ta
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "attn.h")
+
+P = 0x10000          # a fake 16-byte-aligned device address; never dereferenced
+MIS = 0x10004        # misaligned
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(attn_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for n in ("attn_prefill", "attn_vision", "attn_decode", "attn_decode_paged_q8",
+              "attn_decode_workspace_bytes", "attn_last_error", "attn_set_decode_split"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    L = ta.lib()
+    for n in declared_functions():
+        assert hasattr(L, n), n
+    # and the binding offers a function of the same name for each
+    for n in declared_functions():
+        assert callable(getattr(ta, n)), n
+
+
+def test_library_links_no_torch():
+    out = os.popen("ldd %s" % ta.LIB_PATH).read()
+    assert "torch" not in out and "c10" not in out
+    assert "amdhip64" in out
+
+
+def prefill(**kw):
+    a = dict(q=P, k=P, v=P, o=P, dtype=1, seq_len=16, kv_len=16, H=4, Hkv=2, D=128, causal=1,
+             W=0, cap=0.0, scale=0.125)
+    a.update(kw)
+    return ta.lib().attn_prefill(a["q"], a["k"], a["v"], a["o"], a["dtype"], a["seq_len"],
+                                 a["kv_len"], a["H"], a["Hkv"], a["D"], a["causal"], a["W"],
+                                 a["cap"], a["scale"], None)
+
+
+@pytest.mark.parametrize("kw,code,msg", [
+    (dict(q=None), ta.ATTN_ERR_INVALID_ARG, "q must not be null"),
+    (dict(v=MIS), ta.ATTN_ERR_INVALID_ARG, "16-byte aligned"),
+    (dict(dtype=7), ta.ATTN_ERR_INVALID_ARG, "dtype"),
+    (dict(kv_len=0, seq_len=0), ta.ATTN_ERR_INVALID_ARG, "invalid kv_len 0"),
+    (dict(seq_len=17), ta.ATTN_ERR_INVALID_ARG, "seq_len 17"),
+    (dict(H=3), ta.ATTN_ERR_INVALID_ARG, "multiple of num_kv_heads"),
+    (dict(Hkv=0), ta.ATTN_ERR_INVALID_ARG, ">= 1"),
+    (dict(D=96), ta.ATTN_ERR_UNSUPPORTED, "requires head_dim in"),
+    (dict(D=0), ta.ATTN_ERR_INVALID_ARG, "head_dim"),
+    (dict(causal=2), ta.ATTN_ERR_INVALID_ARG, "causal"),
+    (dict(W=-1), ta.ATTN_ERR_INVALID_ARG, "sliding_window"),
+    (dict(cap=-1.0), ta.ATTN_ERR_INVALID_ARG, "attn_softcap"),
+    (dict(cap=float("inf")), ta.ATTN_ERR_INVALID_ARG, "attn_softcap"),
+    (dict(scale=0.0), ta.ATTN_ERR_INVALID_ARG, "scale"),
+    (dict(scale=float("nan")), ta.ATTN_ERR_INVALID_ARG, "scale"),
+])
+def test_prefill_validation(kw, code, msg):
+    assert prefill(**kw) == code
+    assert msg in ta.attn_last_error()
+
+
+def test_vision_validation():
+    L = ta.lib()
+    assert L.attn_vision(P, P, P, P, 0, 16, 64, 0.125, None) == ta.ATTN_ERR_INVALID_ARG
+    assert L.attn_vision(P, P, None, P, 8, 16, 64, 0.125, None) == ta.ATTN_ERR_INVALID_ARG
+    assert L.attn_vision(P, P, P, P, 8, 16, 80, 0.125, None) == ta.ATTN_ERR_UNSUPPORTED
+    assert L.attn_vision(P, P, P, P, 8, 16, 64, -1.0, None) == ta.ATTN_ERR_INVALID_ARG
+
+
+def decode(**kw):
+    a = dict(q=P, k=P, v=P, o=P, H=32, Hkv=8, D=128, L=4096, W=0, cap=0.0, scale=0.088, ws=P,
+             wsb=1 << 30)
+    a.update(kw)
+    return ta.lib().attn_decode(a["q"], a["k"], a["v"], a["o"], a["H"], a["Hkv"], a["D"], a["L"],
+                                a["W"], a["cap"], a["scale"], a["ws"], a["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,code,msg", [
+    (dict(k=None), ta.ATTN_ERR_INVALID_ARG, "k must not be null"),
+    (dict(L=0), ta.ATTN_ERR_INVALID_ARG, "invalid kv_len 0"),
+    (dict(H=30), ta.ATTN_ERR_INVALID_ARG, "multiple"),
+    (dict(D=32), ta.ATTN_ERR_UNSUPPORTED, "head_dim"),
+    (dict(ws=None), ta.ATTN_ERR_WORKSPACE, "workspace must not be null"),
+    (dict(ws=P + 16), ta.ATTN_ERR_WORKSPACE, "256-byte aligned"),
+    (dict(wsb=64), ta.ATTN_ERR_WORKSPACE, "smaller than"),
+    (dict(W=-3), ta.ATTN_ERR_INVALID_ARG, "sliding_window"),
+])
+def test_decode_validation(kw, code, msg):
+    assert decode(**kw) == code
+    assert msg in ta.attn_last_error()
+
+
+def paged(**kw):
+    a = dict(q=P, kp=P, vp=P, ks=P, vs=P, pt=P, kl=P, o=P, B=8, H=32, Hkv=8, D=128, ps=16,
+             npg=16000, mp=2048, W=0, cap=0.0, scale=0.088, ws=P, wsb=1 << 30)
+    a.update(kw)
+    return ta.lib().attn_decode_paged_q8(a["q"], a["kp"], a["vp"], a["ks"], a["vs"], a["pt"],
+                                         a["kl"], a["o"], a["B"], a["H"], a["Hkv"], a["D"],
+                                         a["ps"], a["npg"], a["mp"], a["W"], a["cap"],
+                                         a["scale"], a["ws"], a["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,code,msg", [
+    (dict(pt=None), ta.ATTN_ERR_INVALID_ARG, "page_table must not be null"),
+    (dict(kl=MIS), ta.ATTN_ERR_INVALID_ARG, "kv_lens must be 16-byte aligned"),
+    (dict(B=0), ta.ATTN_ERR_INVALID_ARG, "batch"),
+    (dict(ps=32), ta.ATTN_ERR_UNSUPPORTED, "page_size"),
+    (dict(npg=0), ta.ATTN_ERR_INVALID_ARG, "num_pages"),
+    (dict(ws=None), ta.ATTN_ERR_WORKSPACE, "workspace"),
+    (dict(wsb=1000), ta.ATTN_ERR_WORKSPACE, "smaller than"),
+    (dict(cap=-2.0), ta.ATTN_ERR_INVALID_ARG, "attn_softcap"),
+])
+def test_paged_validation(kw, code, msg):
+    assert paged(**kw) == code
+    assert msg in ta.attn_last_error()
+
+
+def test_workspace_bytes():
+    n = ta.attn_decode_workspace_bytes(1, 32, 8, 128, 4096)
+    assert n > 0 and n % 256 == 0
+    assert ta.attn_decode_workspace_bytes(8, 32, 8, 128, 32768) > n
+    assert ta.attn_decode_workspace_bytes(1, 30, 8, 128, 4096) == 0
+    assert ta.attn_decode_workspace_bytes(1, 32, 8, 100, 4096) == 0
+
+
+def test_split_override_sizes_workspace():
+    base = ta.attn_decode_workspace_bytes(1, 32, 8, 128, 4096)
+    try:
+        ta.attn_set_decode_split(16)
+        small = ta.attn_decode_workspace_bytes(1, 32, 8, 128, 4096)
+        assert small > base
+    finally:
+        ta.attn_set_decode_split(0)
+    assert ta.attn_decode_workspace_bytes(1, 32, 8, 128, 4096) == base
+    with pytest.raises(ta.AttnError):
+        ta.attn_set_decode_split(17)
+
+
+def test_error_string_is_thread_local_and_cleared_on_success():
+    import threading
+    assert prefill(D=96) == ta.ATTN_ERR_UNSUPPORTED
+    seen = {}
+
+    def other():
+        seen["msg"] = ta.attn_last_error()
+
+    t = threading.Thread(target=other)
+    t.start()
+    t.join()
+    assert seen["msg"] == ""
+    assert "head_dim" in ta.attn_last_error()
+    ta.attn_set_decode_split(0)   # a successful call clears it
+    assert ta.attn_last_error() == ""

@@ -1,0 +1,405 @@
+"""GPU parity: every entry point of libattn.so against the float64 CPU oracle on the same
+seeded inputs, element by element.
+
+Tolerances (max-abs, on outputs of O(1)): 1e-4 for the float32 path, 3e-3 for the
+float16 and int8 paths.  Full-size workloads compare every output (decode) or sampled
+query rows computed one by one by the oracle (prefill / vision).  Page-table indexing is
+checked bit-exactly: two placements of the same logical cache give identical bits.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+
+torch = pytest.importorskip("torch")
+import transformer_attention_03_amd as ta  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+
+TOL_F32 = 1e-4
+TOL_F16 = 3e-3
+
+
+@pytest.fixture(scope="module")
+def dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    return torch.device("cuda:0")
+
+
+def to_dev(x, dev):
+    return torch.from_numpy(np.ascontiguousarray(x)).to(dev)
+
+
+def maxabs(a, b):
+    return float(np.max(np.abs(np.asarray(a, np.float64) - np.asarray(b, np.float64))))
+
+
+def say(msg):
+    print(msg, flush=True)
+
+
+# =============================================================================================
+# contiguous f16 decode
+# =============================================================================================
+
+def run_decode(dev, q, k, v, W=0, cap=0.0, scale=None):
+    H, D = q.shape
+    Hkv, L, _ = k.shape
+    scale = scale or 1.0 / math.sqrt(D)
+    qd, kd, vd = to_dev(q, dev), to_dev(k, dev), to_dev(v, dev)
+    od = torch.empty((H, D), dtype=torch.float32, device=dev)
+    ws = ta.decode_workspace(1, H, Hkv, D, L, dev)
+    ta.attn_decode(qd, kd, vd, od, ws, scale=scale, sliding_window=W, attn_softcap=cap)
+    torch.cuda.synchronize()
+    assert int(ws.sum().item()) == 0 or True   # partials may remain; counters checked below
+    return od.cpu().numpy(), ws
+
+
+def decode_oracle(q, k, v, W=0, cap=0.0, scale=None):
+    H, D = q.shape
+    scale = scale or 1.0 / math.sqrt(D)
+    kk = np.transpose(k, (1, 0, 2))[None]       # [1, L, Hkv, D]
+    vv = np.transpose(v, (1, 0, 2))[None]
+    return oracle.attention(q[None, None], kk, vv, causal=True, window=W, softcap=cap,
+                            scale=scale)[0, 0]
+
+
+@pytest.mark.parametrize("H,Hkv,D,L,W,cap", [
+    (8, 2, 128, 300, 0, 0.0),
+    (4, 4, 64, 1, 0, 0.0),
+    (16, 2, 256, 777, 0, 0.0),
+    (8, 8, 128, 129, 0, 0.0),
+    (8, 2, 128, 1000, 100, 0.0),
+    (8, 2, 128, 1000, 0, 50.0),
+    (6, 3, 64, 500, 0, 0.0),
+    (24, 4, 128, 333, 7, 0.0),
+    (64, 8, 128, 2048, 0, 0.0),
+    (32, 8, 128, 4096, 0, 0.0),          # the 32/8-head, 4096-token, head_dim 128 workload
+])
+def test_decode_f16(dev, H, Hkv, D, L, W, cap):
+    say("decode H=%d Hkv=%d D=%d L=%d W=%d cap=%g" % (H, Hkv, D, L, W, cap))
+    c = synth.seed_of(2) + 1000 * H + L
+    q, k, v = synth.decode_inputs(c, H, Hkv, D, L)
+    got, _ = run_decode(dev, q, k, v, W, cap)
+    want = decode_oracle(q, k, v, W, cap)
+    assert np.all(np.isfinite(got))
+    assert maxabs(got, want) < TOL_F16
+
+
+def test_decode_split_sizes_agree(dev):
+    say("decode split sizes")
+    q, k, v = synth.decode_inputs(synth.seed_of(2), 32, 8, 128, 4096)
+    want = decode_oracle(q, k, v)
+    outs = []
+    try:
+        for t in (16, 48, 128, 512, 4096):
+            ta.attn_set_decode_split(t)
+            got, ws = run_decode(dev, q, k, v)
+            assert maxabs(got, want) < TOL_F16, t
+            outs.append(got)
+    finally:
+        ta.attn_set_decode_split(0)
+    for o in outs[1:]:
+        assert maxabs(o, outs[0]) < 1e-5
+
+
+def test_decode_repeat_is_deterministic_and_counters_reset(dev):
+    say("decode repeat")
+    q, k, v = synth.decode_inputs(synth.seed_of(2), 32, 8, 128, 4096)
+    H, D = q.shape
+    qd, kd, vd = to_dev(q, dev), to_dev(k, dev), to_dev(v, dev)
+    ws = ta.decode_workspace(1, 32, 8, 128, 4096, dev)
+    o1 = torch.empty((H, D), dtype=torch.float32, device=dev)
+    o2 = torch.empty_like(o1)
+    for _ in range(3):
+        ta.attn_decode(qd, kd, vd, o1, ws, scale=1 / math.sqrt(128))
+    ta.attn_decode(qd, kd, vd, o2, ws, scale=1 / math.sqrt(128))
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2)
+
+
+def test_decode_softcap_is_applied(dev):
+    """With q scaled x8 and c = 5 the capped and uncapped results differ by >> tolerance."""
+    say("decode softcap sensitivity")
+    q, k, v = synth.decode_inputs(synth.seed_of(2) + 7, 8, 2, 128, 512)
+    q = (q * 8).astype(np.float32)
+    got, _ = run_decode(dev, q, k, v, cap=5.0)
+    capped = decode_oracle(q, k, v, cap=5.0)
+    plain = decode_oracle(q, k, v)
+    assert maxabs(capped, plain) > 30 * TOL_F16
+    assert maxabs(got, capped) < TOL_F16
+
+
+# =============================================================================================
+# paged int8 decode
+# =============================================================================================
+
+def paged_to_dev(d, dev):
+    return {k: to_dev(d[k], dev) for k in ("q", "k_pages", "v_pages", "k_scales", "v_scales",
+                                           "page_table", "kv_lens")}
+
+
+def run_paged(dev, d, W=0, cap=0.0, kv_lens=None, table=None):
+    t = paged_to_dev(d, dev)
+    if kv_lens is not None:
+        t["kv_lens"] = to_dev(np.asarray(kv_lens, np.int32), dev)
+    if table is not None:
+        t["page_table"] = to_dev(table, dev)
+    B, H, D = d["q"].shape
+    Hkv = d["k_pages"].shape[2]
+    mp = d["page_table"].shape[1]
+    o = torch.empty((B, H, D), dtype=torch.float32, device=dev)
+    ws = ta.decode_workspace(B, H, Hkv, D, mp * 16, dev)
+    ta.attn_decode_paged_q8(t["q"], t["k_pages"], t["v_pages"], t["k_scales"], t["v_scales"],
+                            t["page_table"], t["kv_lens"], o, ws, scale=1 / math.sqrt(D),
+                            sliding_window=W, attn_softcap=cap)
+    torch.cuda.synchronize()
+    return o.cpu().numpy()
+
+
+def paged_oracle(d, W=0, cap=0.0):
+    """Oracle over the LOGICAL int8 rows (before paging): never reads the page table."""
+    B, H, D = d["q"].shape
+    Hkv = d["k_q"][0].shape[1]
+    out = np.zeros((B, H, D))
+    for b in range(B):
+        k = oracle.dequant_i8(d["k_q"][b], d["k_s"][b])[None]
+        v = oracle.dequant_i8(d["v_q"][b], d["v_s"][b])[None]
+        out[b] = oracle.attention(d["q"][b][None, None], k, v, causal=True, window=W,
+                                  softcap=cap, scale=1 / math.sqrt(D))[0, 0]
+    return out
+
+
+@pytest.mark.parametrize("lens,H,Hkv,D,W,cap", [
+    ([37, 16, 1, 500], 8, 2, 128, 0, 0.0),
+    ([1000, 2049, 333], 32, 8, 128, 0, 0.0),
+    ([700, 129], 8, 2, 64, 0, 0.0),
+    ([300, 1111], 8, 4, 256, 0, 0.0),
+    ([1500, 900], 8, 2, 128, 256, 0.0),
+    ([1500, 900], 8, 2, 128, 0, 30.0),
+])
+def test_paged_q8(dev, lens, H, Hkv, D, W, cap):
+    say("paged lens=%s H=%d Hkv=%d D=%d W=%d cap=%g" % (lens, H, Hkv, D, W, cap))
+    d = synth.paged_inputs(synth.seed_of(5) + sum(lens), len(lens), H, Hkv, D, lens, n_poison=9)
+    got = run_paged(dev, d, W, cap)
+    want = paged_oracle(d, W, cap)
+    assert np.all(np.isfinite(got))
+    assert maxabs(got, want) < TOL_F16
+
+
+@pytest.fixture(scope="module")
+def c5_inputs():
+    """The batch-8, 32/8-head, head_dim 128 int8 paged workload with kv_len ~ U[16384, 32768]."""
+    c = synth.seed_of(5)
+    lens = synth.paged_kv_lens(c, 8, 16384, 32768)
+    return synth.paged_inputs(c, 8, 32, 8, 128, lens, n_poison=64, max_pages=2048)
+
+
+def test_paged_q8_full_workload(dev, c5_inputs):
+    say("paged full workload")
+    got = run_paged(dev, c5_inputs)
+    want = paged_oracle(c5_inputs)
+    assert np.all(np.isfinite(got))
+    assert maxabs(got, want) < TOL_F16
+
+
+def test_paged_permutation_is_bit_identical(dev):
+    say("paged permutation bit identity")
+    lens = [2000, 1234, 17, 4096]
+    c = synth.seed_of(5) + 99
+    a = synth.paged_inputs(c, 4, 32, 8, 128, lens, n_poison=20)
+    b = synth.paged_inputs(c, 4, 32, 8, 128, lens, n_poison=20, alt_perm=True)
+    assert not np.array_equal(a["page_table"], b["page_table"])
+    oa = run_paged(dev, a)
+    ob = run_paged(dev, b)
+    assert np.array_equal(oa.view(np.uint32), ob.view(np.uint32))
+    assert maxabs(oa, paged_oracle(a)) < TOL_F16
+
+
+def test_paged_negative_control_detects_mis_indexing(dev):
+    """A wrong page-table entry must show up.  One query sees every key, so the result is
+    invariant to the ORDER of its pages; the controls therefore (a) point a logical page at
+    a copy of another one and (b) swap a full page with the poisoned partial last page."""
+    say("paged negative control")
+    lens = [1000, 800]
+    d = synth.paged_inputs(synth.seed_of(5) + 5, 2, 8, 2, 128, lens, n_poison=4)
+    want = paged_oracle(d)
+    assert maxabs(run_paged(dev, d), want) < TOL_F16
+    dup = d["page_table"].copy()
+    dup[0, 3] = dup[0, 40]
+    got = run_paged(dev, d, table=dup)
+    assert maxabs(got[0], want[0]) > 3 * TOL_F16
+    assert maxabs(got[1], want[1]) < TOL_F16
+    swp = d["page_table"].copy()
+    last = (lens[0] + 15) // 16 - 1           # holds 8 live slots and 8 poisoned ones
+    swp[0, 3], swp[0, last] = swp[0, last], swp[0, 3]
+    got = run_paged(dev, d, table=swp)
+    assert np.all(np.isnan(got[0]))
+    assert maxabs(got[1], want[1]) < TOL_F16
+
+
+def test_paged_out_of_contract_kv_len_gives_nan_row(dev):
+    say("paged out-of-contract kv_len")
+    lens = [300, 200, 100]
+    d = synth.paged_inputs(synth.seed_of(5) + 6, 3, 8, 2, 128, lens, n_poison=2)
+    mp = d["page_table"].shape[1]
+    got = run_paged(dev, d, kv_lens=[300, 0, mp * 16 + 1])
+    want = paged_oracle(d)
+    assert maxabs(got[0], want[0]) < TOL_F16
+    assert np.all(np.isnan(got[1])) and np.all(np.isnan(got[2]))
+
+
+# =============================================================================================
+# prefill (token-major) and vision (head-major)
+# =============================================================================================
+
+def run_prefill(dev, q, k, v, causal, W=0, cap=0.0, scale=None):
+    S, H, D = q.shape
+    scale = scale or 1.0 / math.sqrt(D)
+    qd, kd, vd = to_dev(q, dev), to_dev(k, dev), to_dev(v, dev)
+    od = torch.empty_like(qd)
+    ta.attn_prefill(qd, kd, vd, od, causal=causal, scale=scale, sliding_window=W,
+                    attn_softcap=cap)
+    torch.cuda.synchronize()
+    return od.cpu().numpy()
+
+
+def prefill_oracle_rows(q, k, v, rows, causal, W=0, cap=0.0, scale=None):
+    """Oracle for selected query rows, one row at a time (keys up to its position)."""
+    S, H, D = q.shape
+    L = k.shape[0]
+    scale = scale or 1.0 / math.sqrt(D)
+    out = []
+    for i in rows:
+        p = L - S + i
+        hi = p + 1 if causal else L
+        o = oracle.attention(q[None, i:i + 1], k[None, :hi], v[None, :hi], causal=causal,
+                             window=W, softcap=cap, scale=scale)[0, 0]
+        out.append(o)
+    return np.stack(out)
+
+
+@pytest.mark.parametrize("D", [64, 128, 256])
+@pytest.mark.parametrize("S,L,causal,W,cap", [
+    (200, 200, True, 0, 0.0),
+    (200, 200, False, 0, 0.0),
+    (77, 300, True, 0, 0.0),
+    (300, 300, True, 37, 0.0),
+    (300, 300, True, 0, 20.0),
+    (130, 130, True, 64, 50.0),
+])
+def test_prefill_f16(dev, D, S, L, causal, W, cap):
+    say("prefill f16 D=%d S=%d L=%d causal=%d W=%d cap=%g" % (D, S, L, causal, W, cap))
+    q, k, v = synth.prefill_inputs(synth.seed_of(3) + D + S, S, L, 4, 2, D, "f16")
+    got = run_prefill(dev, q, k, v, causal, W, cap)
+    want = oracle.attention(q[None], k[None], v[None], causal=causal, window=W, softcap=cap,
+                            scale=1 / math.sqrt(D))[0]
+    assert np.all(np.isfinite(got))
+    assert maxabs(got, want) < TOL_F16
+
+
+@pytest.mark.parametrize("D,S,L,H,Hkv,causal,W,cap", [
+    (64, 128, 128, 1, 1, True, 0, 0.0),       # the causal 128-token, head_dim 64 f32 workload
+    (64, 100, 250, 2, 1, True, 0, 0.0),
+    (128, 70, 70, 4, 2, True, 16, 0.0),
+    (256, 65, 65, 2, 2, False, 0, 10.0),
+])
+def test_prefill_f32(dev, D, S, L, H, Hkv, causal, W, cap):
+    say("prefill f32 D=%d S=%d L=%d" % (D, S, L))
+    q, k, v = synth.prefill_inputs(synth.seed_of(1) + S + D, S, L, H, Hkv, D, "f32")
+    got = run_prefill(dev, q, k, v, causal, W, cap)
+    want = oracle.attention(q[None], k[None], v[None], causal=causal, window=W, softcap=cap,
+                            scale=1 / math.sqrt(D))[0]
+    assert maxabs(got, want) < TOL_F32
+
+
+@pytest.fixture(scope="module")
+def c3_inputs():
+    """Causal GQA prefill: 2048 tokens, 16/8 heads, head_dim 256, f16."""
+    return synth.prefill_inputs(synth.seed_of(3), 2048, 2048, 16, 8, 256, "f16")
+
+
+C3_ROWS = [0, 1, 2, 15, 16, 63, 64, 127, 128, 255, 256, 511, 512, 513, 777, 1023, 1024, 1500,
+           1919, 2046, 2047]
+
+
+def test_prefill_full_workload_sampled_rows(dev, c3_inputs):
+    say("prefill full workload")
+    q, k, v = c3_inputs
+    got = run_prefill(dev, q, k, v, True, 512, 50.0)
+    assert np.all(np.isfinite(got))
+    want = prefill_oracle_rows(q, k, v, C3_ROWS, True, 512, 50.0)
+    assert maxabs(got[C3_ROWS], want) < TOL_F16
+    # row 0 sees only key 0: its output is v0 exactly, for every head
+    G = 2
+    for h in range(16):
+        assert np.array_equal(got[0, h], v[0, h // G])
+
+
+def test_prefill_softcap_is_applied(dev):
+    say("prefill softcap sensitivity")
+    q, k, v = synth.prefill_inputs(synth.seed_of(3) + 11, 160, 160, 2, 1, 128, "f16")
+    q = (q.astype(np.float32) * 8).astype(np.float16)
+    got = run_prefill(dev, q, k, v, True, 0, 5.0)
+    capped = oracle.attention(q[None], k[None], v[None], causal=True, softcap=5.0,
+                              scale=1 / math.sqrt(128))[0]
+    plain = oracle.attention(q[None], k[None], v[None], causal=True, scale=1 / math.sqrt(128))[0]
+    assert maxabs(capped, plain) > 30 * TOL_F16
+    assert maxabs(got, capped) < TOL_F16
+
+
+def test_prefill_window_row_equals_decode_slice(dev):
+    """Causal + window prefill row i == decode over keys [i-W+1, i] (q f16 -> f32 exactly)."""
+    say("prefill row == decode slice")
+    S, H, Hkv, D, W = 300, 8, 2, 128, 64
+    q, k, v = synth.prefill_inputs(synth.seed_of(3) + 21, S, S, H, Hkv, D, "f16")
+    pre = run_prefill(dev, q, k, v, True, W)
+    for i in (0, 5, 63, 64, 200, 299):
+        lo = max(0, i - W + 1)
+        kk = np.ascontiguousarray(np.transpose(k[lo:i + 1], (1, 0, 2)))
+        vv = np.ascontiguousarray(np.transpose(v[lo:i + 1], (1, 0, 2)))
+        dec, _ = run_decode(dev, q[i].astype(np.float32), kk, vv)
+        assert maxabs(pre[i], dec) < 2 * TOL_F16
+
+
+def run_vision(dev, q, k, v, scale):
+    qd, kd, vd = to_dev(q, dev), to_dev(k, dev), to_dev(v, dev)
+    od = torch.empty_like(qd)
+    ta.attn_vision(qd, kd, vd, od, scale=scale)
+    torch.cuda.synchronize()
+    return od.cpu().numpy()
+
+
+@pytest.mark.parametrize("H,P,D", [(2, 100, 64), (3, 257, 128), (1, 64, 256), (2, 1, 64)])
+def test_vision_small(dev, H, P, D):
+    say("vision H=%d P=%d D=%d" % (H, P, D))
+    q, k, v = synth.vision_inputs(synth.seed_of(4) + P, P, H, D)
+    got = run_vision(dev, q, k, v, 1 / math.sqrt(D))
+    qt, kt, vt = (np.transpose(x, (1, 0, 2)) for x in (q, k, v))
+    want = oracle.attention(qt[None], kt[None], vt[None], causal=False,
+                            scale=1 / math.sqrt(D))[0]
+    assert maxabs(np.transpose(got, (1, 0, 2)), want) < TOL_F16
+
+
+def test_vision_full_workload_sampled_rows(dev):
+    say("vision full workload")
+    q, k, v = synth.vision_inputs(synth.seed_of(4), 2304, 16, 64)
+    got = run_vision(dev, q, k, v, 0.125)
+    assert np.all(np.isfinite(got))
+    rows = [0, 1, 127, 128, 1000, 2047, 2303]
+    qt, kt, vt = (np.transpose(x, (1, 0, 2)) for x in (q, k, v))
+    want = prefill_oracle_rows(qt, kt, vt, rows, False, scale=0.125)
+    assert maxabs(np.transpose(got, (1, 0, 2))[rows], want) < TOL_F16
+
+
+def test_vision_equals_bidirectional_prefill(dev):
+    say("vision == bidirectional prefill")
+    q, k, v = synth.vision_inputs(synth.seed_of(4) + 3, 300, 4, 64)
+    vis = run_vision(dev, q, k, v, 0.125)
+    qt, kt, vt = (np.ascontiguousarray(np.transpose(x, (1, 0, 2))) for x in (q, k, v))
+    pre = run_prefill(dev, qt, kt, vt, False, scale=0.125)
+    assert np.array_equal(np.transpose(vis, (1, 0, 2)), pre)

@@ -16,12 +16,21 @@ def test_counter_based_slices_agree():
     a = synth.splitmix64(77, 0, 1000)
     b = synth.splitmix64(77, 400, 100)
     assert np.array_equal(a[400:500], b)
-    n = synth.normal(5, 1001)
-    assert np.array_equal(n[:1000], synth.normal(5, 1000))
+    n = synth.normal_f32_stream(5, 0, 1001)
+    assert np.array_equal(n[:1000], synth.normal_f32_stream(5, 0, 1000))
+    assert np.array_equal(n[301:700], synth.normal_f32_stream(5, 301, 399))
+
+
+def test_c_loop_matches_numpy_definition():
+    a = synth.normal_f32_stream(42, 0, 200_001)
+    b = synth.normal_numpy(42, 200_001)
+    # same uniforms and formula; libm and numpy may differ in the last f64 ulp only
+    np.testing.assert_allclose(a, b.astype(np.float32), rtol=1e-6, atol=1e-7)
+    assert np.mean(a == b.astype(np.float32)) > 0.999
 
 
 def test_normals_look_normal():
-    x = synth.normal(12345, 400_000)
+    x = synth.normal_f32_stream(12345, 0, 400_000).astype(np.float64)
     assert abs(x.mean()) < 0.01
     assert abs(x.std() - 1.0) < 0.01
     assert abs(np.mean(np.abs(x) < 1.0) - 0.6827) < 0.005

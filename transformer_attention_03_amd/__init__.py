@@ -1,0 +1,170 @@
+"""Softmax attention with online softmax for AMD Instinct MI355X (gfx950).
+
+A thin ctypes binding over ``libattn.so``: each function has the name of the C
+entry point it calls (``include/attn.h``) and only marshals arguments (shapes,
+device pointers, the current HIP stream).  Every step of the computation runs
+in the library's HIP kernels; there is no fallback of any kind, and a missing
+library is an error.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+__all__ = [
+    "AttnError", "lib", "attn_prefill", "attn_vision", "attn_decode", "attn_decode_paged_q8",
+    "attn_decode_workspace_bytes", "attn_set_decode_split", "attn_last_error", "decode_workspace",
+    "ATTN_OK", "ATTN_ERR_INVALID_ARG", "ATTN_ERR_UNSUPPORTED", "ATTN_ERR_WORKSPACE",
+    "ATTN_ERR_LAUNCH", "ATTN_F32", "ATTN_F16", "LIB_PATH",
+]
+
+ATTN_OK, ATTN_ERR_INVALID_ARG, ATTN_ERR_UNSUPPORTED, ATTN_ERR_WORKSPACE, ATTN_ERR_LAUNCH = 0, -1, -2, -3, -4
+ATTN_F32, ATTN_F16 = 0, 1
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libattn.so")
+_lib = None
+
+
+class AttnError(RuntimeError):
+    def __init__(self, code: int, message: str):
+        super().__init__("attn error %d: %s" % (code, message))
+        self.code = code
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libattn.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError("libattn.so is not built (%s); run `python -m "
+                               "transformer_attention_03_amd.build`" % LIB_PATH)
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+        L.attn_prefill.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, i, i, f, f, vp]
+        L.attn_vision.argtypes = [vp, vp, vp, vp, i, i, i, f, vp]
+        L.attn_decode.argtypes = [vp, vp, vp, vp, i, i, i, i, i, f, f, vp, sz, vp]
+        L.attn_decode_paged_q8.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i,
+                                           f, f, vp, sz, vp]
+        L.attn_decode_workspace_bytes.argtypes = [i, i, i, i, i]
+        L.attn_decode_workspace_bytes.restype = sz
+        L.attn_set_decode_split.argtypes = [i]
+        L.attn_last_error.argtypes = []
+        L.attn_last_error.restype = ctypes.c_char_p
+        for name in ("attn_prefill", "attn_vision", "attn_decode", "attn_decode_paged_q8",
+                     "attn_set_decode_split"):
+            getattr(L, name).restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def attn_last_error() -> str:
+    return lib().attn_last_error().decode()
+
+
+def _check(rc: int):
+    if rc != ATTN_OK:
+        raise AttnError(rc, attn_last_error())
+
+
+def _stream(t, stream):
+    if stream is not None:
+        return stream if isinstance(stream, int) else stream.cuda_stream
+    import torch
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _dtype_code(t):
+    import torch
+    if t.dtype == torch.float32:
+        return ATTN_F32
+    if t.dtype == torch.float16:
+        return ATTN_F16
+    raise TypeError("q/k/v/o must be float32 or float16, got %s" % t.dtype)
+
+
+def _need_contig(*ts):
+    for t in ts:
+        if not t.is_contiguous():
+            raise ValueError("tensors must be contiguous")
+
+
+def attn_prefill(q, k, v, o, *, causal: bool, scale: float, sliding_window: int = 0,
+                 attn_softcap: float = 0.0, stream=None):
+    """q, o: [seq_len, num_heads, head_dim]; k, v: [kv_len, num_kv_heads, head_dim]."""
+    _need_contig(q, k, v, o)
+    S, H, D = q.shape
+    L, Hkv, Dk = k.shape
+    if Dk != D or v.shape != k.shape or o.shape != q.shape or o.dtype != q.dtype:
+        raise ValueError("shape/dtype mismatch")
+    _check(lib().attn_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _dtype_code(q), S, L, H, Hkv,
+                              D, 1 if causal else 0, int(sliding_window), float(attn_softcap),
+                              float(scale), _stream(q, stream)))
+
+
+def attn_vision(q, k, v, o, *, scale: float, stream=None):
+    """q, k, v, o: float16 [num_heads, num_patches, head_dim]."""
+    _need_contig(q, k, v, o)
+    H, P, D = q.shape
+    if k.shape != q.shape or v.shape != q.shape or o.shape != q.shape:
+        raise ValueError("shape mismatch")
+    _check(lib().attn_vision(_ptr(q), _ptr(k), _ptr(v), _ptr(o), P, H, D, float(scale),
+                             _stream(q, stream)))
+
+
+def attn_decode_workspace_bytes(batch, num_heads, num_kv_heads, head_dim, max_kv_len) -> int:
+    return int(lib().attn_decode_workspace_bytes(batch, num_heads, num_kv_heads, head_dim,
+                                                 max_kv_len))
+
+
+def attn_set_decode_split(tokens_per_split: int):
+    _check(lib().attn_set_decode_split(int(tokens_per_split)))
+
+
+def decode_workspace(batch, num_heads, num_kv_heads, head_dim, max_kv_len, device):
+    """A zero-filled workspace of the required size, allocated by torch."""
+    import torch
+    n = attn_decode_workspace_bytes(batch, num_heads, num_kv_heads, head_dim, max_kv_len)
+    if n == 0:
+        raise ValueError("invalid decode shape")
+    return torch.zeros(n, dtype=torch.uint8, device=device)
+
+
+def attn_decode(q, k, v, o, workspace, *, scale: float, sliding_window: int = 0,
+                attn_softcap: float = 0.0, stream=None):
+    """q, o: float32 [num_heads, head_dim]; k, v: float16 [num_kv_heads, kv_len, head_dim]."""
+    _need_contig(q, k, v, o)
+    H, D = q.shape
+    Hkv, L, Dk = k.shape
+    if Dk != D or v.shape != k.shape or o.shape != q.shape:
+        raise ValueError("shape mismatch")
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(lib().attn_decode(_ptr(q), _ptr(k), _ptr(v), _ptr(o), H, Hkv, D, L,
+                             int(sliding_window), float(attn_softcap), float(scale),
+                             _ptr(workspace), ws_bytes, _stream(q, stream)))
+
+
+def attn_decode_paged_q8(q, k_pages, v_pages, k_scales, v_scales, page_table, kv_lens, o,
+                         workspace, *, scale: float, sliding_window: int = 0,
+                         attn_softcap: float = 0.0, stream=None):
+    """q, o: float32 [batch, num_heads, head_dim]; pages int8 [num_pages, 16, num_kv_heads,
+    head_dim]; scales float32 [num_pages, 16, num_kv_heads]; page_table int32
+    [batch, max_pages]; kv_lens int32 [batch] (device)."""
+    _need_contig(q, k_pages, v_pages, k_scales, v_scales, page_table, kv_lens, o)
+    B, H, D = q.shape
+    P, ps, Hkv, Dk = k_pages.shape
+    if Dk != D or v_pages.shape != k_pages.shape or o.shape != q.shape:
+        raise ValueError("shape mismatch")
+    if k_scales.shape != (P, ps, Hkv) or v_scales.shape != (P, ps, Hkv):
+        raise ValueError("scales must be [num_pages, page_size, num_kv_heads]")
+    if page_table.shape[0] != B or kv_lens.shape != (B,):
+        raise ValueError("page_table must be [batch, max_pages] and kv_lens [batch]")
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check(lib().attn_decode_paged_q8(
+        _ptr(q), _ptr(k_pages), _ptr(v_pages), _ptr(k_scales), _ptr(v_scales), _ptr(page_table),
+        _ptr(kv_lens), _ptr(o), B, H, Hkv, D, ps, P, page_table.shape[1], int(sliding_window),
+        float(attn_softcap), float(scale), _ptr(workspace), ws_bytes, _stream(q, stream)))

@@ -1,0 +1,330 @@
+// C ABI of libattn.so: argument validation, launch planning and error reporting.
+// Every argument check runs before the first HIP call, so a rejected call queues nothing.
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "attn.h"
+#include "launch.hpp"
+
+namespace {
+
+thread_local char g_err[512] = "";
+thread_local int g_split_override = 0;
+
+int fail(int code, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+    return code;
+}
+
+int ok() {
+    g_err[0] = '\0';
+    return ATTN_OK;
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+int check_ptr(const void* p, const char* name) {
+    if (!p) return fail(ATTN_ERR_INVALID_ARG, "%s must not be null", name);
+    if (!aligned(p, 16)) return fail(ATTN_ERR_INVALID_ARG, "%s must be 16-byte aligned", name);
+    return ATTN_OK;
+}
+
+int check_heads(int num_heads, int num_kv_heads, int head_dim) {
+    if (num_heads < 1 || num_kv_heads < 1)
+        return fail(ATTN_ERR_INVALID_ARG, "num_heads (%d) and num_kv_heads (%d) must be >= 1",
+                    num_heads, num_kv_heads);
+    if (num_heads % num_kv_heads != 0)
+        return fail(ATTN_ERR_INVALID_ARG, "num_heads (%d) must be a multiple of num_kv_heads (%d)",
+                    num_heads, num_kv_heads);
+    if (head_dim < 1) return fail(ATTN_ERR_INVALID_ARG, "head_dim (%d) must be >= 1", head_dim);
+    if (head_dim != 64 && head_dim != 128 && head_dim != 256)
+        return fail(ATTN_ERR_UNSUPPORTED, "head_dim %d is not built; requires head_dim in {64, 128, 256}",
+                    head_dim);
+    return ATTN_OK;
+}
+
+int check_scalars(int sliding_window, float attn_softcap, float scale) {
+    if (sliding_window < 0)
+        return fail(ATTN_ERR_INVALID_ARG, "sliding_window (%d) must be >= 0 (0 = off)", sliding_window);
+    if (!std::isfinite(attn_softcap) || attn_softcap < 0.f)
+        return fail(ATTN_ERR_INVALID_ARG, "attn_softcap must be finite and >= 0 (0 = off)");
+    if (!std::isfinite(scale) || !(scale > 0.f))
+        return fail(ATTN_ERR_INVALID_ARG, "scale must be finite and > 0");
+    return ATTN_OK;
+}
+
+#define TRY(x)                      \
+    do {                            \
+        int _rc = (x);              \
+        if (_rc != ATTN_OK) return _rc; \
+    } while (0)
+
+constexpr long kMaxElems = 1L << 40;
+
+// ---- decode split plan ----------------------------------------------------------------------
+
+struct DecodePlan {
+    int gc;             // query heads per workgroup
+    int nch;            // head chunks per KV head
+    int split_tokens;   // logical tokens per workgroup
+    int n_split;        // grid.x
+};
+
+int heads_per_wg(int group) {
+    for (int gc : {8, 4, 2, 1})
+        if (group % gc == 0) return gc;
+    return 1;
+}
+
+DecodePlan plan_decode(int batch, int num_heads, int num_kv_heads, int head_dim, int eff_len,
+                       bool paged) {
+    DecodePlan p;
+    const int group = num_heads / num_kv_heads;
+    p.gc = heads_per_wg(group);
+    p.nch = group / p.gc;
+    const int min_t = 4 * ta03::decode_tokens_per_block(head_dim, paged);   // one block per wave
+    int t = g_split_override;
+    if (t <= 0) {
+        // aim for about eight workgroups per compute unit over 256 CUs
+        const long rows = (long)eff_len * batch * num_kv_heads * p.nch;
+        long want = (rows + 2047) / 2048;
+        t = (int)(((want + min_t - 1) / min_t) * min_t);
+        if (t < min_t) t = min_t;
+    }
+    p.split_tokens = t;
+    p.n_split = (eff_len + t - 1) / t;
+    if (p.n_split < 1) p.n_split = 1;
+    return p;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+struct WorkspaceLayout {
+    size_t o_off, m_off, l_off, t_off, total;
+};
+
+WorkspaceLayout workspace_layout(int batch, int num_heads, int num_kv_heads, int head_dim,
+                                 const DecodePlan& p) {
+    WorkspaceLayout w;
+    const size_t parts = (size_t)batch * num_heads * p.n_split;
+    w.o_off = 0;
+    w.m_off = w.o_off + align256(parts * head_dim * sizeof(float));
+    w.l_off = w.m_off + align256(parts * sizeof(float));
+    w.t_off = w.l_off + align256(parts * sizeof(float));
+    w.total = w.t_off + align256((size_t)batch * num_kv_heads * p.nch * sizeof(uint32_t));
+    return w;
+}
+
+size_t workspace_bytes_for(int batch, int num_heads, int num_kv_heads, int head_dim, int max_len) {
+    size_t best = 0;
+    for (bool paged : {false, true}) {
+        const DecodePlan p = plan_decode(batch, num_heads, num_kv_heads, head_dim, max_len, paged);
+        const size_t t = workspace_layout(batch, num_heads, num_kv_heads, head_dim, p).total;
+        if (t > best) best = t;
+    }
+    return best;
+}
+
+const float kLog2e = 1.4426950408889634f;
+
+void fill_scalars(ta03::DecodeParams& d, int window, float softcap, float scale) {
+    d.window = window;
+    d.scale = scale;
+    d.scale_log2 = scale * kLog2e;
+    d.softcap = softcap;
+    d.inv_softcap = softcap > 0.f ? 1.0f / softcap : 0.f;
+}
+
+int launch_status(hipError_t e, const char* what) {
+    if (e != hipSuccess) return fail(ATTN_ERR_LAUNCH, "%s: launch failed: %s", what, hipGetErrorString(e));
+    return ok();
+}
+
+int run_fwd(const void* q, const void* k, const void* v, void* o, int dtype, int seq_len, int kv_len,
+            int H, int Hkv, int D, int causal, int window, float softcap, float scale, long q_row,
+            long q_head, long k_row, long k_head, long o_row, long o_head, void* stream,
+            const char* what) {
+    ta03::FwdParams p;
+    p.q = q; p.k = k; p.v = v; p.o = o;
+    p.q_row = q_row; p.q_head = q_head;
+    p.k_row = k_row; p.k_head = k_head;
+    p.o_row = o_row; p.o_head = o_head;
+    p.seq_len = seq_len; p.kv_len = kv_len;
+    p.H = H; p.Hkv = Hkv;
+    p.causal = causal; p.window = window;
+    p.scale = scale; p.scale_log2 = scale * kLog2e;
+    p.softcap = softcap; p.inv_softcap = softcap > 0.f ? 1.0f / softcap : 0.f;
+    const int bm = ta03::fwd_block_rows(D, dtype);
+    p.n_qblocks = (seq_len + bm - 1) / bm;
+    if ((long)p.n_qblocks * H > 0x7fffffffL)
+        return fail(ATTN_ERR_INVALID_ARG, "%s: grid of %ld workgroups exceeds the device limit", what,
+                    (long)p.n_qblocks * H);
+    return launch_status(ta03::launch_fwd(p, D, dtype, reinterpret_cast<hipStream_t>(stream)), what);
+}
+
+}  // namespace
+
+extern "C" {
+
+int attn_prefill(const void* q, const void* k, const void* v, void* o, int dtype, int seq_len,
+                 int kv_len, int num_heads, int num_kv_heads, int head_dim, int causal,
+                 int sliding_window, float attn_softcap, float scale, void* stream) {
+    if (dtype != ATTN_F32 && dtype != ATTN_F16)
+        return fail(ATTN_ERR_INVALID_ARG, "attn_prefill: dtype %d is neither ATTN_F32 nor ATTN_F16", dtype);
+    TRY(check_ptr(q, "q"));
+    TRY(check_ptr(k, "k"));
+    TRY(check_ptr(v, "v"));
+    TRY(check_ptr(o, "o"));
+    if (kv_len < 1) return fail(ATTN_ERR_INVALID_ARG, "attn_prefill: invalid kv_len %d (must be >= 1)", kv_len);
+    if (seq_len < 1 || seq_len > kv_len)
+        return fail(ATTN_ERR_INVALID_ARG, "attn_prefill: seq_len %d must be in [1, kv_len = %d]", seq_len, kv_len);
+    if (causal != 0 && causal != 1) return fail(ATTN_ERR_INVALID_ARG, "attn_prefill: causal must be 0 or 1");
+    TRY(check_heads(num_heads, num_kv_heads, head_dim));
+    TRY(check_scalars(sliding_window, attn_softcap, scale));
+    if ((long)kv_len * num_kv_heads * head_dim > kMaxElems || (long)seq_len * num_heads * head_dim > kMaxElems)
+        return fail(ATTN_ERR_INVALID_ARG, "attn_prefill: tensor too large");
+    const long hd = head_dim;
+    return run_fwd(q, k, v, o, dtype, seq_len, kv_len, num_heads, num_kv_heads, head_dim, causal,
+                   sliding_window, attn_softcap, scale, num_heads * hd, hd, num_kv_heads * hd, hd,
+                   num_heads * hd, hd, stream, "attn_prefill");
+}
+
+int attn_vision(const void* q, const void* k, const void* v, void* o, int num_patches, int num_heads,
+                int head_dim, float scale, void* stream) {
+    TRY(check_ptr(q, "q"));
+    TRY(check_ptr(k, "k"));
+    TRY(check_ptr(v, "v"));
+    TRY(check_ptr(o, "o"));
+    if (num_patches < 1) return fail(ATTN_ERR_INVALID_ARG, "attn_vision: num_patches %d must be >= 1", num_patches);
+    TRY(check_heads(num_heads, num_heads, head_dim));
+    TRY(check_scalars(0, 0.f, scale));
+    if ((long)num_patches * num_heads * head_dim > kMaxElems)
+        return fail(ATTN_ERR_INVALID_ARG, "attn_vision: tensor too large");
+    const long hd = head_dim, ph = (long)num_patches * head_dim;
+    return run_fwd(q, k, v, o, ATTN_F16, num_patches, num_patches, num_heads, num_heads, head_dim, 0, 0,
+                   0.f, scale, hd, ph, hd, ph, hd, ph, stream, "attn_vision");
+}
+
+size_t attn_decode_workspace_bytes(int batch, int num_heads, int num_kv_heads, int head_dim,
+                                   int max_kv_len) {
+    if (batch < 1 || num_heads < 1 || num_kv_heads < 1 || num_heads % num_kv_heads != 0 ||
+        max_kv_len < 1 || (head_dim != 64 && head_dim != 128 && head_dim != 256))
+        return 0;
+    return workspace_bytes_for(batch, num_heads, num_kv_heads, head_dim, max_kv_len);
+}
+
+int attn_set_decode_split(int tokens_per_split) {
+    if (tokens_per_split < 0 || tokens_per_split % 16 != 0 || tokens_per_split > (1 << 24))
+        return fail(ATTN_ERR_INVALID_ARG,
+                    "attn_set_decode_split: %d is not 0 or a positive multiple of 16", tokens_per_split);
+    g_split_override = tokens_per_split;
+    return ok();
+}
+
+int attn_decode(const float* q, const void* k, const void* v, float* o, int num_heads, int num_kv_heads,
+                int head_dim, int kv_len, int sliding_window, float attn_softcap, float scale,
+                void* workspace, size_t workspace_bytes, void* stream) {
+    TRY(check_ptr(q, "q"));
+    TRY(check_ptr(k, "k"));
+    TRY(check_ptr(v, "v"));
+    TRY(check_ptr(o, "o"));
+    TRY(check_heads(num_heads, num_kv_heads, head_dim));
+    if (kv_len < 1) return fail(ATTN_ERR_INVALID_ARG, "attn_decode: invalid kv_len %d (must be >= 1)", kv_len);
+    TRY(check_scalars(sliding_window, attn_softcap, scale));
+    if ((long)kv_len * num_kv_heads * head_dim > kMaxElems)
+        return fail(ATTN_ERR_INVALID_ARG, "attn_decode: tensor too large");
+    const int eff = (sliding_window > 0 && sliding_window < kv_len) ? sliding_window : kv_len;
+    const DecodePlan plan = plan_decode(1, num_heads, num_kv_heads, head_dim, eff, false);
+    const WorkspaceLayout wl = workspace_layout(1, num_heads, num_kv_heads, head_dim, plan);
+    if (plan.n_split > 1) {
+        if (!workspace) return fail(ATTN_ERR_WORKSPACE, "attn_decode: workspace must not be null");
+        if (!aligned(workspace, 256)) return fail(ATTN_ERR_WORKSPACE, "attn_decode: workspace must be 256-byte aligned");
+        if (workspace_bytes < wl.total)
+            return fail(ATTN_ERR_WORKSPACE, "attn_decode: workspace of %zu bytes is smaller than the %zu required",
+                        workspace_bytes, wl.total);
+    }
+    if (plan.n_split > 65535 * 32)
+        return fail(ATTN_ERR_INVALID_ARG, "attn_decode: grid too large");
+    ta03::DecodeParams d{};
+    d.q = q; d.k = k; d.v = v; d.o = o;
+    char* ws = reinterpret_cast<char*>(workspace);
+    d.part_o = reinterpret_cast<float*>(ws + wl.o_off);
+    d.part_m = reinterpret_cast<float*>(ws + wl.m_off);
+    d.part_l = reinterpret_cast<float*>(ws + wl.l_off);
+    d.tickets = reinterpret_cast<uint32_t*>(ws + wl.t_off);
+    d.H = num_heads; d.Hkv = num_kv_heads; d.kv_len = kv_len;
+    d.num_pages = 0; d.max_pages = 0;
+    fill_scalars(d, sliding_window, attn_softcap, scale);
+    d.split_tokens = plan.split_tokens;
+    d.n_split_max = plan.n_split;
+    return launch_status(ta03::launch_decode(d, head_dim, plan.gc, false, 1,
+                                             reinterpret_cast<hipStream_t>(stream)),
+                         "attn_decode");
+}
+
+int attn_decode_paged_q8(const float* q, const int8_t* k_pages, const int8_t* v_pages, const float* k_scales,
+                         const float* v_scales, const int32_t* page_table, const int32_t* kv_lens, float* o,
+                         int batch, int num_heads, int num_kv_heads, int head_dim, int page_size,
+                         int num_pages, int max_pages_per_seq, int sliding_window, float attn_softcap,
+                         float scale, void* workspace, size_t workspace_bytes, void* stream) {
+    TRY(check_ptr(q, "q"));
+    TRY(check_ptr(k_pages, "k_pages"));
+    TRY(check_ptr(v_pages, "v_pages"));
+    TRY(check_ptr(k_scales, "k_scales"));
+    TRY(check_ptr(v_scales, "v_scales"));
+    TRY(check_ptr(page_table, "page_table"));
+    TRY(check_ptr(kv_lens, "kv_lens"));
+    TRY(check_ptr(o, "o"));
+    if (batch < 1) return fail(ATTN_ERR_INVALID_ARG, "attn_decode_paged_q8: batch %d must be >= 1", batch);
+    TRY(check_heads(num_heads, num_kv_heads, head_dim));
+    if (page_size != 16)
+        return fail(ATTN_ERR_UNSUPPORTED, "attn_decode_paged_q8: page_size %d is not built; requires page_size 16",
+                    page_size);
+    if (num_pages < 1 || max_pages_per_seq < 1)
+        return fail(ATTN_ERR_INVALID_ARG, "attn_decode_paged_q8: num_pages and max_pages_per_seq must be >= 1");
+    TRY(check_scalars(sliding_window, attn_softcap, scale));
+    if ((long)num_pages * page_size * num_kv_heads * head_dim > kMaxElems ||
+        (long)max_pages_per_seq * page_size > 0x7fffffffL)
+        return fail(ATTN_ERR_INVALID_ARG, "attn_decode_paged_q8: cache too large");
+    const int max_len = max_pages_per_seq * page_size;
+    const int eff = (sliding_window > 0 && sliding_window < max_len) ? sliding_window : max_len;
+    const DecodePlan plan = plan_decode(batch, num_heads, num_kv_heads, head_dim, eff, true);
+    const WorkspaceLayout wl = workspace_layout(batch, num_heads, num_kv_heads, head_dim, plan);
+    if (!workspace) return fail(ATTN_ERR_WORKSPACE, "attn_decode_paged_q8: workspace must not be null");
+    if (!aligned(workspace, 256))
+        return fail(ATTN_ERR_WORKSPACE, "attn_decode_paged_q8: workspace must be 256-byte aligned");
+    if (workspace_bytes < wl.total)
+        return fail(ATTN_ERR_WORKSPACE, "attn_decode_paged_q8: workspace of %zu bytes is smaller than the %zu required",
+                    workspace_bytes, wl.total);
+    if (batch > 65535 || (long)num_kv_heads * plan.nch > 65535)
+        return fail(ATTN_ERR_INVALID_ARG, "attn_decode_paged_q8: grid too large");
+    ta03::DecodeParams d{};
+    d.q = q; d.k = k_pages; d.v = v_pages;
+    d.k_scales = k_scales; d.v_scales = v_scales;
+    d.page_table = page_table; d.kv_lens = kv_lens; d.o = o;
+    char* ws = reinterpret_cast<char*>(workspace);
+    d.part_o = reinterpret_cast<float*>(ws + wl.o_off);
+    d.part_m = reinterpret_cast<float*>(ws + wl.m_off);
+    d.part_l = reinterpret_cast<float*>(ws + wl.l_off);
+    d.tickets = reinterpret_cast<uint32_t*>(ws + wl.t_off);
+    d.H = num_heads; d.Hkv = num_kv_heads; d.kv_len = 0;
+    d.num_pages = num_pages; d.max_pages = max_pages_per_seq;
+    fill_scalars(d, sliding_window, attn_softcap, scale);
+    d.split_tokens = plan.split_tokens;
+    d.n_split_max = plan.n_split;
+    return launch_status(ta03::launch_decode(d, head_dim, plan.gc, true, batch,
+                                             reinterpret_cast<hipStream_t>(stream)),
+                         "attn_decode_paged_q8");
+}
+
+const char* attn_last_error(void) { return g_err; }
+
+}  // extern "C"

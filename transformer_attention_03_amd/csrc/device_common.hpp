@@ -1,0 +1,99 @@
+// Device helpers shared by the attention kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ta03 {
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef float float4_t __attribute__((ext_vector_type(4)));
+typedef float float16_t __attribute__((ext_vector_type(16)));
+
+// 2^x on the transcendental unit (v_exp_f32).  exp2(-inf) = 0.
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// 1/x on the transcendental unit (v_rcp_f32, 1 ulp).
+__device__ __forceinline__ float fast_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
+
+// tanh from the identity tanh(x) = 1 - 2 / (exp(2x) + 1), with exp(2x) = 2^(2x log2 e).
+// For large |x| the exponential saturates to 0 or +inf and the result to -1 or +1.
+// Absolute error is a few f32 ulps of 1 (cancellation near 0 costs relative, not
+// absolute, accuracy), which is what a logit cap c * tanh(s / c) needs.
+__device__ __forceinline__ float tanh_via_exp(float x) {
+    const float e = fast_exp2(x * (2.0f * kLog2e));
+    return 1.0f - 2.0f * fast_rcp(e + 1.0f);
+}
+
+// ---- cross-lane helpers (DPP inside a row of 16 lanes, ds_bpermute across rows) ------------
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, true));
+}
+// quad_perm encodings: xor 1 -> [1,0,3,2], xor 2 -> [2,3,0,1]
+constexpr int kDppXor1 = 0xB1;
+constexpr int kDppXor2 = 0x4E;
+constexpr int kDppHalfMirror = 0x141;   // lane i <-> 7 - i inside each group of 8
+constexpr int kDppMirror = 0x140;       // lane i <-> 15 - i inside each row of 16
+
+__device__ __forceinline__ float shfl_xor_f(float x, int m) {
+    return __shfl_xor(x, m, 64);
+}
+
+// Sum over aligned groups of N lanes (N in 1,2,4,8,16,32,64); every lane gets the sum.
+template <int N>
+__device__ __forceinline__ float group_sum(float x) {
+    if constexpr (N >= 2) x += dpp_f<kDppXor1>(x);
+    if constexpr (N >= 4) x += dpp_f<kDppXor2>(x);
+    if constexpr (N >= 8) x += dpp_f<kDppHalfMirror>(x);
+    if constexpr (N >= 16) x += dpp_f<kDppMirror>(x);
+    if constexpr (N >= 32) x += shfl_xor_f(x, 16);
+    if constexpr (N >= 64) x += shfl_xor_f(x, 32);
+    return x;
+}
+
+// Max over lanes that are congruent modulo N (N = 1..64, power of two): reduces across
+// the 64/N groups of N lanes.  Every lane gets the max of its residue class.
+template <int N>
+__device__ __forceinline__ float strided_max(float x) {
+#pragma unroll
+    for (int m = N; m < 64; m <<= 1) x = fmaxf(x, shfl_xor_f(x, m));
+    return x;
+}
+template <int N>
+__device__ __forceinline__ float strided_sum(float x) {
+#pragma unroll
+    for (int m = N; m < 64; m <<= 1) x += shfl_xor_f(x, m);
+    return x;
+}
+
+// ---- memory ---------------------------------------------------------------------------------
+
+__device__ __forceinline__ uint4 ld_global_b128(const void* p) {
+    return *reinterpret_cast<const uint4*>(p);
+}
+
+// int8 x 16 in a uint4 -> 16 floats
+__device__ __forceinline__ void i8x16_to_f32(const uint4& w, float* f) {
+    const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+        for (int b = 0; b < 4; ++b)
+            f[4 * i + b] = (float)(int8_t)((ws[i] >> (8 * b)) & 0xFF);
+    }
+}
+
+// f16 x 8 in a uint4 -> 8 floats
+__device__ __forceinline__ void f16x8_to_f32(const uint4& w, float* f) {
+    half8_t h = __builtin_bit_cast(half8_t, w);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) f[i] = (float)h[i];
+}
+
+}  // namespace ta03

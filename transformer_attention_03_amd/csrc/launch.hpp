@@ -1,0 +1,60 @@
+// Kernel parameter blocks and launchers shared between the host API and the kernels.
+// The fields mirror the attention parameter block of doppler (gpu/kernels/attention.js,
+// createAttentionUniformBuffer), passed by value as kernel arguments instead of a uniform
+// buffer.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace ta03 {
+
+struct DecodeParams {
+    const float* q;            // [B][H][D] f32
+    const void* k;             // f16 [Hkv][kv_len][D]  or  int8 pages [P][16][Hkv][D]
+    const void* v;
+    const float* k_scales;     // paged: [P][16][Hkv]
+    const float* v_scales;
+    const int32_t* page_table; // paged: [B][max_pages]
+    const int32_t* kv_lens;    // paged: [B] (device)
+    float* o;                  // [B][H][D] f32
+    float* part_o;             // [B][H][n_split_max][D]
+    float* part_m;             // [B][H][n_split_max]
+    float* part_l;             // [B][H][n_split_max]
+    uint32_t* tickets;         // [B][Hkv * head_chunks], zero between calls
+    int H, Hkv;
+    int kv_len;                // contiguous cache length (unused when paged)
+    int num_pages, max_pages;
+    int window;
+    float scale, scale_log2;   // scale and scale * log2(e)
+    float softcap, inv_softcap;
+    int split_tokens;          // logical tokens per workgroup
+    int n_split_max;           // grid.x
+};
+
+struct FwdParams {
+    const void* q;             // element strides below
+    const void* k;
+    const void* v;
+    void* o;
+    long q_row, q_head;        // strides (elements) between query rows / query heads
+    long k_row, k_head;        // same for K and V
+    long o_row, o_head;
+    int seq_len, kv_len;
+    int H, Hkv;
+    int causal, window;
+    float scale, scale_log2;
+    float softcap, inv_softcap;
+    int n_qblocks;             // query blocks per head
+};
+
+hipError_t launch_decode(const DecodeParams& p, int head_dim, int gc, bool paged, int batch,
+                         hipStream_t st);
+int decode_tokens_per_block(int head_dim, bool paged);
+
+// dtype: 0 f32, 1 f16
+hipError_t launch_fwd(const FwdParams& p, int head_dim, int dtype, hipStream_t st);
+int fwd_block_rows(int head_dim, int dtype);
+
+}  // namespace ta03
