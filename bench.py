@@ -1,0 +1,468 @@
+"""Throughput of the attention hot path on one MI355X, against the roofline.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload decode_f16]
+                    [--only-headline] [--no-cpu-baseline]
+
+A step is one call of the workload's entry point over one batch of synthetic input
+(inputs already resident in HBM).  The headline workload is single-token decode over a
+contiguous f16 KV cache (32 query / 8 KV heads, head_dim 128, kv_len 4096); the other
+four workloads (f32 causal prefill, f16 windowed+softcapped GQA prefill, f16 vision,
+batched paged int8 decode) are measured on the same JSON line under "workloads".
+
+Timing: W untimed steps, then K steps between HIP events recorded on the stream the
+kernels run on, after a device synchronisation on both sides.  Every workload rotates
+over enough independent input copies (>= 1 GiB in total) that each step reads its
+operands from HBM, not from the 256 MB Infinity Cache.
+
+The cpu_baseline leg times the float64 oracle (test infrastructure) on the host cores,
+on the same workload, repeated for about ten seconds.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "attention TFLOP/s (prefill/vision) and KV GB/s (decode), % of MI355X roofline"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+MFMA_F16_PEAK_TFS = 2500.0     # dense f16 MFMA, TFLOP/s
+F32_PEAK_TFS = 157.3           # f32 (vector and matrix), TFLOP/s
+ROTATE_BYTES = 1 << 30
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="decode_f16",
+                    choices=["decode_f16", "prefill_f32", "prefill_f16", "vision_f16",
+                             "decode_paged_q8"])
+    ap.add_argument("--only-headline", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--profile-steps", type=int, default=0,
+                    help="run only this many steps of the headline workload (for profilers)")
+    return ap.parse_args()
+
+
+# ---------------------------------------------------------------------------------------------
+# workloads
+# ---------------------------------------------------------------------------------------------
+
+class Workload:
+    name = ""
+    kind = ""            # "hbm" or "mfma" or "f32"
+    desc = {}
+
+    def units(self):
+        """(algorithmic amount per step, unit): bytes for HBM-bound, FLOPs otherwise."""
+        raise NotImplementedError
+
+
+def n_copies(bytes_per_copy):
+    return max(2, min(512, int(math.ceil(ROTATE_BYTES / max(1, bytes_per_copy)))))
+
+
+def log(msg):
+    print("[bench] " + msg, file=sys.stderr, flush=True)
+
+
+class DecodeF16(Workload):
+    name = "decode_f16"
+    kind = "hbm"
+    kernel = "decode_split_kernel<128, 4, false>"
+
+    def __init__(self, dev, H=32, Hkv=8, D=128, L=4096):
+        import numpy as np
+        import torch
+
+        import synth
+        import transformer_attention_03_amd as ta
+        self.ta, self.torch = ta, torch
+        self.H, self.Hkv, self.D, self.L = H, Hkv, D, L
+        self.q_np, self.k_np, self.v_np = synth.decode_inputs(synth.seed_of(2), H, Hkv, D, L)
+        kv_bytes = 2 * Hkv * L * D * 2
+        self.nc = n_copies(kv_bytes)
+        k = torch.from_numpy(self.k_np).to(dev)
+        v = torch.from_numpy(self.v_np).to(dev)
+        self.q = torch.from_numpy(self.q_np).to(dev)
+        self.ks = [k.clone() for _ in range(self.nc)]
+        self.vs = [v.clone() for _ in range(self.nc)]
+        self.o = torch.empty((H, D), dtype=torch.float32, device=dev)
+        self.ws = ta.decode_workspace(1, H, Hkv, D, L, dev)
+        self.scale = 1.0 / math.sqrt(D)
+        self.desc = {"workload": "single-token decode, f16 KV cache [8, 4096, 128], f32 q "
+                                 "[32, 128], GQA 32/8, scale 1/sqrt(128)",
+                     "batch": 1, "num_heads": H, "num_kv_heads": Hkv, "head_dim": D,
+                     "kv_len": L, "kv_dtype": "f16", "q_dtype": "f32", "input_copies": self.nc}
+
+    def step(self, i):
+        j = i % self.nc
+        self.ta.attn_decode(self.q, self.ks[j], self.vs[j], self.o, self.ws, scale=self.scale)
+
+    def units(self):
+        b = 2 * self.Hkv * self.L * self.D * 2 + 2 * self.H * self.D * 4
+        return b, "bytes"
+
+    def check(self):
+        import numpy as np
+
+        import oracle
+        self.step(0)
+        self.torch.cuda.synchronize()
+        want = oracle.attention(self.q_np[None, None], np.transpose(self.k_np, (1, 0, 2))[None],
+                                np.transpose(self.v_np, (1, 0, 2))[None], causal=True,
+                                scale=self.scale)[0, 0]
+        return float(np.abs(self.o.cpu().numpy() - want).max())
+
+    def cpu_run(self, threads):
+        import numpy as np
+
+        import oracle
+        return oracle.attention(self.q_np[None, None], np.transpose(self.k_np, (1, 0, 2))[None],
+                                np.transpose(self.v_np, (1, 0, 2))[None], causal=True,
+                                scale=self.scale, threads=threads)
+
+
+class PagedQ8(Workload):
+    name = "decode_paged_q8"
+    kind = "hbm"
+    kernel = "decode_split_kernel<128, 4, true>"
+
+    def __init__(self, dev):
+        import numpy as np
+        import torch
+
+        import synth
+        import transformer_attention_03_amd as ta
+        self.ta, self.torch = ta, torch
+        c = synth.seed_of(5)
+        self.lens = synth.paged_kv_lens(c, 8, 16384, 32768)
+        d = synth.paged_inputs(c, 8, 32, 8, 128, self.lens, n_poison=64, max_pages=2048)
+        self.d = d
+        t = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to(dev)
+        self.q = t(d["q"])
+        self.kl = t(d["kv_lens"])
+        self.pt = t(d["page_table"])
+        per = d["k_pages"].nbytes * 2 + d["k_scales"].nbytes * 2
+        self.nc = n_copies(per)
+        kp, vp, ks, vs = t(d["k_pages"]), t(d["v_pages"]), t(d["k_scales"]), t(d["v_scales"])
+        self.copies = [(kp, vp, ks, vs)] + [(kp.clone(), vp.clone(), ks.clone(), vs.clone())
+                                            for _ in range(self.nc - 1)]
+        self.o = torch.empty((8, 32, 128), dtype=torch.float32, device=dev)
+        self.ws = ta.decode_workspace(8, 32, 8, 128, 2048 * 16, dev)
+        self.desc = {"workload": "batched paged int8 decode, batch 8, kv_len ~ U[16384, 32768] "
+                                 "(seeded), 16-token pages placed by a seeded permutation, f32 q, "
+                                 "GQA 32/8, head_dim 128",
+                     "batch": 8, "num_heads": 32, "num_kv_heads": 8, "head_dim": 128,
+                     "kv_lens": [int(x) for x in self.lens], "page_size": 16,
+                     "kv_dtype": "int8", "q_dtype": "f32", "input_copies": self.nc}
+
+    def step(self, i):
+        kp, vp, ks, vs = self.copies[i % self.nc]
+        self.ta.attn_decode_paged_q8(self.q, kp, vp, ks, vs, self.pt, self.kl, self.o, self.ws,
+                                     scale=1 / math.sqrt(128))
+
+    def units(self):
+        tok = int(sum(int(x) for x in self.lens))
+        pages = sum((int(x) + 15) // 16 for x in self.lens)
+        b = tok * 8 * (128 + 128 + 4 + 4) + pages * 4 + 2 * 8 * 32 * 128 * 4
+        return b, "bytes"
+
+    def check(self):
+        import numpy as np
+
+        import oracle
+        self.step(0)
+        self.torch.cuda.synchronize()
+        got = self.o.cpu().numpy()
+        err = 0.0
+        for b in range(8):
+            want = self._oracle_b(b, None)
+            err = max(err, float(np.abs(got[b] - want).max()))
+        return err
+
+    def _oracle_b(self, b, threads):
+        import oracle
+        d = self.d
+        k = oracle.dequant_i8(d["k_q"][b], d["k_s"][b])[None]
+        v = oracle.dequant_i8(d["v_q"][b], d["v_s"][b])[None]
+        return oracle.attention(d["q"][b][None, None], k, v, causal=True,
+                                scale=1 / math.sqrt(128), threads=threads)[0, 0]
+
+    def cpu_run(self, threads):
+        return [self._oracle_b(b, threads) for b in range(8)]
+
+
+class Forward(Workload):
+    """Prefill (token-major) or vision (head-major) forward."""
+
+    def __init__(self, dev, name):
+        import numpy as np
+        import torch
+
+        import synth
+        import transformer_attention_03_amd as ta
+        self.ta, self.torch, self.name = ta, torch, name
+        if name == "prefill_f32":
+            self.S, self.H, self.Hkv, self.D, self.causal, self.W, self.cap = 128, 1, 1, 64, True, 0, 0.0
+            q, k, v = synth.prefill_inputs(synth.seed_of(1), 128, 128, 1, 1, 64, "f32")
+            self.kind = "f32"
+            self.kernel = "fwd_f32_kernel<64>"
+            self.desc = {"workload": "causal prefill, f32, 1 sequence, 1 head, seq_len 128, "
+                                     "head_dim 64, scale 1/8"}
+        elif name == "prefill_f16":
+            self.S, self.H, self.Hkv, self.D, self.causal, self.W, self.cap = 2048, 16, 8, 256, True, 512, 50.0
+            q, k, v = synth.prefill_inputs(synth.seed_of(3), 2048, 2048, 16, 8, 256, "f16")
+            self.kind = "mfma"
+            self.kernel = "fwd_f16_kernel<256>"
+            self.desc = {"workload": "causal GQA prefill, f16, 2048 tokens, 16/8 heads, head_dim "
+                                     "256, sliding window 512, softcap 50, scale 1/16"}
+        else:
+            self.S, self.H, self.Hkv, self.D, self.causal, self.W, self.cap = 2304, 16, 16, 64, False, 0, 0.0
+            q, k, v = synth.vision_inputs(synth.seed_of(4), 2304, 16, 64)
+            self.kind = "mfma"
+            self.kernel = "fwd_f16_kernel<64>"
+            self.desc = {"workload": "bidirectional vision attention, f16 [16, 2304, 64] "
+                                     "head-major, scale 1/8"}
+        self.vision = name == "vision_f16"
+        self.scale = 1.0 / math.sqrt(self.D)
+        self.np_in = (q, k, v)
+        tq, tk, tv = (torch.from_numpy(np.ascontiguousarray(x)).to(dev) for x in (q, k, v))
+        per = tq.nbytes + tk.nbytes + tv.nbytes
+        self.nc = n_copies(per)
+        self.copies = [(tq, tk, tv)] + [(tq.clone(), tk.clone(), tv.clone())
+                                        for _ in range(self.nc - 1)]
+        self.o = torch.empty_like(tq)
+        self.desc["input_copies"] = self.nc
+
+    def live_pairs(self):
+        S = L = self.S
+        if not self.causal:
+            return S * L
+        tot = 0
+        for i in range(S):
+            p = L - S + i
+            lo = max(0, p - self.W + 1) if self.W > 0 else 0
+            tot += p + 1 - lo
+        return tot
+
+    def step(self, i):
+        q, k, v = self.copies[i % self.nc]
+        if self.vision:
+            self.ta.attn_vision(q, k, v, self.o, scale=self.scale)
+        else:
+            self.ta.attn_prefill(q, k, v, self.o, causal=self.causal, scale=self.scale,
+                                 sliding_window=self.W, attn_softcap=self.cap)
+
+    def units(self):
+        return 4 * self.D * self.live_pairs() * self.H, "flops"
+
+    def _oracle_rows(self, rows, threads):
+        import numpy as np
+
+        import oracle
+        q, k, v = self.np_in
+        if self.vision:
+            q, k, v = (np.transpose(x, (1, 0, 2)) for x in (q, k, v))
+        out = []
+        for i in rows:
+            hi = i + 1 if self.causal else k.shape[0]
+            out.append(oracle.attention(q[None, i:i + 1], k[None, :hi], v[None, :hi],
+                                        causal=self.causal, window=self.W, softcap=self.cap,
+                                        scale=self.scale, threads=threads)[0, 0])
+        return np.stack(out)
+
+    def check(self):
+        import numpy as np
+        self.step(0)
+        self.torch.cuda.synchronize()
+        got = self.o.cpu().numpy().astype(np.float64)
+        if self.vision:
+            got = np.transpose(got, (1, 0, 2))
+        rows = sorted(set([0, 1, self.S // 3, self.S // 2, self.S - 2, self.S - 1]))
+        return float(np.abs(got[rows] - self._oracle_rows(rows, None)).max())
+
+    def cpu_rows(self):
+        """A bounded sample of query rows (spread over the sequence) for the CPU baseline."""
+        n = min(self.S, 64)
+        return [int(round(i * (self.S - 1) / max(1, n - 1))) for i in range(n)]
+
+    def cpu_run(self, threads):
+        return self._oracle_rows(self.cpu_rows(), threads)
+
+
+def make(name, dev):
+    if name == "decode_f16":
+        return DecodeF16(dev)
+    if name == "decode_paged_q8":
+        return PagedQ8(dev)
+    return Forward(dev, name)
+
+
+# ---------------------------------------------------------------------------------------------
+# measurement
+# ---------------------------------------------------------------------------------------------
+
+def time_steps(wl, steps, warmup):
+    import torch
+    for i in range(warmup):
+        wl.step(i)
+    torch.cuda.synchronize()
+    st = torch.cuda.current_stream()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(st)
+    for i in range(steps):
+        wl.step(warmup + i)
+    e1.record(st)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps      # ms per step
+
+
+def summarize(wl, ms):
+    amount, unit = wl.units()
+    sec = ms * 1e-3
+    if unit == "bytes":
+        gbs = amount / sec / 1e9
+        return {"value": gbs, "unit": "GB/s", "bound": "hbm", "achieved": gbs,
+                "peak": HBM_PEAK_GBS, "peak_unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
+                "algorithmic_bytes": amount, "us_per_call": ms * 1e3}
+    tfs = amount / sec / 1e12
+    peak = F32_PEAK_TFS if wl.kind == "f32" else MFMA_F16_PEAK_TFS
+    return {"value": tfs, "unit": "TFLOP/s", "bound": "mfma", "achieved": tfs, "peak": peak,
+            "peak_unit": "TFLOP/s", "frac": tfs / peak, "algorithmic_flops": amount,
+            "us_per_call": ms * 1e3}
+
+
+def traffic_for(kernel_src, kernel):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or None when the
+    kernel source changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        rec = json.load(open(path)).get(kernel)
+    except Exception:
+        return None
+    if not rec:
+        return None
+    h = hashlib.sha256(open(kernel_src, "rb").read()).hexdigest()[:16]
+    if rec.get("source_sha256_16") != h:
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(wl, budget_s=10.0):
+    import oracle
+    threads = oracle.default_threads()
+    times = []
+    t_start = time.perf_counter()
+    while True:
+        t0 = time.perf_counter()
+        wl.cpu_run(threads)
+        times.append(time.perf_counter() - t0)
+        if len(times) >= 3 and time.perf_counter() - t_start > budget_s:
+            break
+        if len(times) >= 200:
+            break
+    times.sort()
+    med = times[len(times) // 2]
+    amount, unit = wl.units()
+    if isinstance(wl, Forward):
+        frac = len(wl.cpu_rows()) / wl.S        # rows sampled; work scales with visible keys
+        rows = wl.cpu_rows()
+        if wl.causal:
+            full = wl.live_pairs()
+            part = 0
+            for i in rows:
+                lo = max(0, i - wl.W + 1) if wl.W > 0 else 0
+                part += i + 1 - lo
+            frac = part / full
+        amount = amount * frac
+        sample = "%d of %d query rows, all %d heads, %d repeats" % (len(rows), wl.S, wl.H,
+                                                                    len(times))
+    else:
+        sample = "the full workload, %d repeats" % len(times)
+    val = amount / med / (1e9 if unit == "bytes" else 1e12)
+    return {"value": val, "unit": "GB/s" if unit == "bytes" else "TFLOP/s", "cores": threads,
+            "kind": "oracle", "sample": sample + " (median %.3f s per repeat)" % med}
+
+
+def main():
+    a = parse()
+    if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (the hot path "
+              "shards by head, query block or sequence with no exchange; see the design notes). "
+              "Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import transformer_attention_03_amd as ta
+    if not os.path.exists(ta.LIB_PATH):
+        from transformer_attention_03_amd import build as b
+        b.build()
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+
+    log("preparing %s" % a.workload)
+    head = make(a.workload, dev)
+    if a.profile_steps:
+        for i in range(a.profile_steps):
+            head.step(i)
+        torch.cuda.synchronize()
+        print(json.dumps({"profiled_workload": head.name, "steps": a.profile_steps}))
+        return
+
+    err = head.check()
+    log("%s max-abs error vs oracle %.3g; timing %d steps" % (head.name, err, a.steps))
+    ms = time_steps(head, a.steps, a.warmup)
+    s = summarize(head, ms)
+    src = os.path.join(ROOT, "transformer_attention_03_amd", "csrc",
+                       "decode.hip" if head.kind == "hbm" else "fwd.hip")
+    roof = {"bound": s["bound"], "achieved": round(s["achieved"], 3), "peak": s["peak"],
+            "unit": s["peak_unit"], "frac": round(s["frac"], 4),
+            "traffic": traffic_for(src, head.kernel), "kernel": head.kernel}
+    out = {"metric": METRIC, "value": round(s["value"], 3), "unit": s["unit"], "n_gpus": 1,
+           "steps": a.steps, "warmup": a.warmup, "ms_per_step": round(ms, 6),
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+           "dtype": "f32" if head.kind != "mfma" else "f16",
+           "data": "synthetic (seeded SplitMix64 + Box-Muller, N(0,1))",
+           "config": dict(head.desc), "roofline": roof, "max_abs_err_vs_oracle": err}
+    if not a.no_cpu_baseline:
+        log("cpu baseline (oracle)")
+        out["cpu_baseline"] = cpu_baseline(head)
+    if not a.only_headline:
+        others = {}
+        for name in ("prefill_f32", "prefill_f16", "vision_f16", "decode_paged_q8"):
+            if name == head.name:
+                continue
+            log("preparing %s" % name)
+            wl = make(name, dev)
+            e = wl.check()
+            log("%s max-abs error vs oracle %.3g" % (name, e))
+            ms_w = time_steps(wl, max(20, a.steps // 4), a.warmup)
+            sw = summarize(wl, ms_w)
+            others[name] = {"config": wl.desc, "us_per_call": round(sw["us_per_call"], 3),
+                            "value": round(sw["value"], 3), "unit": sw["unit"],
+                            "roofline": {"bound": sw["bound"], "peak": sw["peak"],
+                                         "frac": round(sw["frac"], 4), "kernel": wl.kernel},
+                            "max_abs_err_vs_oracle": e}
+            del wl
+            torch.cuda.empty_cache()
+        out["workloads"] = others
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

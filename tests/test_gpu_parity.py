@@ -55,7 +55,8 @@ def run_decode(dev, q, k, v, W=0, cap=0.0, scale=None):
     ws = ta.decode_workspace(1, H, Hkv, D, L, dev)
     ta.attn_decode(qd, kd, vd, od, ws, scale=scale, sliding_window=W, attn_softcap=cap)
     torch.cuda.synchronize()
-    assert int(ws.sum().item()) == 0 or True   # partials may remain; counters checked below
+    # the arrival counters (at the end of the workspace) are left at zero
+    assert int(ws[-256:].sum().item()) == 0
     return od.cpu().numpy(), ws
 
 

@@ -79,7 +79,7 @@ struct DecodePlan {
 };
 
 int heads_per_wg(int group) {
-    for (int gc : {8, 4, 2, 1})
+    for (int gc : {4, 2, 1})
         if (group % gc == 0) return gc;
     return 1;
 }
@@ -90,7 +90,8 @@ DecodePlan plan_decode(int batch, int num_heads, int num_kv_heads, int head_dim,
     const int group = num_heads / num_kv_heads;
     p.gc = heads_per_wg(group);
     p.nch = group / p.gc;
-    const int min_t = 4 * ta03::decode_tokens_per_block(head_dim, paged);   // one block per wave
+    // one block per wave at least
+    const int min_t = ta03::decode_waves() * ta03::decode_tokens_per_block(head_dim, paged);
     int t = g_split_override;
     if (t <= 0) {
         // aim for about eight workgroups per compute unit over 256 CUs
@@ -99,6 +100,9 @@ DecodePlan plan_decode(int batch, int num_heads, int num_kv_heads, int head_dim,
         t = (int)(((want + min_t - 1) / min_t) * min_t);
         if (t < min_t) t = min_t;
     }
+    // the merge holds at most decode_max_splits() partials per (sequence, head)
+    const int cap = ta03::decode_max_splits();
+    if ((eff_len + t - 1) / t > cap) t = (((eff_len + cap - 1) / cap) + 15) / 16 * 16;
     p.split_tokens = t;
     p.n_split = (eff_len + t - 1) / t;
     if (p.n_split < 1) p.n_split = 1;

@@ -12,6 +12,8 @@ typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 typedef float float4_t __attribute__((ext_vector_type(4)));
+typedef float float2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef float float16_t __attribute__((ext_vector_type(16)));
 
 // 2^x on the transcendental unit (v_exp_f32).  exp2(-inf) = 0.
@@ -74,6 +76,17 @@ __device__ __forceinline__ float strided_sum(float x) {
 
 // ---- memory ---------------------------------------------------------------------------------
 
+// Device-scope (all XCDs) relaxed store / load: written through, resp. fetched past, the
+// XCD-private L2, so another workgroup on any XCD observes them without cache-wide fences.
+__device__ __forceinline__ void store_agent(float* p, float v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float load_agent(const float* p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// Wait until this wave's outstanding vector-memory operations (including stores) completed.
+__device__ __forceinline__ void wait_stores_complete() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
 __device__ __forceinline__ uint4 ld_global_b128(const void* p) {
     return *reinterpret_cast<const uint4*>(p);
 }
@@ -86,6 +99,15 @@ __device__ __forceinline__ void i8x16_to_f32(const uint4& w, float* f) {
 #pragma unroll
         for (int b = 0; b < 4; ++b)
             f[4 * i + b] = (float)(int8_t)((ws[i] >> (8 * b)) & 0xFF);
+    }
+}
+
+// int8 x 8 in two words -> 8 floats
+__device__ __forceinline__ void i8x8_to_f32(uint32_t lo, uint32_t hi, float* f) {
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+        f[b] = (float)(int8_t)((lo >> (8 * b)) & 0xFF);
+        f[4 + b] = (float)(int8_t)((hi >> (8 * b)) & 0xFF);
     }
 }
 

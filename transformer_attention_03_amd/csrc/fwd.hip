@@ -80,33 +80,101 @@ __device__ __forceinline__ float score_transform(const FwdParams& a, float s) {
 // =============================================================================================
 // f16 inputs, f32 accumulation: v_mfma_f32_16x16x32_f16
 // =============================================================================================
+//
+// LDS holds two stages of (K tile, V^T tile).  K rows are padded by 16 bytes; V^T rows are
+// not padded but each 4-key group is XOR-swizzled by (d mod 16), so both the transposing
+// writes and the 8-byte fragment reads of 16 consecutive d rows hit distinct banks.
+// The next tile's global loads are issued into registers before the current tile is
+// computed and written to the other LDS stage afterwards: one barrier per tile.
 
-template <int D>
+template <int D, int QB_, int NW_>
 struct F16Shape {
-    static constexpr int NW = 4;                  // waves per workgroup
-    static constexpr int QB = 2;                  // 16-row query blocks per wave
+    static constexpr int NW = NW_;                // waves per workgroup
+    static constexpr int QB = QB_;                // 16-row query blocks per wave
+    static constexpr int NT = 64 * NW;
     static constexpr int BM = NW * QB * 16;       // query rows per workgroup
     static constexpr int BN = 64;                 // keys per tile
     static constexpr int KLD = D + 8;             // K row stride in LDS (halves)
-    static constexpr int VLD = BN + 4;            // V^T row stride in LDS (halves)
-    static constexpr int KCH = BN * D / 8 / 256;  // 16-byte K chunks per thread per tile
+    static constexpr int VLD = BN;                // V^T row stride in LDS (halves)
+    static constexpr int KCH = BN * D / 8 / NT;   // 16-byte K chunks per thread per tile
     static constexpr int VGRP = (BN / 4) * (D / 8);        // 4-key x 8-d groups per tile
-    static constexpr int VG_PER_T = (VGRP + 255) / 256;    // per thread
+    static constexpr int VGT = (VGRP + NT - 1) / NT;       // per thread
     static constexpr int DC = D / 32;             // 32-wide k chunks of the QK^T product
     static constexpr int NDB = D / 16;            // 16-row d blocks of O^T
     static constexpr int NKB = BN / 16;           // 16-key blocks of S^T
+    static_assert(KCH * NT == BN * D / 8, "K tile split");
 };
 
-template <int D>
-__global__ void __launch_bounds__(256) fwd_f16_kernel(FwdParams a) {
-    using S = F16Shape<D>;
-    __shared__ __attribute__((aligned(16))) _Float16 k_lds[S::BN * S::KLD];
-    __shared__ __attribute__((aligned(16))) _Float16 vt_lds[D * S::VLD];
+// V^T element (d, key) lives at row d, column 4 * ((key / 4) ^ (d & 15)) + key % 4.
+__device__ __forceinline__ int vt_col(int d, int key4) { return 4 * (key4 ^ (d & 15)); }
+
+template <int D, int QB, int NW>
+__device__ __forceinline__ void f16_load_tile(const FwdParams& a, const _Float16* kg,
+                                              const _Float16* vg, int ks, int tid,
+                                              u32x4_t (&kst)[F16Shape<D, QB, NW>::KCH],
+                                              u32x4_t (&vst)[F16Shape<D, QB, NW>::VGT][4]) {
+    using S = F16Shape<D, QB, NW>;
+#pragma unroll
+    for (int i = 0; i < S::KCH; ++i) {
+        const int ci = tid + S::NT * i;
+        const int r = ci / (D / 8), c = ci % (D / 8);
+        const int key = min(ks + r, a.kv_len - 1);
+        kst[i] = *reinterpret_cast<const u32x4_t*>(kg + (long)key * a.k_row + 8 * c);
+    }
+#pragma unroll
+    for (int i = 0; i < S::VGT; ++i) {
+        const int gi = tid + S::NT * i;
+        if (gi < S::VGRP) {
+            const int k4 = gi % (S::BN / 4), c = gi / (S::BN / 4);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int key = min(ks + 4 * k4 + e, a.kv_len - 1);
+                vst[i][e] = *reinterpret_cast<const u32x4_t*>(vg + (long)key * a.k_row + 8 * c);
+            }
+        }
+    }
+}
+
+template <int D, int QB, int NW>
+__device__ __forceinline__ void f16_store_tile(_Float16* k_lds, _Float16* vt_lds, int tid,
+                                               const u32x4_t (&kst)[F16Shape<D, QB, NW>::KCH],
+                                               const u32x4_t (&vst)[F16Shape<D, QB, NW>::VGT][4]) {
+    using S = F16Shape<D, QB, NW>;
+#pragma unroll
+    for (int i = 0; i < S::KCH; ++i) {
+        const int ci = tid + S::NT * i;
+        const int r = ci / (D / 8), c = ci % (D / 8);
+        *reinterpret_cast<u32x4_t*>(&k_lds[r * S::KLD + 8 * c]) = kst[i];
+    }
+#pragma unroll
+    for (int i = 0; i < S::VGT; ++i) {
+        const int gi = tid + S::NT * i;
+        if (gi < S::VGRP) {
+            const int k4 = gi % (S::BN / 4), c = gi / (S::BN / 4);
+            const half8_t r0 = __builtin_bit_cast(half8_t, vst[i][0]);
+            const half8_t r1 = __builtin_bit_cast(half8_t, vst[i][1]);
+            const half8_t r2 = __builtin_bit_cast(half8_t, vst[i][2]);
+            const half8_t r3 = __builtin_bit_cast(half8_t, vst[i][3]);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int d = 8 * c + e;
+                *reinterpret_cast<half4_t*>(&vt_lds[d * S::VLD + vt_col(d, k4)]) =
+                    half4_t{r0[e], r1[e], r2[e], r3[e]};
+            }
+        }
+    }
+}
+
+template <int D, int QB, int NW>
+__global__ void __launch_bounds__(64 * NW) fwd_f16_kernel(FwdParams a) {
+    using S = F16Shape<D, QB, NW>;
+    __shared__ __attribute__((aligned(16))) _Float16 k_lds[2][S::BN * S::KLD];
+    __shared__ __attribute__((aligned(16))) _Float16 vt_lds[2][D * S::VLD];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int w = tid >> 6;
-    const int ln = lane & 15;          // query column inside a 16-block / row of an A tile
+    const int ln = lane & 15;          // query column of the S^T / O^T blocks; A-tile row
     const int lg = lane >> 4;          // lane group 0..3
 
     int head, qblock;
@@ -118,6 +186,10 @@ __global__ void __launch_bounds__(256) fwd_f16_kernel(FwdParams a) {
     const _Float16* qg = reinterpret_cast<const _Float16*>(a.q) + (long)head * a.q_head;
     const _Float16* kg = reinterpret_cast<const _Float16*>(a.k) + (long)kvh * a.k_head;
     const _Float16* vg = reinterpret_cast<const _Float16*>(a.v) + (long)kvh * a.k_head;
+
+    u32x4_t kst[S::KCH];
+    u32x4_t vst[S::VGT][4];
+    if (tr.kt0 < tr.kt1) f16_load_tile<D, QB, NW>(a, kg, vg, tr.kt0 * S::BN, tid, kst, vst);
 
     // ---- Q fragments (B operand of S^T = K Q^T) --------------------------------------------
     half8_t qf[S::QB][S::DC];
@@ -144,76 +216,37 @@ __global__ void __launch_bounds__(256) fwd_f16_kernel(FwdParams a) {
         l_part[qb] = 0.f;
     }
 
-    // ---- register staging of one K/V tile ------------------------------------------------
-    uint4 kst[S::KCH];
-    uint4 vst[S::VG_PER_T][4];
-    auto load_tile = [&](int kt) {
-        const int ks = kt * S::BN;
-#pragma unroll
-        for (int i = 0; i < S::KCH; ++i) {
-            const int ci = tid + 256 * i;
-            const int r = ci / (D / 8), c = ci % (D / 8);
-            const int key = min(ks + r, a.kv_len - 1);
-            kst[i] = *reinterpret_cast<const uint4*>(kg + (long)key * a.k_row + 8 * c);
-        }
-#pragma unroll
-        for (int i = 0; i < S::VG_PER_T; ++i) {
-            const int gi = tid + 256 * i;
-            if (gi < S::VGRP) {
-                const int k4 = gi / (D / 8), c = gi % (D / 8);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int key = min(ks + 4 * k4 + e, a.kv_len - 1);
-                    vst[i][e] = *reinterpret_cast<const uint4*>(vg + (long)key * a.k_row + 8 * c);
-                }
-            }
-        }
-    };
-    auto store_tile = [&]() {
-#pragma unroll
-        for (int i = 0; i < S::KCH; ++i) {
-            const int ci = tid + 256 * i;
-            const int r = ci / (D / 8), c = ci % (D / 8);
-            *reinterpret_cast<uint4*>(&k_lds[r * S::KLD + 8 * c]) = kst[i];
-        }
-#pragma unroll
-        for (int i = 0; i < S::VG_PER_T; ++i) {
-            const int gi = tid + 256 * i;
-            if (gi < S::VGRP) {
-                const int k4 = gi / (D / 8), c = gi % (D / 8);
-                const half8_t r0 = __builtin_bit_cast(half8_t, vst[i][0]);
-                const half8_t r1 = __builtin_bit_cast(half8_t, vst[i][1]);
-                const half8_t r2 = __builtin_bit_cast(half8_t, vst[i][2]);
-                const half8_t r3 = __builtin_bit_cast(half8_t, vst[i][3]);
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const half4_t col = half4_t{r0[e], r1[e], r2[e], r3[e]};
-                    *reinterpret_cast<half4_t*>(&vt_lds[(8 * c + e) * S::VLD + 4 * k4]) = col;
-                }
-            }
-        }
-    };
+    const bool capped = a.softcap > 0.f;
+    // softcap in log2 units: t = C1 - C2 / (2^(s * K1) + 1), C1 = c log2 e, C2 = 2 c log2 e,
+    // K1 = 2 scale log2 e / c  (c tanh(scale s / c) = c - 2c / (exp(2 scale s / c) + 1))
+    const float K1 = 2.f * a.scale * kLog2e * a.inv_softcap;
+    const float C1 = a.softcap * kLog2e;
+    const float C2 = 2.f * C1;
 
-    if (tr.kt0 < tr.kt1) load_tile(tr.kt0);
+    if (tr.kt0 < tr.kt1) f16_store_tile<D, QB, NW>(k_lds[0], vt_lds[0], tid, kst, vst);
+    __syncthreads();
+
+    int stage = 0;
     for (int kt = tr.kt0; kt < tr.kt1; ++kt) {
-        __syncthreads();
-        store_tile();
-        __syncthreads();
-        if (kt + 1 < tr.kt1) load_tile(kt + 1);
-
+        const bool more = kt + 1 < tr.kt1;
+        if (more) f16_load_tile<D, QB, NW>(a, kg, vg, (kt + 1) * S::BN, tid, kst, vst);
+        const _Float16* kl = k_lds[stage];
+        const _Float16* vl = vt_lds[stage];
         const int ks = kt * S::BN;
         const bool masked = tile_needs_mask(a, tr, ks, S::BN);
 
         // ---- S^T = K Q^T -----------------------------------------------------------------
         float4_t st[S::NKB][S::QB];
 #pragma unroll
-        for (int kb = 0; kb < S::NKB; ++kb) {
+        for (int kb = 0; kb < S::NKB; ++kb)
 #pragma unroll
             for (int qb = 0; qb < S::QB; ++qb) st[kb][qb] = float4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int c = 0; c < S::DC; ++c) {
+        for (int c = 0; c < S::DC; ++c) {
+#pragma unroll
+            for (int kb = 0; kb < S::NKB; ++kb) {
                 const half8_t kf =
-                    *reinterpret_cast<const half8_t*>(&k_lds[(16 * kb + ln) * S::KLD + 32 * c + 8 * lg]);
+                    *reinterpret_cast<const half8_t*>(&kl[(16 * kb + ln) * S::KLD + 32 * c + 8 * lg]);
 #pragma unroll
                 for (int qb = 0; qb < S::QB; ++qb)
                     st[kb][qb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf, qf[qb][c], st[kb][qb], 0, 0, 0);
@@ -224,16 +257,30 @@ __global__ void __launch_bounds__(256) fwd_f16_kernel(FwdParams a) {
         half8_t pf[S::QB][S::BN / 32];
 #pragma unroll
         for (int qb = 0; qb < S::QB; ++qb) {
-            float mx = -INFINITY;
+            if (capped) {
+#pragma unroll
+                for (int kb = 0; kb < S::NKB; ++kb)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const float e2 = fast_exp2(st[kb][qb][i] * K1);
+                        st[kb][qb][i] = __builtin_fmaf(-C2, fast_rcp(e2 + 1.f), C1);
+                    }
+            } else {
+#pragma unroll
+                for (int kb = 0; kb < S::NKB; ++kb) st[kb][qb] *= a.scale_log2;
+            }
+            if (masked) {
+#pragma unroll
+                for (int kb = 0; kb < S::NKB; ++kb)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        st[kb][qb][i] += visible(a, ks + 16 * kb + 4 * lg + i, qpos[qb]) ? 0.f : -INFINITY;
+            }
+            float mx = st[0][qb][0];
 #pragma unroll
             for (int kb = 0; kb < S::NKB; ++kb)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    float t = score_transform(a, st[kb][qb][i]);
-                    if (masked && !visible(a, ks + 16 * kb + 4 * lg + i, qpos[qb])) t = -INFINITY;
-                    st[kb][qb][i] = t;
-                    mx = fmaxf(mx, t);
-                }
+                for (int i = (kb == 0 ? 1 : 0); i < 4; ++i) mx = fmaxf(mx, st[kb][qb][i]);
             mx = fmaxf(mx, shfl_xor_f(mx, 16));
             mx = fmaxf(mx, shfl_xor_f(mx, 32));
             if (__builtin_amdgcn_ballot_w64(mx > m_run[qb] + kSlack) != 0) {
@@ -244,60 +291,64 @@ __global__ void __launch_bounds__(256) fwd_f16_kernel(FwdParams a) {
 #pragma unroll
                 for (int db = 0; db < S::NDB; ++db) acc_o[db][qb] *= alpha;
             }
+            const float mq = m_run[qb];
             float ls = 0.f;
 #pragma unroll
             for (int kb = 0; kb < S::NKB; ++kb)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const float p = fast_exp2(st[kb][qb][i] - m_run[qb]);
+                    const float p = fast_exp2(st[kb][qb][i] - mq);
                     st[kb][qb][i] = p;
                     ls += p;
                 }
             l_part[qb] += ls;
 #pragma unroll
             for (int c = 0; c < S::BN / 32; ++c) {
-                half8_t h;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    h[i] = (_Float16)st[2 * c][qb][i];
-                    h[4 + i] = (_Float16)st[2 * c + 1][qb][i];
-                }
-                pf[qb][c] = h;
+                const half2_t h0 = __builtin_convertvector(float2_t{st[2 * c][qb][0], st[2 * c][qb][1]}, half2_t);
+                const half2_t h1 = __builtin_convertvector(float2_t{st[2 * c][qb][2], st[2 * c][qb][3]}, half2_t);
+                const half2_t h2 = __builtin_convertvector(float2_t{st[2 * c + 1][qb][0], st[2 * c + 1][qb][1]}, half2_t);
+                const half2_t h3 = __builtin_convertvector(float2_t{st[2 * c + 1][qb][2], st[2 * c + 1][qb][3]}, half2_t);
+                pf[qb][c] = half8_t{h0[0], h0[1], h1[0], h1[1], h2[0], h2[1], h3[0], h3[1]};
             }
         }
 
         // ---- O^T += V^T P^T ---------------------------------------------------------------
 #pragma unroll
         for (int db = 0; db < S::NDB; ++db) {
+            const int d = 16 * db + ln;
+            const _Float16* vrow = &vl[d * S::VLD];
 #pragma unroll
             for (int c = 0; c < S::BN / 32; ++c) {
-                const _Float16* vrow = &vt_lds[(16 * db + ln) * S::VLD + 32 * c + 4 * lg];
-                const half4_t lo = *reinterpret_cast<const half4_t*>(vrow);
-                const half4_t hi = *reinterpret_cast<const half4_t*>(vrow + 16);
+                const half4_t lo = *reinterpret_cast<const half4_t*>(vrow + vt_col(d, 8 * c + lg));
+                const half4_t hi = *reinterpret_cast<const half4_t*>(vrow + vt_col(d, 8 * c + 4 + lg));
                 const half8_t vf = half8_t{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 #pragma unroll
                 for (int qb = 0; qb < S::QB; ++qb)
                     acc_o[db][qb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf, pf[qb][c], acc_o[db][qb], 0, 0, 0);
             }
         }
+
+        if (more) f16_store_tile<D, QB, NW>(k_lds[stage ^ 1], vt_lds[stage ^ 1], tid, kst, vst);
+        __syncthreads();
+        stage ^= 1;
     }
 
-    // ---- epilogue: O = O^T^T / l -----------------------------------------------------------
+    // ---- epilogue: O = (O^T)^T / l ---------------------------------------------------------
     _Float16* og = reinterpret_cast<_Float16*>(a.o) + (long)head * a.o_head;
 #pragma unroll
     for (int qb = 0; qb < S::QB; ++qb) {
         float l = l_part[qb];
         l += shfl_xor_f(l, 16);
         l += shfl_xor_f(l, 32);
-        const float inv = l > 0.f ? 1.0f / l : 0.f;
+        const float inv = l != 0.f ? 1.0f / l : 0.f;
         const int row = q0 + (w * S::QB + qb) * 16 + ln;
         if (row < a.seq_len) {
 #pragma unroll
             for (int db = 0; db < S::NDB; ++db) {
-                half4_t h;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) h[i] = (_Float16)(acc_o[db][qb][i] * inv);
-                *reinterpret_cast<half4_t*>(og + (long)row * a.o_row + 16 * db + 4 * lg) = h;
+                const half2_t lo = __builtin_convertvector(float2_t{acc_o[db][qb][0] * inv, acc_o[db][qb][1] * inv}, half2_t);
+                const half2_t hi = __builtin_convertvector(float2_t{acc_o[db][qb][2] * inv, acc_o[db][qb][3] * inv}, half2_t);
+                *reinterpret_cast<half4_t*>(og + (long)row * a.o_row + 16 * db + 4 * lg) =
+                    half4_t{lo[0], lo[1], hi[0], hi[1]};
             }
         }
     }
@@ -404,7 +455,7 @@ __global__ void __launch_bounds__(256) fwd_f32_kernel(FwdParams a) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 float t = score_transform(a, st[kb][i]);
-                if (masked && !visible(a, ks + 16 * kb + 4 * lg + i, qpos)) t = -INFINITY;
+                if (masked) t += visible(a, ks + 16 * kb + 4 * lg + i, qpos) ? 0.f : -INFINITY;
                 st[kb][i] = t;
                 mx = fmaxf(mx, t);
             }
@@ -441,7 +492,7 @@ __global__ void __launch_bounds__(256) fwd_f32_kernel(FwdParams a) {
     float l = l_part;
     l += shfl_xor_f(l, 16);
     l += shfl_xor_f(l, 32);
-    const float inv = l > 0.f ? 1.0f / l : 0.f;
+    const float inv = l != 0.f ? 1.0f / l : 0.f;
     float* og = reinterpret_cast<float*>(a.o) + (long)head * a.o_head;
     if (row < a.seq_len) {
 #pragma unroll
@@ -454,19 +505,30 @@ __global__ void __launch_bounds__(256) fwd_f32_kernel(FwdParams a) {
     }
 }
 
+// Tile configuration per head_dim: (16-row blocks per wave, waves per workgroup).
+template <int D> struct F16Cfg { static constexpr int QB = 2, NW = 4; };
+
 template <int D>
 hipError_t launch_d(const FwdParams& p, int dtype, hipStream_t st) {
     const dim3 grid(p.n_qblocks * p.H);
-    if (dtype == 1) hipLaunchKernelGGL(fwd_f16_kernel<D>, grid, dim3(256), 0, st, p);
-    else hipLaunchKernelGGL(fwd_f32_kernel<D>, grid, dim3(256), 0, st, p);
+    if (dtype == 1) {
+        constexpr int QB = F16Cfg<D>::QB, NW = F16Cfg<D>::NW;
+        hipLaunchKernelGGL((fwd_f16_kernel<D, QB, NW>), grid, dim3(64 * NW), 0, st, p);
+    } else {
+        hipLaunchKernelGGL(fwd_f32_kernel<D>, grid, dim3(256), 0, st, p);
+    }
     return hipGetLastError();
 }
 
 }  // namespace
 
 int fwd_block_rows(int head_dim, int dtype) {
-    (void)head_dim;
-    return dtype == 1 ? F16Shape<64>::BM : F32Shape<64>::BM;
+    if (dtype != 1) return F32Shape<64>::BM;
+    switch (head_dim) {
+        case 64: return F16Cfg<64>::QB * F16Cfg<64>::NW * 16;
+        case 128: return F16Cfg<128>::QB * F16Cfg<128>::NW * 16;
+        default: return F16Cfg<256>::QB * F16Cfg<256>::NW * 16;
+    }
 }
 
 hipError_t launch_fwd(const FwdParams& p, int head_dim, int dtype, hipStream_t st) {
