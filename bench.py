@@ -44,11 +44,14 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="decode_f16",
                     choices=["decode_f16", "prefill_f32", "prefill_f16", "vision_f16",
-                             "decode_paged_q8"])
+                             "decode_paged_q8", "all"])
     ap.add_argument("--only-headline", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile-steps", type=int, default=0,
-                    help="run only this many steps of the headline workload (for profilers)")
+                    help="only run this many steps of the selected workload(s), for profilers")
+    ap.add_argument("--copy-bytes", type=int, default=0,
+                    help="with --profile-steps: also run a plain device copy of this many bytes "
+                         "per step (calibrates the HBM byte counters)")
     return ap.parse_args()
 
 
@@ -299,6 +302,9 @@ class Forward(Workload):
         return self._oracle_rows(self.cpu_rows(), threads)
 
 
+ALL = ["decode_f16", "prefill_f32", "prefill_f16", "vision_f16", "decode_paged_q8"]
+
+
 def make(name, dev):
     if name == "decode_f16":
         return DecodeF16(dev)
@@ -415,15 +421,31 @@ def main():
         sys.exit(1)
     dev = torch.device("cuda:0")
 
-    log("preparing %s" % a.workload)
-    head = make(a.workload, dev)
     if a.profile_steps:
-        for i in range(a.profile_steps):
-            head.step(i)
-        torch.cuda.synchronize()
-        print(json.dumps({"profiled_workload": head.name, "steps": a.profile_steps}))
+        names = ALL if a.workload == "all" else [a.workload]
+        for name in names:
+            log("profiling %s: %d steps" % (name, a.profile_steps))
+            wl = make(name, dev)
+            for i in range(a.profile_steps):
+                wl.step(i)
+            torch.cuda.synchronize()
+            del wl
+            torch.cuda.empty_cache()
+        if a.copy_bytes:
+            n = a.copy_bytes // 4
+            src = torch.ones(n, dtype=torch.float32, device=dev)
+            dst = torch.empty_like(src)
+            for _ in range(a.profile_steps):
+                dst.copy_(src)
+            torch.cuda.synchronize()
+        print(json.dumps({"profiled_workloads": names, "steps": a.profile_steps,
+                          "copy_bytes": a.copy_bytes}))
         return
 
+    if a.workload == "all":
+        a.workload = "decode_f16"
+    log("preparing %s" % a.workload)
+    head = make(a.workload, dev)
     err = head.check()
     log("%s max-abs error vs oracle %.3g; timing %d steps" % (head.name, err, a.steps))
     ms = time_steps(head, a.steps, a.warmup)
@@ -444,7 +466,7 @@ def main():
         out["cpu_baseline"] = cpu_baseline(head)
     if not a.only_headline:
         others = {}
-        for name in ("prefill_f32", "prefill_f16", "vision_f16", "decode_paged_q8"):
+        for name in ALL:
             if name == head.name:
                 continue
             log("preparing %s" % name)

@@ -100,6 +100,8 @@ DecodePlan plan_decode(int batch, int num_heads, int num_kv_heads, int head_dim,
         t = (int)(((want + min_t - 1) / min_t) * min_t);
         if (t < min_t) t = min_t;
     }
+    // the paged kernel stages the page indices of one split in LDS
+    if (paged && t > ta03::decode_max_split_tokens_paged()) t = ta03::decode_max_split_tokens_paged();
     // the merge holds at most decode_max_splits() partials per (sequence, head)
     const int cap = ta03::decode_max_splits();
     if ((eff_len + t - 1) / t > cap) t = (((eff_len + cap - 1) / cap) + 15) / 16 * 16;
@@ -295,9 +297,13 @@ int attn_decode_paged_q8(const float* q, const int8_t* k_pages, const int8_t* v_
     if (num_pages < 1 || max_pages_per_seq < 1)
         return fail(ATTN_ERR_INVALID_ARG, "attn_decode_paged_q8: num_pages and max_pages_per_seq must be >= 1");
     TRY(check_scalars(sliding_window, attn_softcap, scale));
-    if ((long)num_pages * page_size * num_kv_heads * head_dim > kMaxElems ||
-        (long)max_pages_per_seq * page_size > 0x7fffffffL)
+    if ((long)num_pages * page_size * num_kv_heads * head_dim > kMaxElems)
         return fail(ATTN_ERR_INVALID_ARG, "attn_decode_paged_q8: cache too large");
+    if ((long)max_pages_per_seq * page_size >
+        (long)ta03::decode_max_splits() * ta03::decode_max_split_tokens_paged())
+        return fail(ATTN_ERR_UNSUPPORTED,
+                    "attn_decode_paged_q8: requires max_pages_per_seq * page_size <= %d",
+                    ta03::decode_max_splits() * ta03::decode_max_split_tokens_paged());
     const int max_len = max_pages_per_seq * page_size;
     const int eff = (sliding_window > 0 && sliding_window < max_len) ? sliding_window : max_len;
     const DecodePlan plan = plan_decode(batch, num_heads, num_kv_heads, head_dim, eff, true);

@@ -38,6 +38,7 @@ namespace {
 
 constexpr int kDecodeWaves = 8;
 constexpr int kMaxSplits = 256;          // split partials merged per (sequence, head)
+constexpr int kMaxSplitTokens = 4096;    // paged: tokens per workgroup (page slice in LDS)
 constexpr float kRescaleSlack = 8.0f;    // log2 units: accumulators may grow to 2^8
 
 template <int D, int GC, bool PAGED>
@@ -76,15 +77,16 @@ struct RowCtx {
     const char* vbase;
     const float* kscales;
     const float* vscales;
-    const int32_t* ptab;
-    int num_pages, Hkv, kvh, kv_len;
+    const int* pages;      // paged: physical pages of this split, from logical page page0
+    int page0;
+    int Hkv, kvh, kv_len;
 };
 
 // Row index (token t of this KV head) in units of D elements.
 template <bool PAGED>
 __device__ __forceinline__ size_t row_index(const RowCtx& c, int t) {
     if constexpr (PAGED) {
-        const int pg = clamp_page(c.ptab[t >> 4], c.num_pages);
+        const int pg = c.pages[(t >> 4) - c.page0];
         return ((size_t)pg * 16 + (t & 15)) * c.Hkv + c.kvh;
     } else {
         return (size_t)c.kvh * c.kv_len + t;
@@ -234,6 +236,7 @@ __global__ void __launch_bounds__(64 * kDecodeWaves) decode_split_kernel(DecodeP
     __shared__ float lds_l[NW][GC];
     __shared__ float lds_w[GC][kMaxSplits];
     __shared__ float lds_L[GC];
+    __shared__ int lds_pages[PAGED ? kMaxSplitTokens / 16 + 1 : 1];
     __shared__ int lds_last;
     static_assert(NW * D >= kMaxSplits, "l of the split partials is parked in lds_o");
 
@@ -297,11 +300,18 @@ __global__ void __launch_bounds__(64 * kDecodeWaves) decode_split_kernel(DecodeP
     c.vbase = reinterpret_cast<const char*>(a.v);
     c.kscales = a.k_scales;
     c.vscales = a.v_scales;
-    c.ptab = PAGED ? a.page_table + (size_t)b * a.max_pages : nullptr;
-    c.num_pages = a.num_pages;
+    c.pages = lds_pages;
+    c.page0 = t_begin >> 4;
     c.Hkv = a.Hkv;
     c.kvh = kvh;
     c.kv_len = a.kv_len;
+    if constexpr (PAGED) {
+        // the physical pages of this split, fetched once (clamped into range)
+        const int32_t* ptab = a.page_table + (size_t)b * a.max_pages;
+        const int np = ((t_end - 1) >> 4) - c.page0 + 1;
+        for (int i = threadIdx.x; i < np; i += NT) lds_pages[i] = clamp_page(ptab[c.page0 + i], a.num_pages);
+        __syncthreads();
+    }
 
     // ---- stream this wave's blocks, two register buffers in flight ---------------------
     constexpr int STRIDE = NW * S::TB;
@@ -387,6 +397,20 @@ __global__ void __launch_bounds__(64 * kDecodeWaves) decode_split_kernel(DecodeP
     __syncthreads();
     if (!lds_last) return;
 
+    // (0) start fetching the first partial outputs of this thread's (head, d) pairs
+    constexpr int PF = 16;
+    constexpr int PER = (GC * D + NT - 1) / NT;     // (head, d) pairs per thread
+    float pre[PER][PF];
+#pragma unroll
+    for (int r = 0; r < PER; ++r) {
+        const int i = threadIdx.x + r * NT;
+        if (i < GC * D) {
+            const size_t row = (part_base + i / D) * a.n_split_max;
+#pragma unroll
+            for (int s = 0; s < PF; ++s)
+                pre[r][s] = s < n_live ? load_agent(a.part_o + (row + s) * D + (i % D)) : 0.f;
+        }
+    }
     // (1) m and l of every split, one (head, split) pair per thread
     float* lds_ls = &lds_o[0][0][0];      // l of (g, s) at g * n_live + s
     for (int i = threadIdx.x; i < GC * n_live; i += NT) {
@@ -412,12 +436,17 @@ __global__ void __launch_bounds__(64 * kDecodeWaves) decode_split_kernel(DecodeP
         if (lane == 0) lds_L[g] = Ls;
     }
     __syncthreads();
-    // (3) o = sum_s w_s o_s / L, one (head, d) per thread, independent loads
-    for (int i = threadIdx.x; i < GC * D; i += NT) {
+    // (3) o = sum_s w_s o_s / L, one (head, d) per thread
+#pragma unroll
+    for (int r = 0; r < PER; ++r) {
+        const int i = threadIdx.x + r * NT;
+        if (i >= GC * D) break;
         const int g = i / D, d = i % D;
         const size_t row = (part_base + g) * a.n_split_max;
         float os = 0.f;
-        int s = 0;
+#pragma unroll
+        for (int s = 0; s < PF; ++s) os += (s < n_live ? lds_w[g][s] : 0.f) * pre[r][s];
+        int s = PF;
         for (; s + 8 <= n_live; s += 8) {
             float v[8];
 #pragma unroll
@@ -473,5 +502,7 @@ int decode_tokens_per_block(int head_dim, bool paged) {
 int decode_waves() { return kDecodeWaves; }
 
 int decode_max_splits() { return kMaxSplits; }
+
+int decode_max_split_tokens_paged() { return kMaxSplitTokens; }
 
 }  // namespace ta03

@@ -81,95 +81,84 @@ __device__ __forceinline__ float score_transform(const FwdParams& a, float s) {
 // f16 inputs, f32 accumulation: v_mfma_f32_16x16x32_f16
 // =============================================================================================
 //
-// LDS holds two stages of (K tile, V^T tile).  K rows are padded by 16 bytes; V^T rows are
-// not padded but each 4-key group is XOR-swizzled by (d mod 16), so both the transposing
-// writes and the 8-byte fragment reads of 16 consecutive d rows hit distinct banks.
-// The next tile's global loads are issued into registers before the current tile is
-// computed and written to the other LDS stage afterwards: one barrier per tile.
+// K and V tiles go from HBM/L2 straight into LDS with global_load_lds_dwordx4 (no staging
+// registers, no VALU), into a ring of NS stages so that the loads of the next NS-1 tiles
+// are in flight while a tile is computed.  Both tiles keep the natural [key][d] layout;
+// their 16-byte chunks are XOR-swizzled by key so that fragment reads hit distinct banks
+// (the DMA places lane l of a wave at base + 16 l, so rows cannot be padded).
+//   QK^T:  A = K fragment, one ds_read_b128 per lane (16 keys x 32 d),
+//   PV:    A = V^T fragment, two ds_read_b64_tr_b16 per lane: within a 16-lane group,
+//          lane j points at V[key_0 + j/4][d_0 + 4 (j%4)] and lane i receives
+//          V[key_0 + k][d_0 + i] for k = 0..3, which is the transposed operand.
 
-template <int D, int QB_, int NW_>
+template <int D, int QB_, int NW_, int NS_>
 struct F16Shape {
     static constexpr int NW = NW_;                // waves per workgroup
     static constexpr int QB = QB_;                // 16-row query blocks per wave
+    static constexpr int NS = NS_;                // LDS ring stages
     static constexpr int NT = 64 * NW;
     static constexpr int BM = NW * QB * 16;       // query rows per workgroup
     static constexpr int BN = 64;                 // keys per tile
-    static constexpr int KLD = D + 8;             // K row stride in LDS (halves)
-    static constexpr int VLD = BN;                // V^T row stride in LDS (halves)
-    static constexpr int KCH = BN * D / 8 / NT;   // 16-byte K chunks per thread per tile
-    static constexpr int VGRP = (BN / 4) * (D / 8);        // 4-key x 8-d groups per tile
-    static constexpr int VGT = (VGRP + NT - 1) / NT;       // per thread
+    static constexpr int TILE = BN * D * 2;       // bytes of one K (or V) tile
+    static constexpr int LI = TILE / 1024 / NW;   // 1 KB DMA loads per wave per tile, K or V
     static constexpr int DC = D / 32;             // 32-wide k chunks of the QK^T product
     static constexpr int NDB = D / 16;            // 16-row d blocks of O^T
     static constexpr int NKB = BN / 16;           // 16-key blocks of S^T
-    static_assert(KCH * NT == BN * D / 8, "K tile split");
+    static_assert(LI >= 1 && LI * 1024 * NW == TILE, "tile split");
 };
 
-// V^T element (d, key) lives at row d, column 4 * ((key / 4) ^ (d & 15)) + key % 4.
-__device__ __forceinline__ int vt_col(int d, int key4) { return 4 * (key4 ^ (d & 15)); }
+// Physical 16-byte chunk of logical chunk c in K row r / V row r.
+template <int D>
+__device__ __forceinline__ int kswz(int r, int c) { return c ^ (D >= 128 ? (r & 15) : ((r >> 1) & 7)); }
+template <int D>
+__device__ __forceinline__ int vswz(int r, int c) { return c ^ (((r & 7) * 2) & (D / 8 - 1)); }
 
-template <int D, int QB, int NW>
-__device__ __forceinline__ void f16_load_tile(const FwdParams& a, const _Float16* kg,
-                                              const _Float16* vg, int ks, int tid,
-                                              u32x4_t (&kst)[F16Shape<D, QB, NW>::KCH],
-                                              u32x4_t (&vst)[F16Shape<D, QB, NW>::VGT][4]) {
-    using S = F16Shape<D, QB, NW>;
+template <int N>
+__device__ __forceinline__ void wait_vmem_at_most() { asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory"); }
+
+// 16 bytes per lane from global memory straight into LDS at lds_base + 16 * lane.  Issued
+// as inline asm so that the compiler does not guard every later LDS read with a full
+// vector-memory wait (it cannot tell that the ring stage being filled is not the one being
+// read); completion is tracked explicitly with wait_vmem_at_most + a barrier.  m0 is
+// written here and is used by nothing else in these kernels.
+__device__ __forceinline__ void dma16(const void* gptr, const void* lds_base) {
+    const uint32_t off = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)lds_base;
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
+                 :
+                 : "s"(__builtin_amdgcn_readfirstlane(off)), "v"(gptr)
+                 : "memory", "m0");
+}
+
+// DMA one K tile and one V tile (keys ks .. ks+BN-1, clamped) into an LDS stage.
+template <int D, int QB, int NW, int NS>
+__device__ __forceinline__ void f16_dma_tile(const FwdParams& a, const _Float16* kg,
+                                             const _Float16* vg, int ks, int w, int lane,
+                                             char* k_dst, char* v_dst) {
+    using S = F16Shape<D, QB, NW, NS>;
 #pragma unroll
-    for (int i = 0; i < S::KCH; ++i) {
-        const int ci = tid + S::NT * i;
-        const int r = ci / (D / 8), c = ci % (D / 8);
+    for (int j = 0; j < S::LI; ++j) {
+        const int off = (j * NW + w) * 1024;              // byte offset of this instruction
+        const int byte = off + 16 * lane;
+        const int r = byte / (2 * D), p = (byte % (2 * D)) / 16;
         const int key = min(ks + r, a.kv_len - 1);
-        kst[i] = *reinterpret_cast<const u32x4_t*>(kg + (long)key * a.k_row + 8 * c);
-    }
-#pragma unroll
-    for (int i = 0; i < S::VGT; ++i) {
-        const int gi = tid + S::NT * i;
-        if (gi < S::VGRP) {
-            const int k4 = gi % (S::BN / 4), c = gi / (S::BN / 4);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int key = min(ks + 4 * k4 + e, a.kv_len - 1);
-                vst[i][e] = *reinterpret_cast<const u32x4_t*>(vg + (long)key * a.k_row + 8 * c);
-            }
-        }
+        dma16(kg + (long)key * a.k_row + 8 * kswz<D>(r, p), k_dst + off);
+        dma16(vg + (long)key * a.k_row + 8 * vswz<D>(r, p), v_dst + off);
     }
 }
 
-template <int D, int QB, int NW>
-__device__ __forceinline__ void f16_store_tile(_Float16* k_lds, _Float16* vt_lds, int tid,
-                                               const u32x4_t (&kst)[F16Shape<D, QB, NW>::KCH],
-                                               const u32x4_t (&vst)[F16Shape<D, QB, NW>::VGT][4]) {
-    using S = F16Shape<D, QB, NW>;
-#pragma unroll
-    for (int i = 0; i < S::KCH; ++i) {
-        const int ci = tid + S::NT * i;
-        const int r = ci / (D / 8), c = ci % (D / 8);
-        *reinterpret_cast<u32x4_t*>(&k_lds[r * S::KLD + 8 * c]) = kst[i];
-    }
-#pragma unroll
-    for (int i = 0; i < S::VGT; ++i) {
-        const int gi = tid + S::NT * i;
-        if (gi < S::VGRP) {
-            const int k4 = gi % (S::BN / 4), c = gi / (S::BN / 4);
-            const half8_t r0 = __builtin_bit_cast(half8_t, vst[i][0]);
-            const half8_t r1 = __builtin_bit_cast(half8_t, vst[i][1]);
-            const half8_t r2 = __builtin_bit_cast(half8_t, vst[i][2]);
-            const half8_t r3 = __builtin_bit_cast(half8_t, vst[i][3]);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int d = 8 * c + e;
-                *reinterpret_cast<half4_t*>(&vt_lds[d * S::VLD + vt_col(d, k4)]) =
-                    half4_t{r0[e], r1[e], r2[e], r3[e]};
-            }
-        }
-    }
+typedef short short4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ half4_t lds_read_tr16(const char* p) {
+    const short4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) short4_t*)(p));
+    return __builtin_bit_cast(half4_t, v);
 }
 
-template <int D, int QB, int NW>
+template <int D, int QB, int NW, int NS>
 __global__ void __launch_bounds__(64 * NW) fwd_f16_kernel(FwdParams a) {
-    using S = F16Shape<D, QB, NW>;
-    __shared__ __attribute__((aligned(16))) _Float16 k_lds[2][S::BN * S::KLD];
-    __shared__ __attribute__((aligned(16))) _Float16 vt_lds[2][D * S::VLD];
+    using S = F16Shape<D, QB, NW, NS>;
+    __shared__ __attribute__((aligned(1024))) char k_lds[NS][S::TILE];
+    __shared__ __attribute__((aligned(1024))) char v_lds[NS][S::TILE];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -187,9 +176,11 @@ __global__ void __launch_bounds__(64 * NW) fwd_f16_kernel(FwdParams a) {
     const _Float16* kg = reinterpret_cast<const _Float16*>(a.k) + (long)kvh * a.k_head;
     const _Float16* vg = reinterpret_cast<const _Float16*>(a.v) + (long)kvh * a.k_head;
 
-    u32x4_t kst[S::KCH];
-    u32x4_t vst[S::VGT][4];
-    if (tr.kt0 < tr.kt1) f16_load_tile<D, QB, NW>(a, kg, vg, tr.kt0 * S::BN, tid, kst, vst);
+    // prologue: tiles kt0 .. kt0 + NS - 2 in flight
+#pragma unroll
+    for (int st0 = 0; st0 < NS - 1; ++st0)
+        if (tr.kt0 + st0 < tr.kt1)
+            f16_dma_tile<D, QB, NW, NS>(a, kg, vg, (tr.kt0 + st0) * S::BN, w, lane, k_lds[st0], v_lds[st0]);
 
     // ---- Q fragments (B operand of S^T = K Q^T) --------------------------------------------
     half8_t qf[S::QB][S::DC];
@@ -203,35 +194,55 @@ __global__ void __launch_bounds__(64 * NW) fwd_f16_kernel(FwdParams a) {
         for (int c = 0; c < S::DC; ++c)
             qf[qb][c] = *reinterpret_cast<const half8_t*>(qg + (long)rr * a.q_row + 32 * c + 8 * lg);
     }
+    // Settle the Q loads here: the loop below must not wait on the vector-memory counter,
+    // which also counts the in-flight tile DMAs.
+#pragma unroll
+    for (int qb = 0; qb < S::QB; ++qb)
+#pragma unroll
+        for (int c = 0; c < S::DC; ++c) asm volatile("" ::"v"(qf[qb][c]));
 
     float4_t acc_o[S::NDB][S::QB];
 #pragma unroll
     for (int db = 0; db < S::NDB; ++db)
 #pragma unroll
         for (int qb = 0; qb < S::QB; ++qb) acc_o[db][qb] = float4_t{0.f, 0.f, 0.f, 0.f};
-    float m_run[S::QB], l_part[S::QB];
+    float m_run[S::QB];
+    float4_t acc_l[S::QB];               // row sums of P (all four entries equal)
 #pragma unroll
     for (int qb = 0; qb < S::QB; ++qb) {
         m_run[qb] = kMinit;
-        l_part[qb] = 0.f;
+        acc_l[qb] = float4_t{0.f, 0.f, 0.f, 0.f};
     }
+    const half8_t ones = half8_t{1, 1, 1, 1, 1, 1, 1, 1};
 
     const bool capped = a.softcap > 0.f;
+    const float sc2 = capped ? 1.f : a.scale_log2;     // raw score -> log2 units
     // softcap in log2 units: t = C1 - C2 / (2^(s * K1) + 1), C1 = c log2 e, C2 = 2 c log2 e,
     // K1 = 2 scale log2 e / c  (c tanh(scale s / c) = c - 2c / (exp(2 scale s / c) + 1))
     const float K1 = 2.f * a.scale * kLog2e * a.inv_softcap;
     const float C1 = a.softcap * kLog2e;
     const float C2 = 2.f * C1;
 
-    if (tr.kt0 < tr.kt1) f16_store_tile<D, QB, NW>(k_lds[0], vt_lds[0], tid, kst, vst);
-    __syncthreads();
+    // per-lane parts of the V^T fragment addresses: source lane j = ln of its 16-lane group
+    const int tr_key = ln >> 2;                 // + 4 lg + 16 h + 32 c
+    const int tr_d = 4 * (ln & 3);              // + 16 db
 
     int stage = 0;
     for (int kt = tr.kt0; kt < tr.kt1; ++kt) {
-        const bool more = kt + 1 < tr.kt1;
-        if (more) f16_load_tile<D, QB, NW>(a, kg, vg, (kt + 1) * S::BN, tid, kst, vst);
-        const _Float16* kl = k_lds[stage];
-        const _Float16* vl = vt_lds[stage];
+        // this tile's DMA (issued NS - 1 tiles ago) has landed for every wave, and every
+        // wave is done with the stage that the next DMA overwrites
+        if (kt + NS - 2 < tr.kt1) wait_vmem_at_most<2 * S::LI * (NS - 2)>();
+        else wait_vmem_at_most<0>();
+        __syncthreads();
+        {
+            const int nxt = kt + NS - 1;
+            if (nxt < tr.kt1) {
+                const int sn = (stage + NS - 1) % NS;
+                f16_dma_tile<D, QB, NW, NS>(a, kg, vg, nxt * S::BN, w, lane, k_lds[sn], v_lds[sn]);
+            }
+        }
+        const char* kl = k_lds[stage];
+        const char* vl = v_lds[stage];
         const int ks = kt * S::BN;
         const bool masked = tile_needs_mask(a, tr, ks, S::BN);
 
@@ -245,8 +256,8 @@ __global__ void __launch_bounds__(64 * NW) fwd_f16_kernel(FwdParams a) {
         for (int c = 0; c < S::DC; ++c) {
 #pragma unroll
             for (int kb = 0; kb < S::NKB; ++kb) {
-                const half8_t kf =
-                    *reinterpret_cast<const half8_t*>(&kl[(16 * kb + ln) * S::KLD + 32 * c + 8 * lg]);
+                const int r = 16 * kb + ln;
+                const half8_t kf = *reinterpret_cast<const half8_t*>(kl + r * 2 * D + 16 * kswz<D>(r, 4 * c + lg));
 #pragma unroll
                 for (int qb = 0; qb < S::QB; ++qb)
                     st[kb][qb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf, qf[qb][c], st[kb][qb], 0, 0, 0);
@@ -254,6 +265,9 @@ __global__ void __launch_bounds__(64 * NW) fwd_f16_kernel(FwdParams a) {
         }
 
         // ---- online softmax in the S^T layout: lane = query (ln), keys 16kb + 4lg + i ----
+        // Uncapped scores stay raw (scale > 0 preserves the max); the scale is folded into
+        // the exponent: p = 2^(s * scale * log2 e - m).  Capped scores are turned into log2
+        // units first.  Masked keys get -inf added.
         half8_t pf[S::QB][S::BN / 32];
 #pragma unroll
         for (int qb = 0; qb < S::QB; ++qb) {
@@ -265,9 +279,6 @@ __global__ void __launch_bounds__(64 * NW) fwd_f16_kernel(FwdParams a) {
                         const float e2 = fast_exp2(st[kb][qb][i] * K1);
                         st[kb][qb][i] = __builtin_fmaf(-C2, fast_rcp(e2 + 1.f), C1);
                     }
-            } else {
-#pragma unroll
-                for (int kb = 0; kb < S::NKB; ++kb) st[kb][qb] *= a.scale_log2;
             }
             if (masked) {
 #pragma unroll
@@ -283,25 +294,20 @@ __global__ void __launch_bounds__(64 * NW) fwd_f16_kernel(FwdParams a) {
                 for (int i = (kb == 0 ? 1 : 0); i < 4; ++i) mx = fmaxf(mx, st[kb][qb][i]);
             mx = fmaxf(mx, shfl_xor_f(mx, 16));
             mx = fmaxf(mx, shfl_xor_f(mx, 32));
-            if (__builtin_amdgcn_ballot_w64(mx > m_run[qb] + kSlack) != 0) {
-                const float mnew = fmaxf(m_run[qb], mx);
+            const float mxl = mx * sc2;        // in log2 units
+            if (__builtin_amdgcn_ballot_w64(mxl > m_run[qb] + kSlack) != 0) {
+                const float mnew = fmaxf(m_run[qb], mxl);
                 const float alpha = fast_exp2(m_run[qb] - mnew);
                 m_run[qb] = mnew;
-                l_part[qb] *= alpha;
+                acc_l[qb] *= alpha;
 #pragma unroll
                 for (int db = 0; db < S::NDB; ++db) acc_o[db][qb] *= alpha;
             }
             const float mq = m_run[qb];
-            float ls = 0.f;
 #pragma unroll
             for (int kb = 0; kb < S::NKB; ++kb)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const float p = fast_exp2(st[kb][qb][i] - mq);
-                    st[kb][qb][i] = p;
-                    ls += p;
-                }
-            l_part[qb] += ls;
+                for (int i = 0; i < 4; ++i) st[kb][qb][i] = fast_exp2(__builtin_fmaf(st[kb][qb][i], sc2, -mq));
 #pragma unroll
             for (int c = 0; c < S::BN / 32; ++c) {
                 const half2_t h0 = __builtin_convertvector(float2_t{st[2 * c][qb][0], st[2 * c][qb][1]}, half2_t);
@@ -309,37 +315,35 @@ __global__ void __launch_bounds__(64 * NW) fwd_f16_kernel(FwdParams a) {
                 const half2_t h2 = __builtin_convertvector(float2_t{st[2 * c + 1][qb][0], st[2 * c + 1][qb][1]}, half2_t);
                 const half2_t h3 = __builtin_convertvector(float2_t{st[2 * c + 1][qb][2], st[2 * c + 1][qb][3]}, half2_t);
                 pf[qb][c] = half8_t{h0[0], h0[1], h1[0], h1[1], h2[0], h2[1], h3[0], h3[1]};
+                // row sums of P on the matrix core: a block of ones times P^T
+                acc_l[qb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, pf[qb][c], acc_l[qb], 0, 0, 0);
             }
         }
 
         // ---- O^T += V^T P^T ---------------------------------------------------------------
 #pragma unroll
         for (int db = 0; db < S::NDB; ++db) {
-            const int d = 16 * db + ln;
-            const _Float16* vrow = &vl[d * S::VLD];
+            const int d = 16 * db + tr_d;
 #pragma unroll
             for (int c = 0; c < S::BN / 32; ++c) {
-                const half4_t lo = *reinterpret_cast<const half4_t*>(vrow + vt_col(d, 8 * c + lg));
-                const half4_t hi = *reinterpret_cast<const half4_t*>(vrow + vt_col(d, 8 * c + 4 + lg));
+                const int k0 = 32 * c + 4 * lg + tr_key;          // keys for h = 0; h = 1 adds 16
+                const int k1 = k0 + 16;
+                const half4_t lo = lds_read_tr16(vl + k0 * 2 * D + 16 * vswz<D>(k0, d >> 3) + 2 * (d & 7));
+                const half4_t hi = lds_read_tr16(vl + k1 * 2 * D + 16 * vswz<D>(k1, d >> 3) + 2 * (d & 7));
                 const half8_t vf = half8_t{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 #pragma unroll
                 for (int qb = 0; qb < S::QB; ++qb)
                     acc_o[db][qb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf, pf[qb][c], acc_o[db][qb], 0, 0, 0);
             }
         }
-
-        if (more) f16_store_tile<D, QB, NW>(k_lds[stage ^ 1], vt_lds[stage ^ 1], tid, kst, vst);
-        __syncthreads();
-        stage ^= 1;
+        stage = (stage + 1 == NS) ? 0 : stage + 1;
     }
 
     // ---- epilogue: O = (O^T)^T / l ---------------------------------------------------------
     _Float16* og = reinterpret_cast<_Float16*>(a.o) + (long)head * a.o_head;
 #pragma unroll
     for (int qb = 0; qb < S::QB; ++qb) {
-        float l = l_part[qb];
-        l += shfl_xor_f(l, 16);
-        l += shfl_xor_f(l, 32);
+        const float l = acc_l[qb][0];
         const float inv = l != 0.f ? 1.0f / l : 0.f;
         const int row = q0 + (w * S::QB + qb) * 16 + ln;
         if (row < a.seq_len) {
@@ -505,15 +509,18 @@ __global__ void __launch_bounds__(256) fwd_f32_kernel(FwdParams a) {
     }
 }
 
-// Tile configuration per head_dim: (16-row blocks per wave, waves per workgroup).
-template <int D> struct F16Cfg { static constexpr int QB = 2, NW = 4; };
+// Tile configuration per head_dim: 16-row blocks per wave, waves per workgroup, LDS stages.
+template <int D> struct F16Cfg;
+template <> struct F16Cfg<64> { static constexpr int QB = 1, NW = 4, NS = 3; };
+template <> struct F16Cfg<128> { static constexpr int QB = 1, NW = 4, NS = 2; };
+template <> struct F16Cfg<256> { static constexpr int QB = 1, NW = 8, NS = 2; };
 
 template <int D>
 hipError_t launch_d(const FwdParams& p, int dtype, hipStream_t st) {
     const dim3 grid(p.n_qblocks * p.H);
     if (dtype == 1) {
-        constexpr int QB = F16Cfg<D>::QB, NW = F16Cfg<D>::NW;
-        hipLaunchKernelGGL((fwd_f16_kernel<D, QB, NW>), grid, dim3(64 * NW), 0, st, p);
+        constexpr int QB = F16Cfg<D>::QB, NW = F16Cfg<D>::NW, NS = F16Cfg<D>::NS;
+        hipLaunchKernelGGL((fwd_f16_kernel<D, QB, NW, NS>), grid, dim3(64 * NW), 0, st, p);
     } else {
         hipLaunchKernelGGL(fwd_f32_kernel<D>, grid, dim3(256), 0, st, p);
     }

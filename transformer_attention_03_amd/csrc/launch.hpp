@@ -54,6 +54,7 @@ hipError_t launch_decode(const DecodeParams& p, int head_dim, int gc, bool paged
 int decode_tokens_per_block(int head_dim, bool paged);
 int decode_waves();
 int decode_max_splits();
+int decode_max_split_tokens_paged();
 
 // dtype: 0 f32, 1 f16
 hipError_t launch_fwd(const FwdParams& p, int head_dim, int dtype, hipStream_t st);
