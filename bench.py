@@ -47,11 +47,13 @@ def parse():
                              "decode_paged_q8", "all"])
     ap.add_argument("--only-headline", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="launch every step from the host instead of replaying a HIP graph")
     ap.add_argument("--profile-steps", type=int, default=0,
                     help="only run this many steps of the selected workload(s), for profilers")
     ap.add_argument("--copy-bytes", type=int, default=0,
-                    help="with --profile-steps: also run a plain device copy of this many bytes "
-                         "per step (calibrates the HBM byte counters)")
+                    help="with --profile-steps: also run a plain elementwise copy of this many "
+                         "bytes per step (calibrates the HBM byte counters)")
     return ap.parse_args()
 
 
@@ -225,14 +227,14 @@ class Forward(Workload):
             self.S, self.H, self.Hkv, self.D, self.causal, self.W, self.cap = 2048, 16, 8, 256, True, 512, 50.0
             q, k, v = synth.prefill_inputs(synth.seed_of(3), 2048, 2048, 16, 8, 256, "f16")
             self.kind = "mfma"
-            self.kernel = "fwd_f16_kernel<256>"
+            self.kernel = "fwd_f16_kernel<256, 1, 8, 2>"
             self.desc = {"workload": "causal GQA prefill, f16, 2048 tokens, 16/8 heads, head_dim "
                                      "256, sliding window 512, softcap 50, scale 1/16"}
         else:
             self.S, self.H, self.Hkv, self.D, self.causal, self.W, self.cap = 2304, 16, 16, 64, False, 0, 0.0
             q, k, v = synth.vision_inputs(synth.seed_of(4), 2304, 16, 64)
             self.kind = "mfma"
-            self.kernel = "fwd_f16_kernel<64>"
+            self.kernel = "fwd_f16_kernel<64, 1, 4, 3>"
             self.desc = {"workload": "bidirectional vision attention, f16 [16, 2304, 64] "
                                      "head-major, scale 1/8"}
         self.vision = name == "vision_f16"
@@ -317,20 +319,39 @@ def make(name, dev):
 # measurement
 # ---------------------------------------------------------------------------------------------
 
-def time_steps(wl, steps, warmup):
+def time_steps(wl, steps, warmup, graph=True):
+    """ms per step: K steps between HIP events on the launch stream.  With graph=True the K
+    launches (each on its own input copy) are captured once into a HIP graph and replayed,
+    so host-side launch cost does not pace the GPU."""
     import torch
     for i in range(warmup):
         wl.step(i)
     torch.cuda.synchronize()
-    st = torch.cuda.current_stream()
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    e0.record(st)
-    for i in range(steps):
-        wl.step(warmup + i)
-    e1.record(st)
-    torch.cuda.synchronize()
+    if graph:
+        g = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.graph(g, stream=side):
+            for i in range(steps):
+                wl.step(warmup + i)
+        torch.cuda.synchronize()
+        g.replay()                      # untimed replay
+        torch.cuda.synchronize()
+        st = torch.cuda.current_stream()
+        e0.record(st)
+        g.replay()
+        e1.record(st)
+        torch.cuda.synchronize()
+        del g
+    else:
+        st = torch.cuda.current_stream()
+        e0.record(st)
+        for i in range(steps):
+            wl.step(warmup + i)
+        e1.record(st)
+        torch.cuda.synchronize()
     return e0.elapsed_time(e1) / steps      # ms per step
 
 
@@ -432,11 +453,13 @@ def main():
             del wl
             torch.cuda.empty_cache()
         if a.copy_bytes:
+            # a plain elementwise copy kernel (reads n*4 bytes, writes n*4 bytes) whose
+            # source is far larger than L2 + MALL: calibrates FETCH_SIZE / WRITE_SIZE
             n = a.copy_bytes // 4
             src = torch.ones(n, dtype=torch.float32, device=dev)
             dst = torch.empty_like(src)
             for _ in range(a.profile_steps):
-                dst.copy_(src)
+                torch.neg(src, out=dst)
             torch.cuda.synchronize()
         print(json.dumps({"profiled_workloads": names, "steps": a.profile_steps,
                           "copy_bytes": a.copy_bytes}))
@@ -448,7 +471,7 @@ def main():
     head = make(a.workload, dev)
     err = head.check()
     log("%s max-abs error vs oracle %.3g; timing %d steps" % (head.name, err, a.steps))
-    ms = time_steps(head, a.steps, a.warmup)
+    ms = time_steps(head, a.steps, a.warmup, graph=not a.no_graph)
     s = summarize(head, ms)
     src = os.path.join(ROOT, "transformer_attention_03_amd", "csrc",
                        "decode.hip" if head.kind == "hbm" else "fwd.hip")
@@ -460,7 +483,9 @@ def main():
            "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
            "dtype": "f32" if head.kind != "mfma" else "f16",
            "data": "synthetic (seeded SplitMix64 + Box-Muller, N(0,1))",
-           "config": dict(head.desc), "roofline": roof, "max_abs_err_vs_oracle": err}
+           "config": dict(head.desc), "roofline": roof, "max_abs_err_vs_oracle": err,
+           "timing": ("HIP events around one replay of a HIP graph holding the %d launches"
+                      % a.steps) if not a.no_graph else "HIP events around %d host launches" % a.steps}
     if not a.no_cpu_baseline:
         log("cpu baseline (oracle)")
         out["cpu_baseline"] = cpu_baseline(head)
@@ -473,12 +498,17 @@ def main():
             wl = make(name, dev)
             e = wl.check()
             log("%s max-abs error vs oracle %.3g" % (name, e))
-            ms_w = time_steps(wl, max(20, a.steps // 4), a.warmup)
+            ms_w = time_steps(wl, max(20, a.steps // 4), a.warmup, graph=not a.no_graph)
             sw = summarize(wl, ms_w)
             others[name] = {"config": wl.desc, "us_per_call": round(sw["us_per_call"], 3),
                             "value": round(sw["value"], 3), "unit": sw["unit"],
-                            "roofline": {"bound": sw["bound"], "peak": sw["peak"],
-                                         "frac": round(sw["frac"], 4), "kernel": wl.kernel},
+                            "roofline": {"bound": sw["bound"], "achieved": round(sw["achieved"], 3),
+                                         "peak": sw["peak"], "unit": sw["peak_unit"],
+                                         "frac": round(sw["frac"], 4), "kernel": wl.kernel,
+                                         "traffic": traffic_for(os.path.join(
+                                             ROOT, "transformer_attention_03_amd", "csrc",
+                                             "decode.hip" if wl.kind == "hbm" else "fwd.hip"),
+                                             wl.kernel)},
                             "max_abs_err_vs_oracle": e}
             del wl
             torch.cuda.empty_cache()

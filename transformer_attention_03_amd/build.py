@@ -36,6 +36,8 @@ def hipcc() -> str:
 def compile_flags(extra=()):
     return ["-x", "hip", "--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC",
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+            # MFMA results in VGPRs: the softmax reads the score tiles directly
+            "-mllvm", "-amdgpu-mfma-vgpr-form",
             "-I" + INCLUDE, "-I" + CSRC, "-Wall", "-Wno-unused-function",
             "-Wno-unused-variable", "-Wno-unused-but-set-variable", *extra]
 

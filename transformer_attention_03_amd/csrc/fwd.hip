@@ -58,7 +58,8 @@ __device__ __forceinline__ bool tile_needs_mask(const FwdParams& a, const TileRa
 }
 
 __device__ __forceinline__ bool visible(const FwdParams& a, int key, int pos) {
-    return key < a.kv_len && (!a.causal || key <= pos) && (a.window <= 0 || pos - key < a.window);
+    // bitwise, not short-circuit: evaluated for every element of an edge tile
+    return (key < a.kv_len) & ((a.causal == 0) | (key <= pos)) & ((a.window <= 0) | (pos - key < a.window));
 }
 
 // Work item for this workgroup: XCD-aware (consecutive work ids land on one XCD, so the
@@ -129,20 +130,56 @@ __device__ __forceinline__ void dma16(const void* gptr, const void* lds_base) {
                  : "memory", "m0");
 }
 
-// DMA one K tile and one V tile (keys ks .. ks+BN-1, clamped) into an LDS stage.
+// Per-lane byte offsets of the DMA loads of one tile: load j of this wave covers LDS bytes
+// [(j * NW + w) * 1024, +1024); lane l's 16 bytes hold chunk p of row r of the tile.
 template <int D, int QB, int NW, int NS>
-__device__ __forceinline__ void f16_dma_tile(const FwdParams& a, const _Float16* kg,
-                                             const _Float16* vg, int ks, int w, int lane,
-                                             char* k_dst, char* v_dst) {
+struct DmaLane {
+    using S = F16Shape<D, QB, NW, NS>;
+    int r[S::LI];            // tile row (key offset) of load j
+    uint32_t kg[S::LI];      // byte offset of the K chunk from the tile's first key row
+    uint32_t vg[S::LI];      // same for V
+};
+
+template <int D, int QB, int NW, int NS>
+__device__ __forceinline__ void dma_lane_init(DmaLane<D, QB, NW, NS>& L, const FwdParams& a, int w,
+                                              int lane) {
     using S = F16Shape<D, QB, NW, NS>;
 #pragma unroll
     for (int j = 0; j < S::LI; ++j) {
-        const int off = (j * NW + w) * 1024;              // byte offset of this instruction
-        const int byte = off + 16 * lane;
+        const int byte = (j * NW + w) * 1024 + 16 * lane;
         const int r = byte / (2 * D), p = (byte % (2 * D)) / 16;
-        const int key = min(ks + r, a.kv_len - 1);
-        dma16(kg + (long)key * a.k_row + 8 * kswz<D>(r, p), k_dst + off);
-        dma16(vg + (long)key * a.k_row + 8 * vswz<D>(r, p), v_dst + off);
+        L.r[j] = r;
+        L.kg[j] = (uint32_t)(r * a.k_row * 2 + 16 * kswz<D>(r, p));
+        L.vg[j] = (uint32_t)(r * a.k_row * 2 + 16 * vswz<D>(r, p));
+    }
+}
+
+// DMA one K tile and one V tile (keys ks .. ks+BN-1, clamped to kv_len) into an LDS stage.
+template <int D, int QB, int NW, int NS>
+__device__ __forceinline__ void f16_dma_tile(const FwdParams& a, const char* kg, const char* vg,
+                                             const DmaLane<D, QB, NW, NS>& L, int ks, int w,
+                                             int lane, char* k_dst, char* v_dst) {
+    using S = F16Shape<D, QB, NW, NS>;
+    const long row_bytes = a.k_row * 2;
+    if (ks + S::BN <= a.kv_len) {
+        const char* kt = kg + ks * row_bytes;
+        const char* vt = vg + ks * row_bytes;
+#pragma unroll
+        for (int j = 0; j < S::LI; ++j) {
+            const int off = (j * NW + w) * 1024;
+            dma16(kt + L.kg[j], k_dst + off);
+            dma16(vt + L.vg[j], v_dst + off);
+        }
+    } else {
+        // ragged last tile: rows past kv_len repeat the last key (masked out later)
+#pragma unroll
+        for (int j = 0; j < S::LI; ++j) {
+            const int off = (j * NW + w) * 1024;
+            const int key = min(ks + L.r[j], a.kv_len - 1);
+            const long shift = (long)(key - ks - L.r[j]) * row_bytes;
+            dma16(kg + ks * row_bytes + shift + L.kg[j], k_dst + off);
+            dma16(vg + ks * row_bytes + shift + L.vg[j], v_dst + off);
+        }
     }
 }
 
@@ -162,7 +199,7 @@ __global__ void __launch_bounds__(64 * NW) fwd_f16_kernel(FwdParams a) {
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int w = tid >> 6;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int ln = lane & 15;          // query column of the S^T / O^T blocks; A-tile row
     const int lg = lane >> 4;          // lane group 0..3
 
@@ -173,22 +210,32 @@ __global__ void __launch_bounds__(64 * NW) fwd_f16_kernel(FwdParams a) {
     const TileRange tr = tile_range(a, q0, S::BM, S::BN);
 
     const _Float16* qg = reinterpret_cast<const _Float16*>(a.q) + (long)head * a.q_head;
-    const _Float16* kg = reinterpret_cast<const _Float16*>(a.k) + (long)kvh * a.k_head;
-    const _Float16* vg = reinterpret_cast<const _Float16*>(a.v) + (long)kvh * a.k_head;
+    const char* kg = reinterpret_cast<const char*>(reinterpret_cast<const _Float16*>(a.k) + (long)kvh * a.k_head);
+    const char* vg = reinterpret_cast<const char*>(reinterpret_cast<const _Float16*>(a.v) + (long)kvh * a.k_head);
+
+    DmaLane<D, QB, NW, NS> dl;
+    dma_lane_init(dl, a, w, lane);
 
     // prologue: tiles kt0 .. kt0 + NS - 2 in flight
 #pragma unroll
     for (int st0 = 0; st0 < NS - 1; ++st0)
         if (tr.kt0 + st0 < tr.kt1)
-            f16_dma_tile<D, QB, NW, NS>(a, kg, vg, (tr.kt0 + st0) * S::BN, w, lane, k_lds[st0], v_lds[st0]);
+            f16_dma_tile<D, QB, NW, NS>(a, kg, vg, dl, (tr.kt0 + st0) * S::BN, w, lane, k_lds[st0], v_lds[st0]);
 
     // ---- Q fragments (B operand of S^T = K Q^T) --------------------------------------------
     half8_t qf[S::QB][S::DC];
     int qpos[S::QB];
+    int vlo[S::QB];
+    unsigned vspan[S::QB];
 #pragma unroll
     for (int qb = 0; qb < S::QB; ++qb) {
         const int row = q0 + (w * S::QB + qb) * 16 + ln;
         qpos[qb] = a.kv_len - a.seq_len + row;
+        const int hi = a.causal ? min(qpos[qb], a.kv_len - 1) : a.kv_len - 1;
+        const int lo = a.window > 0 ? max(0, qpos[qb] - a.window + 1) : 0;
+        // an empty interval (padding rows past seq_len only) keeps every key masked
+        vlo[qb] = hi >= lo ? lo : 0x40000000;
+        vspan[qb] = hi >= lo ? (unsigned)(hi - lo) : 0u;
         const int rr = min(row, a.seq_len - 1);
 #pragma unroll
         for (int c = 0; c < S::DC; ++c)
@@ -223,9 +270,24 @@ __global__ void __launch_bounds__(64 * NW) fwd_f16_kernel(FwdParams a) {
     const float C1 = a.softcap * kLog2e;
     const float C2 = 2.f * C1;
 
-    // per-lane parts of the V^T fragment addresses: source lane j = ln of its 16-lane group
-    const int tr_key = ln >> 2;                 // + 4 lg + 16 h + 32 c
-    const int tr_d = 4 * (ln & 3);              // + 16 db
+    // Tile-invariant parts of the fragment addresses (the swizzles depend on the row only
+    // through bits that the per-block steps 16 kb, 32 c + 16 h do not change).
+    //   K:   row 16 kb + ln, logical chunk 4 c + lg
+    //   V^T: source lane j = ln of its 16-lane group reads key 32 c + 16 h + 4 lg + ln / 4,
+    //        d = 16 db + 4 (ln % 4)
+    int koff[S::DC];
+#pragma unroll
+    for (int c = 0; c < S::DC; ++c) koff[c] = ln * 2 * D + 16 * kswz<D>(ln, 4 * c + lg);
+    int voff[S::NDB];
+    {
+        const int k0 = 4 * lg + (ln >> 2);
+        const int d0 = 4 * (ln & 3);
+#pragma unroll
+        for (int db = 0; db < S::NDB; ++db) {
+            const int d = 16 * db + d0;
+            voff[db] = k0 * 2 * D + 16 * vswz<D>(k0, d >> 3) + 2 * (d & 7);
+        }
+    }
 
     int stage = 0;
     for (int kt = tr.kt0; kt < tr.kt1; ++kt) {
@@ -238,7 +300,7 @@ __global__ void __launch_bounds__(64 * NW) fwd_f16_kernel(FwdParams a) {
             const int nxt = kt + NS - 1;
             if (nxt < tr.kt1) {
                 const int sn = (stage + NS - 1) % NS;
-                f16_dma_tile<D, QB, NW, NS>(a, kg, vg, nxt * S::BN, w, lane, k_lds[sn], v_lds[sn]);
+                f16_dma_tile<D, QB, NW, NS>(a, kg, vg, dl, nxt * S::BN, w, lane, k_lds[sn], v_lds[sn]);
             }
         }
         const char* kl = k_lds[stage];
@@ -252,16 +314,23 @@ __global__ void __launch_bounds__(64 * NW) fwd_f16_kernel(FwdParams a) {
         for (int kb = 0; kb < S::NKB; ++kb)
 #pragma unroll
             for (int qb = 0; qb < S::QB; ++qb) st[kb][qb] = float4_t{0.f, 0.f, 0.f, 0.f};
+        // K fragments are fetched a 32-wide d chunk ahead of their products
+        half8_t kf[2][S::NKB];
+#pragma unroll
+        for (int kb = 0; kb < S::NKB; ++kb)
+            kf[0][kb] = *reinterpret_cast<const half8_t*>(kl + koff[0] + 16 * kb * 2 * D);
 #pragma unroll
         for (int c = 0; c < S::DC; ++c) {
+            if (c + 1 < S::DC) {
 #pragma unroll
-            for (int kb = 0; kb < S::NKB; ++kb) {
-                const int r = 16 * kb + ln;
-                const half8_t kf = *reinterpret_cast<const half8_t*>(kl + r * 2 * D + 16 * kswz<D>(r, 4 * c + lg));
+                for (int kb = 0; kb < S::NKB; ++kb)
+                    kf[(c + 1) & 1][kb] = *reinterpret_cast<const half8_t*>(kl + koff[c + 1] + 16 * kb * 2 * D);
+            }
+#pragma unroll
+            for (int kb = 0; kb < S::NKB; ++kb)
 #pragma unroll
                 for (int qb = 0; qb < S::QB; ++qb)
-                    st[kb][qb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf, qf[qb][c], st[kb][qb], 0, 0, 0);
-            }
+                    st[kb][qb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf[c & 1][kb], qf[qb][c], st[kb][qb], 0, 0, 0);
         }
 
         // ---- online softmax in the S^T layout: lane = query (ln), keys 16kb + 4lg + i ----
@@ -281,11 +350,13 @@ __global__ void __launch_bounds__(64 * NW) fwd_f16_kernel(FwdParams a) {
                     }
             }
             if (masked) {
+                // visible keys of this row form [vlo, vhi]; key - vlo <= vhi - vlo (unsigned)
+                const int off = ks + 4 * lg - vlo[qb];
 #pragma unroll
                 for (int kb = 0; kb < S::NKB; ++kb)
 #pragma unroll
                     for (int i = 0; i < 4; ++i)
-                        st[kb][qb][i] += visible(a, ks + 16 * kb + 4 * lg + i, qpos[qb]) ? 0.f : -INFINITY;
+                        st[kb][qb][i] = ((unsigned)(off + 16 * kb + i) <= vspan[qb]) ? st[kb][qb][i] : -INFINITY;
             }
             float mx = st[0][qb][0];
 #pragma unroll
@@ -323,13 +394,10 @@ __global__ void __launch_bounds__(64 * NW) fwd_f16_kernel(FwdParams a) {
         // ---- O^T += V^T P^T ---------------------------------------------------------------
 #pragma unroll
         for (int db = 0; db < S::NDB; ++db) {
-            const int d = 16 * db + tr_d;
 #pragma unroll
             for (int c = 0; c < S::BN / 32; ++c) {
-                const int k0 = 32 * c + 4 * lg + tr_key;          // keys for h = 0; h = 1 adds 16
-                const int k1 = k0 + 16;
-                const half4_t lo = lds_read_tr16(vl + k0 * 2 * D + 16 * vswz<D>(k0, d >> 3) + 2 * (d & 7));
-                const half4_t hi = lds_read_tr16(vl + k1 * 2 * D + 16 * vswz<D>(k1, d >> 3) + 2 * (d & 7));
+                const half4_t lo = lds_read_tr16(vl + voff[db] + (32 * c) * 2 * D);
+                const half4_t hi = lds_read_tr16(vl + voff[db] + (32 * c + 16) * 2 * D);
                 const half8_t vf = half8_t{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 #pragma unroll
                 for (int qb = 0; qb < S::QB; ++qb)
