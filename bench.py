@@ -82,7 +82,7 @@ def log(msg):
 class DecodeF16(Workload):
     name = "decode_f16"
     kind = "hbm"
-    kernel = "decode_split_kernel<128, 4, false>"
+    kernel = "decode_split_kernel<128, 4, false, false>"
 
     def __init__(self, dev, H=32, Hkv=8, D=128, L=4096):
         import numpy as np
@@ -139,7 +139,7 @@ class DecodeF16(Workload):
 class PagedQ8(Workload):
     name = "decode_paged_q8"
     kind = "hbm"
-    kernel = "decode_split_kernel<128, 4, true>"
+    kernel = "decode_split_kernel<128, 4, true, false>"
 
     def __init__(self, dev):
         import numpy as np

@@ -91,6 +91,21 @@ def test_decode_f16(dev, H, Hkv, D, L, W, cap):
     assert maxabs(got, want) < TOL_F16
 
 
+@pytest.mark.parametrize("H,Hkv,D,L,cap,tol", [
+    (32, 8, 128, 4096, 0.0, 1e-5),
+    (16, 2, 256, 777, 0.0, 1e-5),
+    (8, 2, 128, 1000, 50.0, 2e-5),
+])
+def test_decode_keeps_f32_accuracy(dev, H, Hkv, D, L, cap, tol):
+    """f16 K/V times the f32 query and softmax weights, each split into two f16 parts, are
+    exact products: the result must sit at f32 rounding level, far inside the f16 bound."""
+    say("decode f32-level accuracy H=%d Hkv=%d D=%d L=%d cap=%g" % (H, Hkv, D, L, cap))
+    c = synth.seed_of(2) + 1000 * H + L
+    q, k, v = synth.decode_inputs(c, H, Hkv, D, L)
+    got, _ = run_decode(dev, q, k, v, 0, cap)
+    assert maxabs(got, decode_oracle(q, k, v, 0, cap)) < tol
+
+
 def test_decode_split_sizes_agree(dev):
     say("decode split sizes")
     q, k, v = synth.decode_inputs(synth.seed_of(2), 32, 8, 128, 4096)
@@ -190,6 +205,25 @@ def test_paged_q8(dev, lens, H, Hkv, D, W, cap):
     want = paged_oracle(d, W, cap)
     assert np.all(np.isfinite(got))
     assert maxabs(got, want) < TOL_F16
+
+
+@pytest.mark.parametrize("lens,H,Hkv,D,vf", [
+    ([1000, 2049, 333], 32, 8, 128, 1.0),
+    ([700, 129], 16, 2, 128, 1.0),          # eight query heads per KV head
+    ([1000, 517], 8, 2, 128, 1e4),          # large V scales
+    ([1000, 517], 8, 2, 128, 1e-4),         # small V scales
+])
+def test_paged_q8_relative_accuracy(dev, lens, H, Hkv, D, vf):
+    """int8 K/V enter the products exactly; the V scales are normalised by a power of two
+    before the f16 split, so the relative error stays near f32 level for any scale range."""
+    say("paged relative accuracy lens=%s H=%d Hkv=%d D=%d vf=%g" % (lens, H, Hkv, D, vf))
+    d = synth.paged_inputs(synth.seed_of(5) + sum(lens), len(lens), H, Hkv, D, lens, n_poison=9)
+    d["v_scales"] = (d["v_scales"] * np.float32(vf)).astype(np.float32)
+    d["v_s"] = [(x * np.float32(vf)).astype(np.float32) for x in d["v_s"]]
+    got = run_paged(dev, d)
+    want = paged_oracle(d)
+    assert np.all(np.isfinite(got))
+    assert maxabs(got, want) < 5e-5 * np.abs(want).max()
 
 
 @pytest.fixture(scope="module")

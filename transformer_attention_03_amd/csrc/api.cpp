@@ -79,7 +79,7 @@ struct DecodePlan {
 };
 
 int heads_per_wg(int group) {
-    for (int gc : {4, 2, 1})
+    for (int gc : {8, 4, 2, 1})
         if (group % gc == 0) return gc;
     return 1;
 }
@@ -90,15 +90,17 @@ DecodePlan plan_decode(int batch, int num_heads, int num_kv_heads, int head_dim,
     const int group = num_heads / num_kv_heads;
     p.gc = heads_per_wg(group);
     p.nch = group / p.gc;
-    // one block per wave at least
-    const int min_t = ta03::decode_waves() * ta03::decode_tokens_per_block(head_dim, paged);
+    // Whole rounds of 16-token blocks per wave, at least two; aim for about three waves of
+    // workgroups over the resident capacity (256 CUs), which keeps the tail of ragged paged
+    // lengths short while the per-workgroup merge stays a small share.
+    const int unit = ta03::decode_waves(head_dim, paged) * ta03::decode_tokens_per_block();
     int t = g_split_override;
     if (t <= 0) {
-        // aim for about eight workgroups per compute unit over 256 CUs
         const long rows = (long)eff_len * batch * num_kv_heads * p.nch;
-        long want = (rows + 2047) / 2048;
-        t = (int)(((want + min_t - 1) / min_t) * min_t);
-        if (t < min_t) t = min_t;
+        const long resident = 256L * ta03::decode_workgroups_per_cu(head_dim, paged);
+        const long want = (rows + 3 * resident - 1) / (3 * resident);
+        t = (int)(((want + unit - 1) / unit) * unit);
+        if (t < 2 * unit) t = 2 * unit;
     }
     // the paged kernel stages the page indices of one split in LDS
     if (paged && t > ta03::decode_max_split_tokens_paged()) t = ta03::decode_max_split_tokens_paged();

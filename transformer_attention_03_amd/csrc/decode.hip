@@ -1,4 +1,4 @@
-// Split-KV single-token decode for gfx950.
+// Split-KV single-token decode for gfx950, on the matrix cores.
 //
 // One query token per sequence attends over a KV cache held either as contiguous f16
 // rows ([num_kv_heads][kv_len][D], f32 query) or as 16-token pages of symmetric int8 rows
@@ -8,26 +8,33 @@
 // pageSize and a page table; kvLenSource = 1 reads kvLen from a buffer).
 //
 // Work decomposition (ours, not the pages'): grid (split, kv head x head chunk, batch).
-// A workgroup owns GC query heads that share one KV head (the K/V rows are read once for
-// all of them) and a contiguous logical token range.  Each of its NW waves streams blocks
-// of TB tokens (4 KB of K and 4 KB of V per block), with the loads of the next block
-// issued before the current one is processed (register double buffering):
-//   K phase: LPT = D/16 lanes per K row, 16 elements per lane, 128-bit loads; the partial
-//            dot products for the GC heads are summed across the LPT lanes with DPP.
-//   softmax: the block max per head is reduced across the wave; the running maximum is
-//            only moved (and the accumulators rescaled) when the block max exceeds it by
-//            more than 2^8, so most blocks skip the rescale; exp2 of each (token, head)
-//            score is evaluated once, by one lane, and parked in LDS.
-//   V phase: V rows are read fully coalesced (one 16-byte chunk per lane), and each lane
-//            accumulates p * v for the GC heads over its fixed chunk.
+// A workgroup owns GC <= 8 query heads that share one KV head (the K/V rows are read once
+// for all of them) and a contiguous logical token range.  Each of its NW waves streams
+// blocks of 16 tokens through a private ring of RING LDS slots filled by global->LDS DMA
+// (RING-1 blocks in flight, no staging registers, no barrier between waves).
+//
+// Both products run as f16 MFMAs with f32 accumulation while keeping f32 accuracy: every
+// f32 operand x (the scaled query, and the softmax weight p) is split as
+// hi = f16(x), lo = f16(x - hi), and hi and lo occupy two adjacent columns of the 16-wide
+// MFMA operand, so column 2g + part of a product holds part of head g.  int8 K/V values
+// and f16 K/V values are exact in f16, so each product term is exact and the pair sum
+// (one DPP add) restores q.k and p.v to about 2^-22 relative.
+//   QK:  S^T[token][col] = K[token][:] . Qx[col][:]       (16x16x32, A = K rows from LDS)
+//   PV:  O^T[d][col]    += V^T[d][token] . P^T[token][col] (16x16x16, A = V^T by LDS
+//        transposing reads), where P^T comes straight from the S^T accumulator layout.
+// The running maximum per head follows the block maxima exactly (every increase rescales),
+// so p <= 1.  For int8 V the per-token V scale is folded into p, normalised by a running
+// power of two of the largest V scale seen, which keeps the f16 operands in range.
+//
 // The waves of a workgroup are merged through LDS; the workgroups of one (sequence, KV
 // head) are merged by the last one to arrive (log-sum-exp over the split partials),
 // counted with a device-scope atomic that this last workgroup resets to zero.  Partials
 // travel through device-scope stores and loads, so no cache-wide fence is needed.
 //
 // Paged addressing is integer-exact: physical page = page_table[b][t >> 4], slot t & 15,
-// row ((page * 16 + slot) * Hkv + kvh) * D.  Rows at or past kv_len are never loaded, so
-// poisoned slots of a partial last page cannot reach the result.
+// row ((page * 16 + slot) * Hkv + kvh) * D.  Rows at or past kv_len are never read: the
+// DMA of a block's tail fetches the split's last valid row instead, and those tokens are
+// masked, so poisoned slots of a partial last page cannot reach the result.
 
 #include "device_common.hpp"
 #include "launch.hpp"
@@ -36,40 +43,108 @@ namespace ta03 {
 
 namespace {
 
-constexpr int kDecodeWaves = 8;
+constexpr int kTB = 16;                  // tokens per block: one MFMA tile
+constexpr int kLdsBudget = 136 * 1024;   // ring bytes per workgroup
 constexpr int kMaxSplits = 256;          // split partials merged per (sequence, head)
 constexpr int kMaxSplitTokens = 4096;    // paged: tokens per workgroup (page slice in LDS)
-constexpr float kRescaleSlack = 8.0f;    // log2 units: accumulators may grow to 2^8
 
-template <int D, int GC, bool PAGED>
-struct DecodeShape {
+template <int D, bool PAGED>
+struct DecShape {
     static constexpr int ESZ = PAGED ? 1 : 2;          // bytes per K/V element
-    static constexpr int LPT = D / 16;                  // K-phase lanes per row
-    static constexpr int RPW = 64 / LPT;                // K rows per wave-load
-    static constexpr int TB = 4096 / (D * 2);           // tokens per wave block (f16: 4 KB of K)
-    static constexpr int U = TB / RPW;                  // K row-sets per block
-    static constexpr int KCH = ESZ;                     // 16-byte chunks per lane per K row
-    static constexpr int EV = 8;                        // elements per lane per V row
-    static constexpr int CPR = D / EV;                  // lanes per V row (8-element chunks)
-    static constexpr int VR = 64 / CPR;                 // V rows per wave-load
-    static constexpr int NVL = TB / VR;                 // V loads per lane per block
-    static_assert(LPT >= 4 && LPT <= 16, "head_dim");
-    static_assert(GC <= 4, "heads per workgroup");
-    static_assert(U >= 1 && TB % RPW == 0 && TB % VR == 0, "block shape");
+    static constexpr int RB = D * ESZ;                  // bytes per K (or V) row
+    static constexpr int TILE = kTB * RB;               // bytes of K (or of V) per block
+    static constexpr int SCB = PAGED ? 512 : 0;         // K and V scales of a block
+    static constexpr int SLOT = 2 * TILE + SCB;
+    // f16: eight waves with two slots each where that fits, else four; int8: four waves (two
+    // workgroups share a compute unit).  Then as many ring slots per wave (up to four) as
+    // the budget allows.
+    static constexpr int NW = (!PAGED && 8 * 2 * SLOT <= kLdsBudget) ? 8 : 4;
+    static constexpr int RING = kLdsBudget / (NW * SLOT) >= 4 ? 4 : kLdsBudget / (NW * SLOT);
+    static constexpr int NT = 64 * NW;
+    static constexpr int WAVE_LDS = RING * SLOT;
+    static constexpr int TD = TILE / 1024;              // 16-byte DMAs per lane per tile
+    static constexpr int NDMA = 2 * TD + (PAGED ? 2 : 0);
+    static constexpr int RPL = RB >= 256 ? 1 : 256 / RB;  // rows per 256-byte bank line
+    static constexpr int CPR = RB / 16;                 // 16-byte chunks per row
+    static constexpr int KC = D / 32;                   // QK MFMA steps
+    static constexpr int DT = D / 16;                   // PV output tiles
+    static_assert(TILE % 1024 == 0 && CPR >= 4, "tile shape");
+    static_assert(RING >= 2, "at least one block in flight while one is processed");
 };
 
-template <int D, int GC, bool PAGED>
-struct BlockRegs {
-    using S = DecodeShape<D, GC, PAGED>;
-    uint4 k[S::U][S::KCH];
-    float ks[S::U];     // K scale of the K-phase row (paged)
-    float vs[S::U];     // V scale of the same row (paged)
-    // f16: 16-byte chunks (8 halves); int8: 8-byte chunks (8 bytes) in .x, .y
-    uint4 v[S::NVL];
-};
+// LDS swizzles at 16-byte granularity: chunk c of row r is stored at chunk position
+// c ^ sw(r).  K rows are read 16 rows at a time at one chunk, so ksw spreads 16 rows over
+// distinct banks; V rows are read in chunk pairs by the transposing loads, so vsw is even
+// and keeps each pair adjacent.
+template <int RPL>
+__device__ __forceinline__ int ksw(int r) {
+    if constexpr (RPL == 1) return r & 15;
+    else if constexpr (RPL == 2) return (r >> 1) & 7;
+    else return (r >> 2) & 3;
+}
+template <int RPL>
+__device__ __forceinline__ int vsw(int r) {
+    if constexpr (RPL == 1) return 2 * (r & 7);
+    else if constexpr (RPL == 2) return 2 * ((r >> 1) & 3);
+    else return 2 * ((r >> 2) & 1);
+}
 
 __device__ __forceinline__ int clamp_page(int p, int num_pages) {
     return p < 0 ? 0 : (p >= num_pages ? num_pages - 1 : p);
+}
+
+// 16 bytes (dwordx4) or 4 bytes (dword) per lane from global memory straight into LDS, at
+// lds_base + size * lane.  Issued as inline asm so that the compiler does not guard later
+// LDS reads with full vector-memory waits; completion is tracked per wave with counted
+// vmcnt waits.  m0 is written here and is used by nothing else in this kernel.
+__device__ __forceinline__ void dma16(const void* gptr, const void* lds_base) {
+    const uint32_t off = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)lds_base;
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
+                 :
+                 : "s"(__builtin_amdgcn_readfirstlane(off)), "v"(gptr)
+                 : "memory", "m0");
+}
+__device__ __forceinline__ void dma4(const void* gptr, const void* lds_base) {
+    const uint32_t off = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)lds_base;
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, off"
+                 :
+                 : "s"(__builtin_amdgcn_readfirstlane(off)), "v"(gptr)
+                 : "memory", "m0");
+}
+template <int N>
+__device__ __forceinline__ void wait_vmem_at_most() { asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory"); }
+__device__ __forceinline__ void wait_lds_reads() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
+// Reductions across the four 16-lane rows (lanes congruent mod 16) with the gfx950 lane
+// swaps: after permlane16_swap(x, x) (resp. permlane32_swap) a lane holds its own value
+// and that of lane ^ 16 (resp. ^ 32), in an order that depends on the lane.
+__device__ __forceinline__ float rows_max(float x) {
+    auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float rows_sum(float x) {
+    auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+// 2^e for integer e (exact); 0 below the normal range.
+__device__ __forceinline__ float pow2i(int e) {
+    return e < -126 ? 0.f : __int_as_float((min(e, 127) + 127) << 23);
+}
+
+// int8 -> f16 for the MFMA operands without any arithmetic: with u = b + 128 (sign bit
+// flipped) the f16 bit pattern 0x3C00 | u is exactly 1 + u / 1024.  For such values x a
+// product sum obeys  sum y b = 1024 sum y x - 1152 sum y,  so the kernel subtracts the
+// second term once per score (K) or once at the end (V).  A dword gives the f16 pairs
+// (u0, u2) and (u1, u3): the other operand of the product uses the same element order.
+__device__ __forceinline__ void i8x4_biased(uint32_t w, uint32_t& even, uint32_t& odd) {
+    w ^= 0x80808080u;
+    even = __builtin_amdgcn_perm(0x3C3C3C3Cu, w, 0x04020400u);
+    odd = __builtin_amdgcn_perm(0x3C3C3C3Cu, w, 0x04030401u);
 }
 
 struct RowCtx {
@@ -82,7 +157,7 @@ struct RowCtx {
     int Hkv, kvh, kv_len;
 };
 
-// Row index (token t of this KV head) in units of D elements.
+// Row index (token t of this KV head) in rows of D elements.
 template <bool PAGED>
 __device__ __forceinline__ size_t row_index(const RowCtx& c, int t) {
     if constexpr (PAGED) {
@@ -93,155 +168,261 @@ __device__ __forceinline__ size_t row_index(const RowCtx& c, int t) {
     }
 }
 
-template <int D, int GC, bool PAGED>
-__device__ __forceinline__ void load_block(BlockRegs<D, GC, PAGED>& B, const RowCtx& c, int tb,
-                                           int t_end, int j, int rg, int vrg, int vc) {
-    using S = DecodeShape<D, GC, PAGED>;
-#pragma unroll
-    for (int u = 0; u < S::U; ++u) {
-        const int t = tb + u * S::RPW + rg;
-        B.ks[u] = 1.f;
-        B.vs[u] = 1.f;
-        if (t < t_end) {
-            const size_t ri = row_index<PAGED>(c, t);
-            const char* kr = c.kbase + ri * D * S::ESZ;
-            if constexpr (PAGED) {
-                B.k[u][0] = ld_global_b128(kr + 16 * j);
-                B.ks[u] = c.kscales[ri];
-                B.vs[u] = c.vscales[ri];
-            } else {
-                B.k[u][0] = ld_global_b128(kr + 16 * j);
-                B.k[u][S::KCH - 1] = ld_global_b128(kr + 16 * (j + S::LPT));
-            }
-        } else {
-#pragma unroll
-            for (int q = 0; q < S::KCH; ++q) B.k[u][q] = make_uint4(0, 0, 0, 0);
-        }
-    }
-#pragma unroll
-    for (int r = 0; r < S::NVL; ++r) {
-        const int t = tb + r * S::VR + vrg;
-        if (t < t_end) {
-            const size_t ri = row_index<PAGED>(c, t);
-            const char* vp = c.vbase + ri * D * S::ESZ + S::EV * S::ESZ * vc;
-            if constexpr (PAGED) {
-                const uint2 x = *reinterpret_cast<const uint2*>(vp);
-                B.v[r] = make_uint4(x.x, x.y, 0, 0);
-            } else {
-                B.v[r] = ld_global_b128(vp);
-            }
-        } else {
-            B.v[r] = make_uint4(0, 0, 0, 0);
-        }
-    }
+// The same DMAs with a uniform 64-bit base in SGPRs and a 32-bit per-lane offset.
+__device__ __forceinline__ void dma16s(const void* sbase, uint32_t voff, const void* lds_base) {
+    const uint32_t off = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)lds_base;
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
+                 :
+                 : "s"(__builtin_amdgcn_readfirstlane(off)), "v"(voff), "s"(sbase)
+                 : "memory", "m0");
+}
+__device__ __forceinline__ void dma4s(const void* sbase, uint32_t voff, const void* lds_base) {
+    const uint32_t off = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)lds_base;
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, %2"
+                 :
+                 : "s"(__builtin_amdgcn_readfirstlane(off)), "v"(voff), "s"(sbase)
+                 : "memory", "m0");
 }
 
-template <int D, int GC, bool PAGED>
-__device__ __forceinline__ void process_block(const BlockRegs<D, GC, PAGED>& B, int tb, int t_end,
-                                              const DecodeParams& a, const float (&qr)[GC][16],
-                                              float (&m_run)[GC], float (&lsum)[GC],
-                                              float (&acc)[GC][DecodeShape<D, GC, PAGED>::EV],
-                                              float (*lds_p)[GC], int j, int rg, int vrg) {
-    using S = DecodeShape<D, GC, PAGED>;
-    // ---- K phase: scores in log2 units -----------------------------------------------
-    float sc[S::U][GC];
+// Per-lane byte offsets, relative to a block's first row, of the 16-byte chunks this lane
+// moves when the block's 16 rows are RS bytes apart in memory (a full block; paged, one
+// page).  Slot layout: K tile, V tile, 256 bytes of K scales, 256 bytes of V scales.
+template <int D, bool PAGED>
+struct DmaLane {
+    uint32_t k[DecShape<D, PAGED>::TD];
+    uint32_t v[DecShape<D, PAGED>::TD];
+    uint32_t sc;           // paged: scale of row lane & 15
+};
+
+template <int D, bool PAGED>
+__device__ __forceinline__ DmaLane<D, PAGED> dma_lane(int lane, uint32_t rs, int Hkv) {
+    using S = DecShape<D, PAGED>;
+    DmaLane<D, PAGED> L;
 #pragma unroll
-    for (int u = 0; u < S::U; ++u) {
-        float kf[16];
+    for (int i = 0; i < S::TD; ++i) {
+        const int p = 1024 * i + 16 * lane;
+        const int r = p / S::RB, cpos = (p % S::RB) / 16;
+        L.k[i] = r * rs + 16 * (cpos ^ ksw<S::RPL>(r));
+        L.v[i] = r * rs + 16 * (cpos ^ vsw<S::RPL>(r));
+    }
+    L.sc = (uint32_t)((lane & 15) * Hkv) * 4u;
+    return L;
+}
+
+// DMA the block of tokens tb .. tb+15 into a ring slot (row r of a tile = token tb + r,
+// swizzled chunks; scale areas: row r at 4r, repeated for lanes 16-63).  A full block (and,
+// paged, one whose 16 tokens share a page) takes the uniform-base path; otherwise every
+// lane resolves its own row, and tokens at or past t_end fetch the row of token t_end - 1.
+template <int D, bool PAGED>
+__device__ __forceinline__ void dma_block(char* slot, const RowCtx& c, const DmaLane<D, PAGED>& L,
+                                          int tb, int t_end, int lane) {
+    using S = DecShape<D, PAGED>;
+    const bool full = tb + kTB <= t_end && (!PAGED || (tb & 15) == 0);
+    if (full) {
+        size_t row0;
         if constexpr (PAGED) {
-            i8x16_to_f32(B.k[u][0], kf);
+            const int pg = __builtin_amdgcn_readfirstlane(c.pages[(tb >> 4) - c.page0]);
+            row0 = (size_t)pg * 16 * c.Hkv + c.kvh;
         } else {
-            f16x8_to_f32(B.k[u][0], kf);
-            f16x8_to_f32(B.k[u][S::KCH - 1], kf + 8);
+            row0 = (size_t)c.kvh * c.kv_len + tb;
         }
-        const bool valid = (tb + u * S::RPW + rg) < t_end;
+        const char* kb = c.kbase + row0 * S::RB;
+        const char* vb = c.vbase + row0 * S::RB;
 #pragma unroll
-        for (int g = 0; g < GC; ++g) {
-            float d0 = 0.f;
-#pragma unroll
-            for (int e = 0; e < 16; ++e) d0 = __builtin_fmaf(qr[g][e], kf[e], d0);
-            float s = group_sum<S::LPT>(d0) * B.ks[u];
-            if (a.softcap > 0.f)
-                s = a.softcap * tanh_via_exp(s * a.scale * a.inv_softcap) * kLog2e;
-            else
-                s = s * a.scale_log2;
-            sc[u][g] = valid ? s : -INFINITY;
+        for (int i = 0; i < S::TD; ++i) {
+            dma16s(kb, L.k[i], slot + 1024 * i);
+            dma16s(vb, L.v[i], slot + S::TILE + 1024 * i);
         }
-    }
-
-    // ---- block max per head, lazy rescale ----------------------------------------------
+        if constexpr (PAGED) {
+            dma4s(c.kscales + row0, L.sc, slot + 2 * S::TILE);
+            dma4s(c.vscales + row0, L.sc, slot + 2 * S::TILE + 256);
+        }
+    } else {
 #pragma unroll
-    for (int g = 0; g < GC; ++g) {
-        float mb = sc[0][g];
-#pragma unroll
-        for (int u = 1; u < S::U; ++u) mb = fmaxf(mb, sc[u][g]);
-        mb = strided_max<S::LPT>(mb);
-        if (mb > m_run[g] + kRescaleSlack) {
-            const float alpha = (m_run[g] == -INFINITY) ? 0.f : fast_exp2(m_run[g] - mb);
-            m_run[g] = mb;
-            lsum[g] *= alpha;
-#pragma unroll
-            for (int e = 0; e < S::EV; ++e) acc[g][e] *= alpha;
+        for (int i = 0; i < S::TD; ++i) {
+            const int p = 1024 * i + 16 * lane;
+            const int r = p / S::RB, cpos = (p % S::RB) / 16;
+            const size_t ri = row_index<PAGED>(c, min(tb + r, t_end - 1));
+            dma16(c.kbase + ri * S::RB + 16 * (cpos ^ ksw<S::RPL>(r)), slot + 1024 * i);
+            dma16(c.vbase + ri * S::RB + 16 * (cpos ^ vsw<S::RPL>(r)), slot + S::TILE + 1024 * i);
+        }
+        if constexpr (PAGED) {
+            const size_t ri = row_index<PAGED>(c, min(tb + (lane & 15), t_end - 1));
+            dma4(c.kscales + ri, slot + 2 * S::TILE);
+            dma4(c.vscales + ri, slot + 2 * S::TILE + 256);
         }
     }
-
-    // ---- p = exp2(s - m): one lane per (token, head), parked in LDS ----------------------
-    if (j < GC) {
-#pragma unroll
-        for (int u = 0; u < S::U; ++u) {
-            float x = sc[u][0], m = m_run[0];
-#pragma unroll
-            for (int g = 1; g < GC; ++g) {
-                x = (j == g) ? sc[u][g] : x;
-                m = (j == g) ? m_run[g] : m;
-            }
-            const float p = (x == -INFINITY) ? 0.f : fast_exp2(x - m);
-#pragma unroll
-            for (int g = 0; g < GC; ++g) lsum[g] += (j == g) ? p : 0.f;
-            lds_p[u * S::RPW + rg][j] = PAGED ? p * B.vs[u] : p;
-        }
-    }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-
-    // ---- V phase -----------------------------------------------------------------------
-#pragma unroll
-    for (int r = 0; r < S::NVL; ++r) {
-        const int tl = r * S::VR + vrg;
-        float pg[GC];
-#pragma unroll
-        for (int g = 0; g < GC; ++g) pg[g] = lds_p[tl][g];
-        float vf[S::EV];
-        if constexpr (PAGED) i8x8_to_f32(B.v[r].x, B.v[r].y, vf);
-        else f16x8_to_f32(B.v[r], vf);
-#pragma unroll
-        for (int g = 0; g < GC; ++g)
-#pragma unroll
-            for (int e = 0; e < S::EV; ++e) acc[g][e] = __builtin_fmaf(pg[g], vf[e], acc[g][e]);
-    }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-template <int D, int GC, bool PAGED>
-__global__ void __launch_bounds__(64 * kDecodeWaves) decode_split_kernel(DecodeParams a) {
-    using S = DecodeShape<D, GC, PAGED>;
-    constexpr int NW = kDecodeWaves;
-    constexpr int NT = 64 * NW;
-    __shared__ float lds_p[NW][S::TB][GC];
-    __shared__ float lds_o[NW][GC][D];
+// Per-wave state of the online softmax for the MFMA column this lane holds.
+template <int D>
+struct WaveAcc {
+    float4_t o[D / 16];   // O^T tiles: column lane % 16, d = 16 dt + 4 (lane / 16) + v
+    float m;              // running max of the column's head (log2 units)
+    float l;              // this lane's share of the running sum of p
+    float xs;             // paged: this lane's share of the sum of the PV operand values
+    int e;                // paged: running exponent of the largest V scale (wave-uniform)
+};
+
+__device__ __forceinline__ uint32_t rows_max_u(uint32_t x) {
+    auto a = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+    x = max((uint32_t)a[0], (uint32_t)a[1]);
+    auto b = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+    return max((uint32_t)b[0], (uint32_t)b[1]);
+}
+
+// f16 operand of the split product: hi in even columns, lo in odd columns.
+__device__ __forceinline__ _Float16 split_part(float x, bool odd) {
+    const _Float16 hi = (_Float16)x;
+    const _Float16 lo = (_Float16)(x - (float)hi);
+    return odd ? lo : hi;
+}
+
+// One block of 16 tokens.  full: all 16 tokens are below t_end (no masking).
+template <int D, bool PAGED, bool CAP>
+__device__ __forceinline__ void process_block(const char* slot, int tb, int t_end, bool full,
+                                              float cap_log2, float qbias,
+                                              const half8_t (&qx)[D / 32], WaveAcc<D>& A,
+                                              int lane) {
+    using S = DecShape<D, PAGED>;
+    const char* kt = slot;
+    const char* vt = slot + S::TILE;
+    const int r16 = lane & 15;     // K row (token) of the A operand; MFMA column
+    const int g4 = lane >> 4;      // 16-lane row of the wave
+    const bool odd = lane & 1;
+
+    // ---- S^T = K Qx^T --------------------------------------------------------------------
+    float4_t sacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kc = 0; kc < S::KC; ++kc) {
+        half8_t a;
+        if constexpr (PAGED) {
+            const int c = 2 * kc + (g4 >> 1);
+            const uint2 w = *reinterpret_cast<const uint2*>(kt + r16 * S::RB + 16 * (c ^ ksw<S::RPL>(r16)) + 8 * (g4 & 1));
+            uint32_t e0, o0, e1, o1;
+            i8x4_biased(w.x, e0, o0);
+            i8x4_biased(w.y, e1, o1);
+            a = __builtin_bit_cast(half8_t, u32x4_t{e0, o0, e1, o1});
+        } else {
+            const int c = 4 * kc + g4;
+            a = *reinterpret_cast<const half8_t*>(kt + r16 * S::RB + 16 * (c ^ ksw<S::RPL>(r16)));
+        }
+        sacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, qx[kc], sacc, 0, 0, 0);
+    }
+
+    // scores of tokens tb + 4 g4 + v for this lane's column (hi + lo pair summed)
+    float4_t ks = {1.f, 1.f, 1.f, 1.f}, vs = {1.f, 1.f, 1.f, 1.f};
+    if constexpr (PAGED) {
+        ks = *reinterpret_cast<const float4_t*>(slot + 2 * S::TILE + 16 * g4);
+        vs = *reinterpret_cast<const float4_t*>(slot + 2 * S::TILE + 256 + 16 * g4);
+    }
+    float s[4];
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+        float x = sacc[v] + dpp_f<kDppXor1>(sacc[v]);
+        if constexpr (PAGED) x = __builtin_fmaf(x, 1024.f, -qbias) * ks[v];
+        if constexpr (CAP) x = tanh_via_exp(x) * cap_log2;
+        s[v] = x;
+    }
+    if (!full) {
+#pragma unroll
+        for (int v = 0; v < 4; ++v) s[v] = (tb + 4 * g4 + v < t_end) ? s[v] : -INFINITY;
+    }
+    const float mb = rows_max(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])));
+    int eb = A.e;
+    if constexpr (PAGED) {
+        // exponent bound of the block's V scales (tokens past t_end repeat a valid row)
+        uint32_t vb = max(max(__float_as_uint(vs[0]) & 0x7FFFFFFFu, __float_as_uint(vs[1]) & 0x7FFFFFFFu),
+                          max(__float_as_uint(vs[2]) & 0x7FFFFFFFu, __float_as_uint(vs[3]) & 0x7FFFFFFFu));
+        vb = rows_max_u(vb);
+        eb = (int)(vb >> 23) - 126;   // |vs| < 2^eb
+    }
+
+    // ---- move the running max (and the V-scale exponent) when a block exceeds them ---------
+    const bool need = mb > A.m || eb > A.e;
+    if (__builtin_amdgcn_ballot_w64(need)) {
+        const float mn = fmaxf(A.m, mb);
+        const int en = max(A.e, eb);
+        const float al = fast_exp2(A.m - mn);          // 0 on the first block (m = -inf)
+        const float ao = al * pow2i(A.e - en);
+        A.l *= al;
+        A.xs *= ao;
+#pragma unroll
+        for (int dt = 0; dt < S::DT; ++dt) A.o[dt] *= ao;
+        A.m = mn;
+        A.e = en;
+    }
+
+    // ---- p = 2^(s - m), split into the f16 hi (even column) / lo (odd column) operand ------
+    const float pe = PAGED ? pow2i(-A.e) : 1.f;
+    float xv[4];
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+        const float p = fast_exp2(s[v] - A.m);
+        A.l += p;
+        xv[v] = PAGED ? p * vs[v] * pe : p;
+        if constexpr (PAGED) A.xs += xv[v];
+    }
+    // paged: token order (0, 2, 1, 3), the order of the biased int8 V operand
+    const half4_t pb = PAGED ? half4_t{split_part(xv[0], odd), split_part(xv[2], odd),
+                                       split_part(xv[1], odd), split_part(xv[3], odd)}
+                             : half4_t{split_part(xv[0], odd), split_part(xv[1], odd),
+                                       split_part(xv[2], odd), split_part(xv[3], odd)};
+
+    // ---- O^T += V^T P^T --------------------------------------------------------------------
+    if constexpr (PAGED) {
+        // one transposing byte read feeds two d tiles: source lane j gives 8 bytes of token
+        // row 4 g4 + (j/2 & 3), d tile dt + j/8, half j & 1
+        const int j = lane & 15;
+        const int r = 4 * g4 + ((j >> 1) & 3);
+        const int hsel = j >> 3;
+#pragma unroll
+        for (int dt = 0; dt < S::DT; dt += 2) {
+            const char* addr = vt + r * S::RB + 16 * ((dt + hsel) ^ vsw<S::RPL>(r)) + 8 * (j & 1);
+            typedef int i2_t __attribute__((ext_vector_type(2)));
+            const i2_t w = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+                (__attribute__((address_space(3))) i2_t*)(uintptr_t)(const __attribute__((address_space(3))) char*)addr);
+            uint32_t e0, o0, e1, o1;
+            i8x4_biased((uint32_t)w.x, e0, o0);
+            i8x4_biased((uint32_t)w.y, e1, o1);
+            const half4_t a0 = __builtin_bit_cast(half4_t, uint2{e0, o0});
+            const half4_t a1 = __builtin_bit_cast(half4_t, uint2{e1, o1});
+            A.o[dt] = __builtin_amdgcn_mfma_f32_16x16x16f16(a0, pb, A.o[dt], 0, 0, 0);
+            A.o[dt + 1] = __builtin_amdgcn_mfma_f32_16x16x16f16(a1, pb, A.o[dt + 1], 0, 0, 0);
+        }
+    } else {
+        // source lane j gives 4 halves of token row 4 g4 + j/4 at d = 16 dt + 4 (j & 3)
+        const int j = lane & 15;
+        const int r = 4 * g4 + (j >> 2);
+        const int csel = (j & 3) >> 1;
+#pragma unroll
+        for (int dt = 0; dt < S::DT; ++dt) {
+            const char* addr = vt + r * S::RB + 16 * ((2 * dt + csel) ^ vsw<S::RPL>(r)) + 8 * (j & 1);
+            typedef short s4_t __attribute__((ext_vector_type(4)));
+            const s4_t w = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) s4_t*)(uintptr_t)(const __attribute__((address_space(3))) char*)addr);
+            A.o[dt] = __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(half4_t, w), pb, A.o[dt], 0, 0, 0);
+        }
+    }
+}
+
+template <int D, int GC, bool PAGED, bool CAP>
+__global__ void __launch_bounds__((DecShape<D, PAGED>::NT)) decode_split_kernel(DecodeParams a) {
+    using S = DecShape<D, PAGED>;
+    constexpr int NW = S::NW;
+    constexpr int NT = S::NT;
+    static_assert(GC >= 1 && GC <= 8, "heads per workgroup");
+    // per-wave DMA rings; the wave-merge buffer lds_o reuses this memory afterwards
+    __shared__ __attribute__((aligned(1024))) char rings[NW * S::WAVE_LDS];
     __shared__ float lds_m[NW][GC];
     __shared__ float lds_l[NW][GC];
-    __shared__ float lds_w[GC][kMaxSplits];
-    __shared__ float lds_L[GC];
     __shared__ int lds_pages[PAGED ? kMaxSplitTokens / 16 + 1 : 1];
     __shared__ int lds_last;
-    static_assert(NW * D >= kMaxSplits, "l of the split partials is parked in lds_o");
+    float(*lds_o)[GC][D] = reinterpret_cast<float(*)[GC][D]>(rings);                    // [NW][GC][D]
+    static_assert(sizeof(float) * NW * GC * D <= NW * S::WAVE_LDS, "merge buffer fits in the rings");
 
     const int lane = threadIdx.x & 63;
-    const int w = threadIdx.x >> 6;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int split = blockIdx.x;
     const int G = a.H / a.Hkv;
     const int nch = G / GC;
@@ -267,34 +448,6 @@ __global__ void __launch_bounds__(64 * kDecodeWaves) decode_split_kernel(DecodeP
     const int t_begin = k_lo + split * a.split_tokens;
     const int t_end = min(L, t_begin + a.split_tokens);
 
-    // ---- query slice held by this lane for the K phase ----------------------------------
-    const int j = lane % S::LPT;          // position inside the row's lane group
-    const int rg = lane / S::LPT;         // row within a K row-set
-    float qr[GC][16];
-#pragma unroll
-    for (int g = 0; g < GC; ++g) {
-        const float* qh = a.q + ((size_t)b * a.H + h0 + g) * D;
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-            int d;
-            if constexpr (PAGED) d = 16 * j + e;
-            else d = (e < 8) ? 8 * j + e : 8 * (j + S::LPT) + (e - 8);
-            qr[g][e] = qh[d];
-        }
-    }
-
-    const int vrg = lane / S::CPR;        // row within a V row-set
-    const int vc = lane % S::CPR;         // V chunk owned by this lane
-
-    float m_run[GC], lsum[GC], acc[GC][S::EV];
-#pragma unroll
-    for (int g = 0; g < GC; ++g) {
-        m_run[g] = -INFINITY;
-        lsum[g] = 0.f;
-#pragma unroll
-        for (int e = 0; e < S::EV; ++e) acc[g][e] = 0.f;
-    }
-
     RowCtx c;
     c.kbase = reinterpret_cast<const char*>(a.k);
     c.vbase = reinterpret_cast<const char*>(a.v);
@@ -313,41 +466,104 @@ __global__ void __launch_bounds__(64 * kDecodeWaves) decode_split_kernel(DecodeP
         __syncthreads();
     }
 
-    // ---- stream this wave's blocks, two register buffers in flight ---------------------
-    constexpr int STRIDE = NW * S::TB;
-    BlockRegs<D, GC, PAGED> A, Bf;
-    int tb = t_begin + w * S::TB;
-    if (tb < t_end) load_block(A, c, tb, t_end, j, rg, vrg, vc);
-    while (tb < t_end) {
-        const int t1 = tb + STRIDE;
-        if (t1 < t_end) load_block(Bf, c, t1, t_end, j, rg, vrg, vc);
-        process_block(A, tb, t_end, a, qr, m_run, lsum, acc, lds_p[w], j, rg, vrg);
-        if (t1 >= t_end) break;
-        const int t2 = t1 + STRIDE;
-        if (t2 < t_end) load_block(A, c, t2, t_end, j, rg, vrg, vc);
-        process_block(Bf, t1, t_end, a, qr, m_run, lsum, acc, lds_p[w], j, rg, vrg);
-        tb = t2;
+    // ---- this wave's blocks start at first + k * NW * 16; fill the ring ------------------
+    constexpr int STRIDE = NW * kTB;
+    char* ring = rings + w * S::WAVE_LDS;
+    const int first = t_begin + w * kTB;
+    const int nb = first < t_end ? (t_end - first + STRIDE - 1) / STRIDE : 0;
+    const DmaLane<D, PAGED> dl = dma_lane<D, PAGED>(lane, (uint32_t)((PAGED ? a.Hkv : 1) * S::RB), a.Hkv);
+#pragma unroll
+    for (int k = 0; k < S::RING - 1; ++k)
+        if (k < nb) dma_block<D, PAGED>(ring + k * S::SLOT, c, dl, first + k * STRIDE, t_end, lane);
+
+    // ---- Qx: B operand of the QK product.  Column n = lane % 16 holds part n & 1 of head
+    // n / 2 (hi, lo); k = d = 32 kc + 8 (lane / 16) + e, with e in the element order of the
+    // K operand (int8: 0 2 1 3 4 6 5 7).  The query is pre-multiplied so that the scores come
+    // out in log2 units (or as the tanh argument when a cap is set).
+    const float qmul = CAP ? a.scale * a.inv_softcap : a.scale_log2;
+    const float cap_log2 = a.softcap * kLog2e;
+    const int col = lane & 15;
+    const int hq = col >> 1;
+    half8_t qx[S::KC];
+    float qbias;
+    {
+        float qf[S::KC][8];
+        const float* qh = a.q + ((size_t)b * a.H + h0 + min(hq, GC - 1)) * D + 8 * (lane >> 4);
+#pragma unroll
+        for (int kc = 0; kc < S::KC; ++kc) {
+            const float4_t x0 = *reinterpret_cast<const float4_t*>(qh + 32 * kc);
+            const float4_t x1 = *reinterpret_cast<const float4_t*>(qh + 32 * kc + 4);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                qf[kc][e] = x0[e];
+                qf[kc][4 + e] = x1[e];
+            }
+        }
+        // settle the q loads here, so that inside the loop only the DMA counter is waited on
+#pragma unroll
+        for (int kc = 0; kc < S::KC; ++kc)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) asm volatile("" ::"v"(qf[kc][e]));
+        constexpr int kOrder[8] = {0, 2, 1, 3, 4, 6, 5, 7};
+        float qsum = 0.f;
+#pragma unroll
+        for (int kc = 0; kc < S::KC; ++kc)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float x = hq < GC ? qf[kc][PAGED ? kOrder[e] : e] * qmul : 0.f;
+                qx[kc][e] = split_part(x, col & 1);
+                qsum += (float)qx[kc][e];
+            }
+        // int8 K: the bias term 1152 * sum_d q[d] of the head (hi + lo columns, all rows)
+        qsum = rows_sum(qsum);
+        qbias = 1152.f * (qsum + dpp_f<kDppXor1>(qsum));
     }
 
-    // ---- merge inside the wave --------------------------------------------------------
+    WaveAcc<D> A;
 #pragma unroll
-    for (int g = 0; g < GC; ++g) {
-        lsum[g] = strided_sum<S::LPT>(lsum[g]);     // lanes j == g held it; others hold 0
-        lsum[g] = group_sum<S::LPT>(lsum[g]);
-#pragma unroll
-        for (int e = 0; e < S::EV; ++e) acc[g][e] = strided_sum<S::CPR>(acc[g][e]);
+    for (int dt = 0; dt < S::DT; ++dt) A.o[dt] = float4_t{0.f, 0.f, 0.f, 0.f};
+    A.m = -INFINITY;
+    A.l = 0.f;
+    A.xs = 0.f;
+    A.e = PAGED ? -126 : 0;
+
+    for (int k = 0; k < nb; ++k) {
+        const int kn = k + S::RING - 1;
+        if (kn < nb) {
+            // slot kn % RING was read in the previous iteration: those reads must be done
+            wait_lds_reads();
+            dma_block<D, PAGED>(ring + (kn % S::RING) * S::SLOT, c, dl, first + kn * STRIDE, t_end, lane);
+        }
+        // block k has landed once no more than (blocks issued after it) * NDMA loads remain
+        const int after = min(S::RING - 1, nb - 1 - k);
+        if (after >= 3) wait_vmem_at_most<3 * S::NDMA>();
+        else if (after == 2) wait_vmem_at_most<2 * S::NDMA>();
+        else if (after == 1) wait_vmem_at_most<S::NDMA>();
+        else wait_vmem_at_most<0>();
+        const int tb = first + k * STRIDE;
+        process_block<D, PAGED, CAP>(ring + (k % S::RING) * S::SLOT, tb, t_end, tb + kTB <= t_end,
+                                     cap_log2, qbias, qx, A, lane);
     }
-    if (lane < S::CPR) {
+
+    // ---- finish the wave: pair sums (hi + lo columns), row sums over the 16-lane rows ------
+    const float lw = rows_sum(A.l);
+    const float oscale = PAGED ? pow2i(A.e) : 1.f;
+    const float vbias = PAGED ? 1152.f * rows_sum(A.xs) : 0.f;   // int8 V: 1152 * sum of operands
+    __syncthreads();                      // every wave is done with its ring
+    {
+        const bool writer = (col & 1) == 0 && hq < GC;
 #pragma unroll
-        for (int g = 0; g < GC; ++g)
+        for (int dt = 0; dt < S::DT; ++dt)
 #pragma unroll
-            for (int e = 0; e < S::EV; ++e) lds_o[w][g][lane * S::EV + e] = acc[g][e];
-    }
-    if (lane == 0) {
-#pragma unroll
-        for (int g = 0; g < GC; ++g) {
-            lds_m[w][g] = m_run[g];
-            lds_l[w][g] = lsum[g];
+            for (int v = 0; v < 4; ++v) {
+                float o = A.o[dt][v] + dpp_f<kDppXor1>(A.o[dt][v]);
+                if constexpr (PAGED) o = __builtin_fmaf(o, 1024.f, -vbias);
+                o *= oscale;
+                if (writer) lds_o[w][hq][16 * dt + 4 * (lane >> 4) + v] = o;
+            }
+        if (writer && lane < 16) {
+            lds_m[w][hq] = A.m;
+            lds_l[w][hq] = lw;
         }
     }
     __syncthreads();
@@ -397,79 +613,79 @@ __global__ void __launch_bounds__(64 * kDecodeWaves) decode_split_kernel(DecodeP
     __syncthreads();
     if (!lds_last) return;
 
-    // (0) start fetching the first partial outputs of this thread's (head, d) pairs
-    constexpr int PF = 16;
+    // One pass over the split partials per (head, d) pair, entirely in registers: the
+    // partials of CH splits are fetched together (outputs, maxima and sums), folded into a
+    // running maximum M, weighted sum and normaliser, then the next CH splits.
     constexpr int PER = (GC * D + NT - 1) / NT;     // (head, d) pairs per thread
-    float pre[PER][PF];
+    constexpr int CH = PER <= 1 ? 32 : (PER <= 2 ? 16 : (PER <= 4 ? 8 : 4));
+    float M[PER], Lsum[PER], acc[PER];
 #pragma unroll
     for (int r = 0; r < PER; ++r) {
-        const int i = threadIdx.x + r * NT;
-        if (i < GC * D) {
+        M[r] = -INFINITY;
+        Lsum[r] = 0.f;
+        acc[r] = 0.f;
+    }
+    for (int s0 = 0; s0 < n_live; s0 += CH) {
+        float ms[PER][CH], ls[PER][CH], os[PER][CH];
+#pragma unroll
+        for (int r = 0; r < PER; ++r) {
+            const int i = min(threadIdx.x + r * NT, GC * D - 1);
             const size_t row = (part_base + i / D) * a.n_split_max;
 #pragma unroll
-            for (int s = 0; s < PF; ++s)
-                pre[r][s] = s < n_live ? load_agent(a.part_o + (row + s) * D + (i % D)) : 0.f;
+            for (int u = 0; u < CH; ++u) {
+                const bool in = s0 + u < n_live;
+                const size_t slot = row + min(s0 + u, n_live - 1);
+                ms[r][u] = load_agent(a.part_m + slot);
+                ls[r][u] = load_agent(a.part_l + slot);
+                os[r][u] = load_agent(a.part_o + slot * D + (i % D));
+                if (!in) {
+                    ms[r][u] = -INFINITY;
+                    ls[r][u] = 0.f;
+                    os[r][u] = 0.f;
+                }
+            }
+        }
+#pragma unroll
+        for (int r = 0; r < PER; ++r) {
+            float mc = M[r];
+#pragma unroll
+            for (int u = 0; u < CH; ++u) mc = fmaxf(mc, ms[r][u]);
+            const float f = (M[r] == -INFINITY) ? 0.f : fast_exp2(M[r] - mc);
+            acc[r] *= f;
+            Lsum[r] *= f;
+#pragma unroll
+            for (int u = 0; u < CH; ++u) {
+                const float wgt = (ms[r][u] == -INFINITY) ? 0.f : fast_exp2(ms[r][u] - mc);
+                acc[r] = __builtin_fmaf(wgt, os[r][u], acc[r]);
+                Lsum[r] = __builtin_fmaf(wgt, ls[r][u], Lsum[r]);
+            }
+            M[r] = mc;
         }
     }
-    // (1) m and l of every split, one (head, split) pair per thread
-    float* lds_ls = &lds_o[0][0][0];      // l of (g, s) at g * n_live + s
-    for (int i = threadIdx.x; i < GC * n_live; i += NT) {
-        const int g = i / n_live, s = i % n_live;
-        const size_t slot = (part_base + g) * a.n_split_max + s;
-        lds_w[g][s] = load_agent(a.part_m + slot);
-        lds_ls[i] = load_agent(a.part_l + slot);
-    }
-    __syncthreads();
-    // (2) per head: M, weights exp2(m_s - M), L = sum w_s l_s  (one wave per head)
-    for (int g = w; g < GC; g += NW) {
-        float M = -INFINITY;
-        for (int s = lane; s < n_live; s += 64) M = fmaxf(M, lds_w[g][s]);
-        M = strided_max<1>(M);
-        float Ls = 0.f;
-        for (int s = lane; s < n_live; s += 64) {
-            const float ms = lds_w[g][s];
-            const float f = (ms == -INFINITY) ? 0.f : fast_exp2(ms - M);
-            lds_w[g][s] = f;
-            Ls += f * lds_ls[g * n_live + s];
-        }
-        Ls = strided_sum<1>(Ls);
-        if (lane == 0) lds_L[g] = Ls;
-    }
-    __syncthreads();
-    // (3) o = sum_s w_s o_s / L, one (head, d) per thread
 #pragma unroll
     for (int r = 0; r < PER; ++r) {
         const int i = threadIdx.x + r * NT;
-        if (i >= GC * D) break;
-        const int g = i / D, d = i % D;
-        const size_t row = (part_base + g) * a.n_split_max;
-        float os = 0.f;
-#pragma unroll
-        for (int s = 0; s < PF; ++s) os += (s < n_live ? lds_w[g][s] : 0.f) * pre[r][s];
-        int s = PF;
-        for (; s + 8 <= n_live; s += 8) {
-            float v[8];
-#pragma unroll
-            for (int u = 0; u < 8; ++u) v[u] = load_agent(a.part_o + (row + s + u) * D + d);
-#pragma unroll
-            for (int u = 0; u < 8; ++u) os += lds_w[g][s + u] * v[u];
-        }
-        for (; s < n_live; ++s) os += lds_w[g][s] * load_agent(a.part_o + (row + s) * D + d);
-        const float Ls = lds_L[g];
-        a.o[(part_base + g) * D + d] = Ls != 0.f ? os / Ls : 0.f;
+        if (i < GC * D) a.o[(part_base + i / D) * D + (i % D)] = Lsum[r] != 0.f ? acc[r] / Lsum[r] : 0.f;
     }
+}
+
+template <int D, bool PAGED, bool CAP>
+hipError_t launch_decode_c(const DecodeParams& p, int gc, dim3 grid, hipStream_t st) {
+    const dim3 block(DecShape<D, PAGED>::NT);
+    switch (gc) {
+        case 1: hipLaunchKernelGGL((decode_split_kernel<D, 1, PAGED, CAP>), grid, block, 0, st, p); break;
+        case 2: hipLaunchKernelGGL((decode_split_kernel<D, 2, PAGED, CAP>), grid, block, 0, st, p); break;
+        case 4: hipLaunchKernelGGL((decode_split_kernel<D, 4, PAGED, CAP>), grid, block, 0, st, p); break;
+        case 8: hipLaunchKernelGGL((decode_split_kernel<D, 8, PAGED, CAP>), grid, block, 0, st, p); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
 }
 
 template <int D, bool PAGED>
 hipError_t launch_decode_d(const DecodeParams& p, int gc, dim3 grid, hipStream_t st) {
-    const dim3 block(64 * kDecodeWaves);
-    switch (gc) {
-        case 1: hipLaunchKernelGGL((decode_split_kernel<D, 1, PAGED>), grid, block, 0, st, p); break;
-        case 2: hipLaunchKernelGGL((decode_split_kernel<D, 2, PAGED>), grid, block, 0, st, p); break;
-        case 4: hipLaunchKernelGGL((decode_split_kernel<D, 4, PAGED>), grid, block, 0, st, p); break;
-        default: return hipErrorInvalidValue;
-    }
-    return hipGetLastError();
+    return p.softcap > 0.f ? launch_decode_c<D, PAGED, true>(p, gc, grid, st)
+                           : launch_decode_c<D, PAGED, false>(p, gc, grid, st);
 }
 
 }  // namespace
@@ -494,15 +710,29 @@ hipError_t launch_decode(const DecodeParams& p, int head_dim, int gc, bool paged
     return hipErrorInvalidValue;
 }
 
-int decode_tokens_per_block(int head_dim, bool paged) {
-    (void)paged;
-    return 4096 / (head_dim * 2);
+int decode_tokens_per_block() { return kTB; }
+
+int decode_waves(int head_dim, bool paged) {
+    if (paged) return head_dim == 64 ? DecShape<64, true>::NW : head_dim == 128 ? DecShape<128, true>::NW : DecShape<256, true>::NW;
+    return head_dim == 64 ? DecShape<64, false>::NW : head_dim == 128 ? DecShape<128, false>::NW : DecShape<256, false>::NW;
 }
 
-int decode_waves() { return kDecodeWaves; }
+int decode_workgroups_per_cu(int head_dim, bool paged) {
+    // 160 KB of LDS per compute unit; besides the rings a workgroup holds about 2 KB more
+    auto per = [](int ring_bytes) { return (160 * 1024) / (ring_bytes + 2048); };
+    if (paged)
+        return head_dim == 64 ? per(DecShape<64, true>::NW * DecShape<64, true>::WAVE_LDS)
+             : head_dim == 128 ? per(DecShape<128, true>::NW * DecShape<128, true>::WAVE_LDS)
+                               : per(DecShape<256, true>::NW * DecShape<256, true>::WAVE_LDS);
+    return head_dim == 64 ? per(DecShape<64, false>::NW * DecShape<64, false>::WAVE_LDS)
+         : head_dim == 128 ? per(DecShape<128, false>::NW * DecShape<128, false>::WAVE_LDS)
+                           : per(DecShape<256, false>::NW * DecShape<256, false>::WAVE_LDS);
+}
 
 int decode_max_splits() { return kMaxSplits; }
 
 int decode_max_split_tokens_paged() { return kMaxSplitTokens; }
+
+int decode_max_heads_per_workgroup() { return 8; }
 
 }  // namespace ta03

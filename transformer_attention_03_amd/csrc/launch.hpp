@@ -51,8 +51,10 @@ struct FwdParams {
 
 hipError_t launch_decode(const DecodeParams& p, int head_dim, int gc, bool paged, int batch,
                          hipStream_t st);
-int decode_tokens_per_block(int head_dim, bool paged);
-int decode_waves();
+int decode_tokens_per_block();
+int decode_waves(int head_dim, bool paged);
+int decode_max_heads_per_workgroup();
+int decode_workgroups_per_cu(int head_dim, bool paged);
 int decode_max_splits();
 int decode_max_split_tokens_paged();
 
