@@ -113,6 +113,22 @@ __device__ __forceinline__ void dma4(const void* gptr, const void* lds_base) {
 }
 template <int N>
 __device__ __forceinline__ void wait_vmem_at_most() { asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory"); }
+// Device-coherent variants (sc1: fetched past the XCD-private L2), for data written by
+// workgroups on other XCDs.
+__device__ __forceinline__ void dma16_coherent(const void* gptr, const void* lds_base) {
+    const uint32_t off = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)lds_base;
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off sc1"
+                 :
+                 : "s"(__builtin_amdgcn_readfirstlane(off)), "v"(gptr)
+                 : "memory", "m0");
+}
+__device__ __forceinline__ void dma4_coherent(const void* gptr, const void* lds_base) {
+    const uint32_t off = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)lds_base;
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, off sc1"
+                 :
+                 : "s"(__builtin_amdgcn_readfirstlane(off)), "v"(gptr)
+                 : "memory", "m0");
+}
 __device__ __forceinline__ void wait_lds_reads() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
 // Reductions across the four 16-lane rows (lanes congruent mod 16) with the gfx950 lane
@@ -169,18 +185,24 @@ __device__ __forceinline__ size_t row_index(const RowCtx& c, int t) {
 }
 
 // The same DMAs with a uniform 64-bit base in SGPRs and a 32-bit per-lane offset.
+__device__ __forceinline__ uint64_t uniform_ptr(const void* p) {
+    const uint64_t b = (uint64_t)(uintptr_t)p;
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)b);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(b >> 32));
+    return ((uint64_t)hi << 32) | lo;
+}
 __device__ __forceinline__ void dma16s(const void* sbase, uint32_t voff, const void* lds_base) {
     const uint32_t off = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)lds_base;
     asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
                  :
-                 : "s"(__builtin_amdgcn_readfirstlane(off)), "v"(voff), "s"(sbase)
+                 : "s"(__builtin_amdgcn_readfirstlane(off)), "v"(voff), "s"(uniform_ptr(sbase))
                  : "memory", "m0");
 }
 __device__ __forceinline__ void dma4s(const void* sbase, uint32_t voff, const void* lds_base) {
     const uint32_t off = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)lds_base;
     asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, %2"
                  :
-                 : "s"(__builtin_amdgcn_readfirstlane(off)), "v"(voff), "s"(sbase)
+                 : "s"(__builtin_amdgcn_readfirstlane(off)), "v"(voff), "s"(uniform_ptr(sbase))
                  : "memory", "m0");
 }
 
@@ -279,6 +301,14 @@ __device__ __forceinline__ _Float16 split_part(float x, bool odd) {
 }
 
 // One block of 16 tokens.  full: all 16 tokens are below t_end (no masking).
+// Splits per chunk of the final merge: outputs [GC][CS][D] plus m and l [GC][CS] in the rings.
+template <int D, int GC, bool PAGED>
+constexpr int merge_chunk() {
+    constexpr int floats = DecShape<D, PAGED>::NW * DecShape<D, PAGED>::WAVE_LDS / 4;
+    constexpr int cs = floats / (GC * (D + 2));
+    return cs > kMaxSplits ? kMaxSplits : cs;
+}
+
 template <int D, bool PAGED, bool CAP>
 __device__ __forceinline__ void process_block(const char* slot, int tb, int t_end, bool full,
                                               float cap_log2, float qbias,
@@ -291,8 +321,36 @@ __device__ __forceinline__ void process_block(const char* slot, int tb, int t_en
     const int g4 = lane >> 4;      // 16-lane row of the wave
     const bool odd = lane & 1;
 
-    // ---- S^T = K Qx^T --------------------------------------------------------------------
-    float4_t sacc = {0.f, 0.f, 0.f, 0.f};
+    // ---- V^T operands, read ahead of the softmax so the LDS latency overlaps it ----------
+    // f16: source lane j gives 4 halves of token row 4 g4 + j/4 at d = 16 dt + 4 (j & 3).
+    // int8: one transposing byte read feeds two d tiles: source lane j gives 8 bytes of
+    // token row 4 g4 + (j/2 & 3), d tile dt + j/8, half j & 1.
+    typedef short s4_t __attribute__((ext_vector_type(4)));
+    typedef int i2_t __attribute__((ext_vector_type(2)));
+    constexpr int NVR = PAGED ? S::DT / 2 : S::DT;
+    uint2 vraw[NVR];
+    {
+        const int j = lane & 15;
+#pragma unroll
+        for (int i = 0; i < NVR; ++i) {
+            if constexpr (PAGED) {
+                const int r = 4 * g4 + ((j >> 1) & 3);
+                const char* addr = vt + r * S::RB + 16 * ((2 * i + (j >> 3)) ^ vsw<S::RPL>(r)) + 8 * (j & 1);
+                const i2_t w = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+                    (__attribute__((address_space(3))) i2_t*)(uintptr_t)(const __attribute__((address_space(3))) char*)addr);
+                vraw[i] = __builtin_bit_cast(uint2, w);
+            } else {
+                const int r = 4 * g4 + (j >> 2);
+                const char* addr = vt + r * S::RB + 16 * ((2 * i + ((j & 3) >> 1)) ^ vsw<S::RPL>(r)) + 8 * (j & 1);
+                const s4_t w = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (__attribute__((address_space(3))) s4_t*)(uintptr_t)(const __attribute__((address_space(3))) char*)addr);
+                vraw[i] = __builtin_bit_cast(uint2, w);
+            }
+        }
+    }
+
+    // ---- S^T = K Qx^T (two accumulation chains) ---------------------------------------------
+    float4_t sacc2[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
     for (int kc = 0; kc < S::KC; ++kc) {
         half8_t a;
@@ -307,8 +365,9 @@ __device__ __forceinline__ void process_block(const char* slot, int tb, int t_en
             const int c = 4 * kc + g4;
             a = *reinterpret_cast<const half8_t*>(kt + r16 * S::RB + 16 * (c ^ ksw<S::RPL>(r16)));
         }
-        sacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, qx[kc], sacc, 0, 0, 0);
+        sacc2[kc & 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, qx[kc], sacc2[kc & 1], 0, 0, 0);
     }
+    const float4_t sacc = sacc2[0] + sacc2[1];
 
     // scores of tokens tb + 4 g4 + v for this lane's column (hi + lo pair summed)
     float4_t ks = {1.f, 1.f, 1.f, 1.f}, vs = {1.f, 1.f, 1.f, 1.f};
@@ -370,38 +429,18 @@ __device__ __forceinline__ void process_block(const char* slot, int tb, int t_en
                                        split_part(xv[2], odd), split_part(xv[3], odd)};
 
     // ---- O^T += V^T P^T --------------------------------------------------------------------
-    if constexpr (PAGED) {
-        // one transposing byte read feeds two d tiles: source lane j gives 8 bytes of token
-        // row 4 g4 + (j/2 & 3), d tile dt + j/8, half j & 1
-        const int j = lane & 15;
-        const int r = 4 * g4 + ((j >> 1) & 3);
-        const int hsel = j >> 3;
 #pragma unroll
-        for (int dt = 0; dt < S::DT; dt += 2) {
-            const char* addr = vt + r * S::RB + 16 * ((dt + hsel) ^ vsw<S::RPL>(r)) + 8 * (j & 1);
-            typedef int i2_t __attribute__((ext_vector_type(2)));
-            const i2_t w = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-                (__attribute__((address_space(3))) i2_t*)(uintptr_t)(const __attribute__((address_space(3))) char*)addr);
+    for (int i = 0; i < NVR; ++i) {
+        if constexpr (PAGED) {
             uint32_t e0, o0, e1, o1;
-            i8x4_biased((uint32_t)w.x, e0, o0);
-            i8x4_biased((uint32_t)w.y, e1, o1);
-            const half4_t a0 = __builtin_bit_cast(half4_t, uint2{e0, o0});
-            const half4_t a1 = __builtin_bit_cast(half4_t, uint2{e1, o1});
-            A.o[dt] = __builtin_amdgcn_mfma_f32_16x16x16f16(a0, pb, A.o[dt], 0, 0, 0);
-            A.o[dt + 1] = __builtin_amdgcn_mfma_f32_16x16x16f16(a1, pb, A.o[dt + 1], 0, 0, 0);
-        }
-    } else {
-        // source lane j gives 4 halves of token row 4 g4 + j/4 at d = 16 dt + 4 (j & 3)
-        const int j = lane & 15;
-        const int r = 4 * g4 + (j >> 2);
-        const int csel = (j & 3) >> 1;
-#pragma unroll
-        for (int dt = 0; dt < S::DT; ++dt) {
-            const char* addr = vt + r * S::RB + 16 * ((2 * dt + csel) ^ vsw<S::RPL>(r)) + 8 * (j & 1);
-            typedef short s4_t __attribute__((ext_vector_type(4)));
-            const s4_t w = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (__attribute__((address_space(3))) s4_t*)(uintptr_t)(const __attribute__((address_space(3))) char*)addr);
-            A.o[dt] = __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(half4_t, w), pb, A.o[dt], 0, 0, 0);
+            i8x4_biased(vraw[i].x, e0, o0);
+            i8x4_biased(vraw[i].y, e1, o1);
+            A.o[2 * i] = __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(half4_t, uint2{e0, o0}), pb,
+                                                              A.o[2 * i], 0, 0, 0);
+            A.o[2 * i + 1] = __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(half4_t, uint2{e1, o1}), pb,
+                                                                  A.o[2 * i + 1], 0, 0, 0);
+        } else {
+            A.o[i] = __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(half4_t, vraw[i]), pb, A.o[i], 0, 0, 0);
         }
     }
 }
@@ -418,6 +457,8 @@ __global__ void __launch_bounds__((DecShape<D, PAGED>::NT)) decode_split_kernel(
     __shared__ float lds_l[NW][GC];
     __shared__ int lds_pages[PAGED ? kMaxSplitTokens / 16 + 1 : 1];
     __shared__ int lds_last;
+    __shared__ half8_t lds_qx[S::KC][64];
+    __shared__ float lds_qs[S::KC][64];
     float(*lds_o)[GC][D] = reinterpret_cast<float(*)[GC][D]>(rings);                    // [NW][GC][D]
     static_assert(sizeof(float) * NW * GC * D <= NW * S::WAVE_LDS, "merge buffer fits in the rings");
 
@@ -484,36 +525,35 @@ __global__ void __launch_bounds__((DecShape<D, PAGED>::NT)) decode_split_kernel(
     const float cap_log2 = a.softcap * kLog2e;
     const int col = lane & 15;
     const int hq = col >> 1;
+    // Computed once per workgroup: wave w converts the d chunks kc = w, w + NW, ... and
+    // every wave reads all of them back from LDS.
     half8_t qx[S::KC];
     float qbias;
     {
-        float qf[S::KC][8];
+        constexpr int kOrder[8] = {0, 2, 1, 3, 4, 6, 5, 7};
         const float* qh = a.q + ((size_t)b * a.H + h0 + min(hq, GC - 1)) * D + 8 * (lane >> 4);
-#pragma unroll
-        for (int kc = 0; kc < S::KC; ++kc) {
+        for (int kc = w; kc < S::KC; kc += NW) {
             const float4_t x0 = *reinterpret_cast<const float4_t*>(qh + 32 * kc);
             const float4_t x1 = *reinterpret_cast<const float4_t*>(qh + 32 * kc + 4);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                qf[kc][e] = x0[e];
-                qf[kc][4 + e] = x1[e];
-            }
-        }
-        // settle the q loads here, so that inside the loop only the DMA counter is waited on
-#pragma unroll
-        for (int kc = 0; kc < S::KC; ++kc)
-#pragma unroll
-            for (int e = 0; e < 8; ++e) asm volatile("" ::"v"(qf[kc][e]));
-        constexpr int kOrder[8] = {0, 2, 1, 3, 4, 6, 5, 7};
-        float qsum = 0.f;
-#pragma unroll
-        for (int kc = 0; kc < S::KC; ++kc)
+            const float qf[8] = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+            half8_t h;
+            float qs = 0.f;
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                const float x = hq < GC ? qf[kc][PAGED ? kOrder[e] : e] * qmul : 0.f;
-                qx[kc][e] = split_part(x, col & 1);
-                qsum += (float)qx[kc][e];
+                const float x = hq < GC ? qf[PAGED ? kOrder[e] : e] * qmul : 0.f;
+                h[e] = split_part(x, col & 1);
+                qs += (float)h[e];
             }
+            lds_qx[kc][lane] = h;
+            lds_qs[kc][lane] = qs;
+        }
+        __syncthreads();
+        float qsum = 0.f;
+#pragma unroll
+        for (int kc = 0; kc < S::KC; ++kc) {
+            qx[kc] = lds_qx[kc][lane];
+            qsum += lds_qs[kc][lane];
+        }
         // int8 K: the bias term 1152 * sum_d q[d] of the head (hi + lo columns, all rows)
         qsum = rows_sum(qsum);
         qbias = 1152.f * (qsum + dpp_f<kDppXor1>(qsum));
@@ -613,11 +653,15 @@ __global__ void __launch_bounds__((DecShape<D, PAGED>::NT)) decode_split_kernel(
     __syncthreads();
     if (!lds_last) return;
 
-    // One pass over the split partials per (head, d) pair, entirely in registers: the
-    // partials of CH splits are fetched together (outputs, maxima and sums), folded into a
-    // running maximum M, weighted sum and normaliser, then the next CH splits.
-    constexpr int PER = (GC * D + NT - 1) / NT;     // (head, d) pairs per thread
-    constexpr int CH = PER <= 1 ? 32 : (PER <= 2 ? 16 : (PER <= 4 ? 8 : 4));
+    // The split partials (device-scope data) are pulled into LDS by DMA, CS splits at a
+    // time, and folded per (head, d) pair into a running maximum, weighted sum and
+    // normaliser.  Compact loops: this code runs once per (sequence, head chunk), on a
+    // compute unit that has not executed it before.
+    constexpr int CS = merge_chunk<D, GC, PAGED>();
+    float* lds_po = reinterpret_cast<float*>(rings);          // [GC][CS][D]
+    float* lds_pm = lds_po + GC * CS * D;                      // [GC][CS]
+    float* lds_pl = lds_pm + GC * CS;                          // [GC][CS]
+    constexpr int PER = (GC * D + NT - 1) / NT;                // (head, d) pairs per thread
     float M[PER], Lsum[PER], acc[PER];
 #pragma unroll
     for (int r = 0; r < PER; ++r) {
@@ -625,42 +669,48 @@ __global__ void __launch_bounds__((DecShape<D, PAGED>::NT)) decode_split_kernel(
         Lsum[r] = 0.f;
         acc[r] = 0.f;
     }
-    for (int s0 = 0; s0 < n_live; s0 += CH) {
-        float ms[PER][CH], ls[PER][CH], os[PER][CH];
+    for (int s0 = 0; s0 < n_live; s0 += CS) {
+        const int cs = min(CS, n_live - s0);
+        // outputs: head g's cs * D floats are contiguous in the workspace and in LDS
+        const int n16 = GC * cs * D / 4;                       // 16-byte pieces
+        for (int c0 = w * 64; c0 < n16; c0 += NT) {
+            const int c = c0 + lane;
+            const int g = c / (cs * D / 4), off = c % (cs * D / 4);
+            if (c < n16)
+                dma16_coherent(a.part_o + ((part_base + g) * a.n_split_max + s0) * D + 4 * off,
+                               lds_po + 4 * c0);
+        }
+        for (int c0 = w * 64; c0 < GC * cs; c0 += NT) {
+            const int c = c0 + lane;
+            const int g = c / cs, s = c % cs;
+            if (c < GC * cs) {
+                dma4_coherent(a.part_m + (part_base + g) * a.n_split_max + s0 + s, lds_pm + c0);
+                dma4_coherent(a.part_l + (part_base + g) * a.n_split_max + s0 + s, lds_pl + c0);
+            }
+        }
+        wait_vmem_at_most<0>();
+        __syncthreads();
+        // LDS now holds outputs at [g][s][d] with stride cs * D per head, and m, l at [g][s]
 #pragma unroll
         for (int r = 0; r < PER; ++r) {
             const int i = min(threadIdx.x + r * NT, GC * D - 1);
-            const size_t row = (part_base + i / D) * a.n_split_max;
-#pragma unroll
-            for (int u = 0; u < CH; ++u) {
-                const bool in = s0 + u < n_live;
-                const size_t slot = row + min(s0 + u, n_live - 1);
-                ms[r][u] = load_agent(a.part_m + slot);
-                ls[r][u] = load_agent(a.part_l + slot);
-                os[r][u] = load_agent(a.part_o + slot * D + (i % D));
-                if (!in) {
-                    ms[r][u] = -INFINITY;
-                    ls[r][u] = 0.f;
-                    os[r][u] = 0.f;
-                }
-            }
-        }
-#pragma unroll
-        for (int r = 0; r < PER; ++r) {
+            const int g = i / D, d = i % D;
             float mc = M[r];
-#pragma unroll
-            for (int u = 0; u < CH; ++u) mc = fmaxf(mc, ms[r][u]);
+            for (int s = 0; s < cs; ++s) mc = fmaxf(mc, lds_pm[g * cs + s]);
             const float f = (M[r] == -INFINITY) ? 0.f : fast_exp2(M[r] - mc);
-            acc[r] *= f;
-            Lsum[r] *= f;
-#pragma unroll
-            for (int u = 0; u < CH; ++u) {
-                const float wgt = (ms[r][u] == -INFINITY) ? 0.f : fast_exp2(ms[r][u] - mc);
-                acc[r] = __builtin_fmaf(wgt, os[r][u], acc[r]);
-                Lsum[r] = __builtin_fmaf(wgt, ls[r][u], Lsum[r]);
+            float o = acc[r] * f, l = Lsum[r] * f;
+#pragma unroll 4
+            for (int s = 0; s < cs; ++s) {
+                const float ms = lds_pm[g * cs + s];
+                const float wgt = (ms == -INFINITY) ? 0.f : fast_exp2(ms - mc);
+                o = __builtin_fmaf(wgt, lds_po[(g * cs + s) * D + d], o);
+                l = __builtin_fmaf(wgt, lds_pl[g * cs + s], l);
             }
             M[r] = mc;
+            acc[r] = o;
+            Lsum[r] = l;
         }
+        __syncthreads();
     }
 #pragma unroll
     for (int r = 0; r < PER; ++r) {
@@ -718,8 +768,8 @@ int decode_waves(int head_dim, bool paged) {
 }
 
 int decode_workgroups_per_cu(int head_dim, bool paged) {
-    // 160 KB of LDS per compute unit; besides the rings a workgroup holds about 2 KB more
-    auto per = [](int ring_bytes) { return (160 * 1024) / (ring_bytes + 2048); };
+    // 160 KB of LDS per compute unit; besides the rings a workgroup holds up to 6 KB more
+    auto per = [](int ring_bytes) { return (160 * 1024) / (ring_bytes + 6144); };
     if (paged)
         return head_dim == 64 ? per(DecShape<64, true>::NW * DecShape<64, true>::WAVE_LDS)
              : head_dim == 128 ? per(DecShape<128, true>::NW * DecShape<128, true>::WAVE_LDS)
