@@ -22,6 +22,8 @@ LIB = os.path.join(PKG, "libattn.so")
 BUILD_DIR = os.path.join(PKG, "_build")
 
 SOURCES = ["api.cpp", "decode.hip", "fwd.hip"]
+# per-source extra hipcc flags (none at present)
+KERNEL_FLAGS = {}
 ARCH = os.environ.get("TA03_OFFLOAD_ARCH", "gfx950")
 
 
@@ -44,7 +46,7 @@ def compile_flags(extra=()):
 
 def _compile(src: str, extra=()) -> str:
     obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc(), *compile_flags(extra), "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [hipcc(), *compile_flags(extra), *KERNEL_FLAGS.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("hipcc failed for %s:\n%s\n%s" % (src, " ".join(cmd), r.stderr[-8000:]))

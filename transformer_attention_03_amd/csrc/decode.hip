@@ -98,14 +98,14 @@ __device__ __forceinline__ int clamp_page(int p, int num_pages) {
 // LDS reads with full vector-memory waits; completion is tracked per wave with counted
 // vmcnt waits.  m0 is written here and is used by nothing else in this kernel.
 __device__ __forceinline__ void dma16(const void* gptr, const void* lds_base) {
-    const uint32_t off = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)lds_base;
+    const uint32_t off = lds_offset(lds_base);
     asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
                  :
                  : "s"(__builtin_amdgcn_readfirstlane(off)), "v"(gptr)
                  : "memory", "m0");
 }
 __device__ __forceinline__ void dma4(const void* gptr, const void* lds_base) {
-    const uint32_t off = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)lds_base;
+    const uint32_t off = lds_offset(lds_base);
     asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, off"
                  :
                  : "s"(__builtin_amdgcn_readfirstlane(off)), "v"(gptr)
@@ -116,36 +116,20 @@ __device__ __forceinline__ void wait_vmem_at_most() { asm volatile("s_waitcnt vm
 // Device-coherent variants (sc1: fetched past the XCD-private L2), for data written by
 // workgroups on other XCDs.
 __device__ __forceinline__ void dma16_coherent(const void* gptr, const void* lds_base) {
-    const uint32_t off = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)lds_base;
+    const uint32_t off = lds_offset(lds_base);
     asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off sc1"
                  :
                  : "s"(__builtin_amdgcn_readfirstlane(off)), "v"(gptr)
                  : "memory", "m0");
 }
 __device__ __forceinline__ void dma4_coherent(const void* gptr, const void* lds_base) {
-    const uint32_t off = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)lds_base;
+    const uint32_t off = lds_offset(lds_base);
     asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, off sc1"
                  :
                  : "s"(__builtin_amdgcn_readfirstlane(off)), "v"(gptr)
                  : "memory", "m0");
 }
 __device__ __forceinline__ void wait_lds_reads() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
-
-// Reductions across the four 16-lane rows (lanes congruent mod 16) with the gfx950 lane
-// swaps: after permlane16_swap(x, x) (resp. permlane32_swap) a lane holds its own value
-// and that of lane ^ 16 (resp. ^ 32), in an order that depends on the lane.
-__device__ __forceinline__ float rows_max(float x) {
-    auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
-    auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
-}
-__device__ __forceinline__ float rows_sum(float x) {
-    auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
-    auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
-}
 
 // 2^e for integer e (exact); 0 below the normal range.
 __device__ __forceinline__ float pow2i(int e) {
@@ -192,14 +176,14 @@ __device__ __forceinline__ uint64_t uniform_ptr(const void* p) {
     return ((uint64_t)hi << 32) | lo;
 }
 __device__ __forceinline__ void dma16s(const void* sbase, uint32_t voff, const void* lds_base) {
-    const uint32_t off = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)lds_base;
+    const uint32_t off = lds_offset(lds_base);
     asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
                  :
                  : "s"(__builtin_amdgcn_readfirstlane(off)), "v"(voff), "s"(uniform_ptr(sbase))
                  : "memory", "m0");
 }
 __device__ __forceinline__ void dma4s(const void* sbase, uint32_t voff, const void* lds_base) {
-    const uint32_t off = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)lds_base;
+    const uint32_t off = lds_offset(lds_base);
     asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, %2"
                  :
                  : "s"(__builtin_amdgcn_readfirstlane(off)), "v"(voff), "s"(uniform_ptr(sbase))
@@ -337,13 +321,13 @@ __device__ __forceinline__ void process_block(const char* slot, int tb, int t_en
                 const int r = 4 * g4 + ((j >> 1) & 3);
                 const char* addr = vt + r * S::RB + 16 * ((2 * i + (j >> 3)) ^ vsw<S::RPL>(r)) + 8 * (j & 1);
                 const i2_t w = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-                    (__attribute__((address_space(3))) i2_t*)(uintptr_t)(const __attribute__((address_space(3))) char*)addr);
+                    (__attribute__((address_space(3))) i2_t*)lds_offset(addr));
                 vraw[i] = __builtin_bit_cast(uint2, w);
             } else {
                 const int r = 4 * g4 + (j >> 2);
                 const char* addr = vt + r * S::RB + 16 * ((2 * i + ((j & 3) >> 1)) ^ vsw<S::RPL>(r)) + 8 * (j & 1);
                 const s4_t w = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (__attribute__((address_space(3))) s4_t*)(uintptr_t)(const __attribute__((address_space(3))) char*)addr);
+                    (__attribute__((address_space(3))) s4_t*)lds_offset(addr));
                 vraw[i] = __builtin_bit_cast(uint2, w);
             }
         }

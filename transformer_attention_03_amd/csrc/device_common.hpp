@@ -74,7 +74,27 @@ __device__ __forceinline__ float strided_sum(float x) {
     return x;
 }
 
+// Reductions across the four 16-lane rows (lanes congruent mod 16) with the gfx950 lane
+// swaps: after permlane16_swap(x, x) (resp. permlane32_swap) a lane holds its own value
+// and that of lane ^ 16 (resp. ^ 32), in an order that depends on the lane.
+__device__ __forceinline__ float rows_max(float x) {
+    auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float rows_sum(float x) {
+    auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
 // ---- memory ---------------------------------------------------------------------------------
+
+// Byte offset in LDS of a generic pointer into shared memory: the LDS aperture is 4 GB
+// aligned, so the low 32 bits of the generic address are the offset (no null check).
+__device__ __forceinline__ uint32_t lds_offset(const void* p) { return (uint32_t)(uintptr_t)p; }
 
 // Device-scope (all XCDs) relaxed store / load: written through, resp. fetched past, the
 // XCD-private L2, so another workgroup on any XCD observes them without cache-wide fences.

@@ -112,7 +112,11 @@ struct F16Shape {
 template <int D>
 __device__ __forceinline__ int kswz(int r, int c) { return c ^ (D >= 128 ? (r & 15) : ((r >> 1) & 7)); }
 template <int D>
-__device__ __forceinline__ int vswz(int r, int c) { return c ^ (((r & 7) * 2) & (D / 8 - 1)); }
+__device__ __forceinline__ int vswz(int r, int c) {
+    // pairs of chunks stay adjacent (the transposing reads take 32 bytes of a row); with
+    // 128-byte rows two rows share a 256-byte bank line, so the row's low bit is left out
+    return c ^ (D >= 128 ? 2 * (r & 7) : 2 * ((r >> 1) & 3));
+}
 
 template <int N>
 __device__ __forceinline__ void wait_vmem_at_most() { asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory"); }
@@ -123,7 +127,7 @@ __device__ __forceinline__ void wait_vmem_at_most() { asm volatile("s_waitcnt vm
 // read); completion is tracked explicitly with wait_vmem_at_most + a barrier.  m0 is
 // written here and is used by nothing else in these kernels.
 __device__ __forceinline__ void dma16(const void* gptr, const void* lds_base) {
-    const uint32_t off = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)lds_base;
+    const uint32_t off = lds_offset(lds_base);
     asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
                  :
                  : "s"(__builtin_amdgcn_readfirstlane(off)), "v"(gptr)
@@ -187,11 +191,11 @@ typedef short short4_t __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ half4_t lds_read_tr16(const char* p) {
     const short4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (__attribute__((address_space(3))) short4_t*)(p));
+        (__attribute__((address_space(3))) short4_t*)lds_offset(p));
     return __builtin_bit_cast(half4_t, v);
 }
 
-template <int D, int QB, int NW, int NS>
+template <int D, int QB, int NW, int NS, bool CAP>
 __global__ void __launch_bounds__(64 * NW) fwd_f16_kernel(FwdParams a) {
     using S = F16Shape<D, QB, NW, NS>;
     __shared__ __attribute__((aligned(1024))) char k_lds[NS][S::TILE];
@@ -262,8 +266,7 @@ __global__ void __launch_bounds__(64 * NW) fwd_f16_kernel(FwdParams a) {
     }
     const half8_t ones = half8_t{1, 1, 1, 1, 1, 1, 1, 1};
 
-    const bool capped = a.softcap > 0.f;
-    const float sc2 = capped ? 1.f : a.scale_log2;     // raw score -> log2 units
+    const float sc2 = CAP ? 1.f : a.scale_log2;        // raw score -> log2 units
     // softcap in log2 units: t = C1 - C2 / (2^(s * K1) + 1), C1 = c log2 e, C2 = 2 c log2 e,
     // K1 = 2 scale log2 e / c  (c tanh(scale s / c) = c - 2c / (exp(2 scale s / c) + 1))
     const float K1 = 2.f * a.scale * kLog2e * a.inv_softcap;
@@ -333,6 +336,17 @@ __global__ void __launch_bounds__(64 * NW) fwd_f16_kernel(FwdParams a) {
                     st[kb][qb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf[c & 1][kb], qf[qb][c], st[kb][qb], 0, 0, 0);
         }
 
+        // V^T fragments of the tile's first 32 keys, read ahead of the softmax so that their
+        // LDS latency overlaps it
+        constexpr int NPF = D >= 256 ? S::NDB / 2 : S::NDB;   // register budget
+        half8_t vf0[NPF];
+#pragma unroll
+        for (int db = 0; db < NPF; ++db) {
+            const half4_t lo = lds_read_tr16(vl + voff[db]);
+            const half4_t hi = lds_read_tr16(vl + voff[db] + 16 * 2 * D);
+            vf0[db] = half8_t{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        }
+
         // ---- online softmax in the S^T layout: lane = query (ln), keys 16kb + 4lg + i ----
         // Uncapped scores stay raw (scale > 0 preserves the max); the scale is folded into
         // the exponent: p = 2^(s * scale * log2 e - m).  Capped scores are turned into log2
@@ -340,7 +354,7 @@ __global__ void __launch_bounds__(64 * NW) fwd_f16_kernel(FwdParams a) {
         half8_t pf[S::QB][S::BN / 32];
 #pragma unroll
         for (int qb = 0; qb < S::QB; ++qb) {
-            if (capped) {
+            if constexpr (CAP) {
 #pragma unroll
                 for (int kb = 0; kb < S::NKB; ++kb)
 #pragma unroll
@@ -363,8 +377,7 @@ __global__ void __launch_bounds__(64 * NW) fwd_f16_kernel(FwdParams a) {
             for (int kb = 0; kb < S::NKB; ++kb)
 #pragma unroll
                 for (int i = (kb == 0 ? 1 : 0); i < 4; ++i) mx = fmaxf(mx, st[kb][qb][i]);
-            mx = fmaxf(mx, shfl_xor_f(mx, 16));
-            mx = fmaxf(mx, shfl_xor_f(mx, 32));
+            mx = rows_max(mx);
             const float mxl = mx * sc2;        // in log2 units
             if (__builtin_amdgcn_ballot_w64(mxl > m_run[qb] + kSlack) != 0) {
                 const float mnew = fmaxf(m_run[qb], mxl);
@@ -393,12 +406,17 @@ __global__ void __launch_bounds__(64 * NW) fwd_f16_kernel(FwdParams a) {
 
         // ---- O^T += V^T P^T ---------------------------------------------------------------
 #pragma unroll
-        for (int db = 0; db < S::NDB; ++db) {
+        for (int c = 0; c < S::BN / 32; ++c) {
 #pragma unroll
-            for (int c = 0; c < S::BN / 32; ++c) {
-                const half4_t lo = lds_read_tr16(vl + voff[db] + (32 * c) * 2 * D);
-                const half4_t hi = lds_read_tr16(vl + voff[db] + (32 * c + 16) * 2 * D);
-                const half8_t vf = half8_t{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+            for (int db = 0; db < S::NDB; ++db) {
+                half8_t vf;
+                if (c == 0 && db < NPF) {
+                    vf = vf0[db];
+                } else {
+                    const half4_t lo = lds_read_tr16(vl + voff[db] + (32 * c) * 2 * D);
+                    const half4_t hi = lds_read_tr16(vl + voff[db] + (32 * c + 16) * 2 * D);
+                    vf = half8_t{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+                }
 #pragma unroll
                 for (int qb = 0; qb < S::QB; ++qb)
                     acc_o[db][qb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf, pf[qb][c], acc_o[db][qb], 0, 0, 0);
@@ -588,7 +606,10 @@ hipError_t launch_d(const FwdParams& p, int dtype, hipStream_t st) {
     const dim3 grid(p.n_qblocks * p.H);
     if (dtype == 1) {
         constexpr int QB = F16Cfg<D>::QB, NW = F16Cfg<D>::NW, NS = F16Cfg<D>::NS;
-        hipLaunchKernelGGL((fwd_f16_kernel<D, QB, NW, NS>), grid, dim3(64 * NW), 0, st, p);
+        if (p.softcap > 0.f)
+            hipLaunchKernelGGL((fwd_f16_kernel<D, QB, NW, NS, true>), grid, dim3(64 * NW), 0, st, p);
+        else
+            hipLaunchKernelGGL((fwd_f16_kernel<D, QB, NW, NS, false>), grid, dim3(64 * NW), 0, st, p);
     } else {
         hipLaunchKernelGGL(fwd_f32_kernel<D>, grid, dim3(256), 0, st, p);
     }
