@@ -99,8 +99,9 @@ DecodePlan plan_decode(int batch, int num_heads, int num_kv_heads, int head_dim,
         const long rows = (long)eff_len * batch * num_kv_heads * p.nch;
         const long resident = 256L * ta03::decode_workgroups_per_cu(head_dim, paged);
         const long want = (rows + 3 * resident - 1) / (3 * resident);
-        t = (int)(((want + unit - 1) / unit) * unit);
-        if (t < 2 * unit) t = 2 * unit;
+        // short splits: two rounds of blocks per wave; long ones in steps of four rounds
+        const long step = want <= 2 * unit ? 2 * unit : 4 * unit;
+        t = (int)(((want + step - 1) / step) * step);
     }
     // the paged kernel stages the page indices of one split in LDS
     if (paged && t > ta03::decode_max_split_tokens_paged()) t = ta03::decode_max_split_tokens_paged();
