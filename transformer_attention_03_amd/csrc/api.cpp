@@ -74,8 +74,9 @@ constexpr long kMaxElems = 1L << 40;
 struct DecodePlan {
     int gc;             // query heads per workgroup
     int nch;            // head chunks per KV head
-    int split_tokens;   // logical tokens per workgroup
-    int n_split;        // grid.x
+    int split_tokens;   // contiguous: logical tokens per workgroup
+    int n_split;        // split partials per (sequence, head): workspace row stride
+    int n_wg;           // paged: workgroups per head chunk, balanced over the batch
 };
 
 int heads_per_wg(int group) {
@@ -90,27 +91,44 @@ DecodePlan plan_decode(int batch, int num_heads, int num_kv_heads, int head_dim,
     const int group = num_heads / num_kv_heads;
     p.gc = heads_per_wg(group);
     p.nch = group / p.gc;
+    const int unit = ta03::decode_waves(head_dim, paged) * ta03::decode_tokens_per_block();
+    const long resident = 256L * ta03::decode_workgroups_per_cu(head_dim, paged);
+    const long chunks = (long)num_kv_heads * p.nch;
+    if (paged) {
+        // Two rounds of resident workgroups, shared out over the batch by length inside the
+        // kernel; every sequence needs at least ceil(len / max split) of them.  An override
+        // of the split length asks for about batch * eff_len / override workgroups instead.
+        const int max_split = ta03::decode_max_split_tokens_paged();
+        const long lbmax = (eff_len + max_split - 1) / max_split;
+        long target = (2 * resident + chunks - 1) / chunks;
+        if (g_split_override > 0) target = ((long)batch * eff_len + g_split_override - 1) / g_split_override;
+        long n_wg = target > (long)batch * lbmax ? target : (long)batch * lbmax;
+        if (n_wg > 65535) n_wg = 65535;
+        long cap = lbmax + target;
+        if (cap > n_wg) cap = n_wg;
+        p.n_wg = (int)n_wg;
+        p.n_split = (int)cap;
+        p.split_tokens = unit;
+        return p;
+    }
     // Whole rounds of 16-token blocks per wave, at least two; aim for about three waves of
     // workgroups over the resident capacity (256 CUs), which keeps the tail of ragged paged
     // lengths short while the per-workgroup merge stays a small share.
-    const int unit = ta03::decode_waves(head_dim, paged) * ta03::decode_tokens_per_block();
     int t = g_split_override;
     if (t <= 0) {
         const long rows = (long)eff_len * batch * num_kv_heads * p.nch;
-        const long resident = 256L * ta03::decode_workgroups_per_cu(head_dim, paged);
         const long want = (rows + 3 * resident - 1) / (3 * resident);
         // short splits: two rounds of blocks per wave; long ones in steps of four rounds
         const long step = want <= 2 * unit ? 2 * unit : 4 * unit;
         t = (int)(((want + step - 1) / step) * step);
     }
-    // the paged kernel stages the page indices of one split in LDS
-    if (paged && t > ta03::decode_max_split_tokens_paged()) t = ta03::decode_max_split_tokens_paged();
     // the merge holds at most decode_max_splits() partials per (sequence, head)
     const int cap = ta03::decode_max_splits();
     if ((eff_len + t - 1) / t > cap) t = (((eff_len + cap - 1) / cap) + 15) / 16 * 16;
     p.split_tokens = t;
     p.n_split = (eff_len + t - 1) / t;
     if (p.n_split < 1) p.n_split = 1;
+    p.n_wg = p.n_split;
     return p;
 }
 
@@ -317,8 +335,15 @@ int attn_decode_paged_q8(const float* q, const int8_t* k_pages, const int8_t* v_
     if (workspace_bytes < wl.total)
         return fail(ATTN_ERR_WORKSPACE, "attn_decode_paged_q8: workspace of %zu bytes is smaller than the %zu required",
                     workspace_bytes, wl.total);
-    if (batch > 65535 || (long)num_kv_heads * plan.nch > 65535)
+    if ((long)num_kv_heads * plan.nch > 65535)
         return fail(ATTN_ERR_INVALID_ARG, "attn_decode_paged_q8: grid too large");
+    {
+        const long per_seq = (eff + ta03::decode_max_split_tokens_paged() - 1) / ta03::decode_max_split_tokens_paged();
+        if ((long)plan.n_wg < (long)batch * per_seq)
+            return fail(ATTN_ERR_UNSUPPORTED,
+                        "attn_decode_paged_q8: batch * ceil(max length / %d) must be <= 65535",
+                        ta03::decode_max_split_tokens_paged());
+    }
     ta03::DecodeParams d{};
     d.q = q; d.k = k_pages; d.v = v_pages;
     d.k_scales = k_scales; d.v_scales = v_scales;
@@ -333,6 +358,8 @@ int attn_decode_paged_q8(const float* q, const int8_t* k_pages, const int8_t* v_
     fill_scalars(d, sliding_window, attn_softcap, scale);
     d.split_tokens = plan.split_tokens;
     d.n_split_max = plan.n_split;
+    d.batch = batch;
+    d.n_wg = plan.n_wg;
     return launch_status(ta03::launch_decode(d, head_dim, plan.gc, true, batch,
                                              reinterpret_cast<hipStream_t>(stream)),
                          "attn_decode_paged_q8");

@@ -55,11 +55,12 @@ struct DecShape {
     static constexpr int TILE = kTB * RB;               // bytes of K (or of V) per block
     static constexpr int SCB = PAGED ? 512 : 0;         // K and V scales of a block
     static constexpr int SLOT = 2 * TILE + SCB;
-    // f16: eight waves with two slots each where that fits, else four; int8: four waves (two
-    // workgroups share a compute unit).  Then as many ring slots per wave (up to four) as
-    // the budget allows.
-    static constexpr int NW = (!PAGED && 8 * 2 * SLOT <= kLdsBudget) ? 8 : 4;
-    static constexpr int RING = kLdsBudget / (NW * SLOT) >= 4 ? 4 : kLdsBudget / (NW * SLOT);
+    // Eight waves with at least two slots each where that fits, else four waves; f16: as
+    // many slots per wave (up to four) as the budget allows; int8: two slots, so that two
+    // workgroups (sixteen waves) share a compute unit.
+    static constexpr int NW = (8 * 2 * SLOT <= kLdsBudget) ? 8 : 4;
+    static constexpr int RING_FIT = kLdsBudget / (NW * SLOT) >= 4 ? 4 : kLdsBudget / (NW * SLOT);
+    static constexpr int RING = PAGED && NW == 8 ? 2 : RING_FIT;
     static constexpr int NT = 64 * NW;
     static constexpr int WAVE_LDS = RING * SLOT;
     static constexpr int TD = TILE / 1024;              // 16-byte DMAs per lane per tile
@@ -448,30 +449,74 @@ __global__ void __launch_bounds__((DecShape<D, PAGED>::NT)) decode_split_kernel(
 
     const int lane = threadIdx.x & 63;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int split = blockIdx.x;
     const int G = a.H / a.Hkv;
     const int nch = G / GC;
     const int kvh = blockIdx.y / nch;
     const int h0 = kvh * G + (blockIdx.y % nch) * GC;
-    const int b = blockIdx.z;
 
     // ---- key range of this sequence, and of this split --------------------------------
-    int L = a.kv_len;
+    int b, split, n_live, t_begin, t_end, L;
     if constexpr (PAGED) {
+        // Balanced splits over the whole batch: workgroup x of this head chunk takes split s
+        // of sequence b, where sequence i gets lb_i = ceil(len_i / kMaxSplitTokens) splits
+        // plus its share, by length, of the remaining workgroups (at most one block round per
+        // wave less than a split).  Every workgroup derives the same assignment from kv_lens.
+        const int max_len = a.max_pages * 16;
+        auto eff_of = [&](int li) {
+            const bool valid = li >= 1 && li <= max_len;
+            return valid ? ((a.window > 0 && li > a.window) ? a.window : li) : 0;
+        };
+        long tot = 0;
+        int lb_sum = 0;
+        for (int i = 0; i < a.batch; ++i) {
+            const int e = eff_of(a.kv_lens[i]);
+            tot += e;
+            lb_sum += e > 0 ? (e + kMaxSplitTokens - 1) / kMaxSplitTokens : 1;
+        }
+        const int extra = max(0, (int)gridDim.x - lb_sum);
+        const int p = blockIdx.x;
+        int cum = 0, nb_b = 0;
+        b = -1;
+        for (int i = 0; i < a.batch; ++i) {
+            const int e = eff_of(a.kv_lens[i]);
+            const int lb = e > 0 ? (e + kMaxSplitTokens - 1) / kMaxSplitTokens : 1;
+            int n = lb + (tot > 0 ? (int)((long)extra * e / tot) : 0);
+            n = min(n, max(lb, (e + NW * kTB - 1) / (NW * kTB)));
+            n = min(n, a.n_split_max);
+            if (p < cum + n) {
+                b = i;
+                nb_b = n;
+                break;
+            }
+            cum += n;
+        }
+        if (b < 0) return;                        // more workgroups than splits
+        split = p - cum;
         L = a.kv_lens[b];
-        if (L < 1 || L > a.max_pages * 16) {
+        if (L < 1 || L > max_len) {
             // out of contract: the row becomes NaN; nothing else is read
             if (split == 0)
                 for (int i = threadIdx.x; i < GC * D; i += NT)
                     a.o[((size_t)b * a.H + h0 + i / D) * D + (i % D)] = __builtin_nanf("");
             return;
         }
+        const int k_lo = (a.window > 0 && L > a.window) ? L - a.window : 0;
+        const int eff = L - k_lo;
+        const int tsplit = (((eff + nb_b - 1) / nb_b) + 15) & ~15;   // <= kMaxSplitTokens
+        n_live = (eff + tsplit - 1) / tsplit;
+        if (split >= n_live) return;
+        t_begin = k_lo + split * tsplit;
+        t_end = min(L, t_begin + tsplit);
+    } else {
+        split = blockIdx.x;
+        b = blockIdx.z;
+        L = a.kv_len;
+        const int k_lo = (a.window > 0 && L > a.window) ? L - a.window : 0;
+        n_live = (L - k_lo + a.split_tokens - 1) / a.split_tokens;
+        if (split >= n_live) return;
+        t_begin = k_lo + split * a.split_tokens;
+        t_end = min(L, t_begin + a.split_tokens);
     }
-    const int k_lo = (a.window > 0 && L > a.window) ? L - a.window : 0;
-    const int n_live = (L - k_lo + a.split_tokens - 1) / a.split_tokens;
-    if (split >= n_live) return;
-    const int t_begin = k_lo + split * a.split_tokens;
-    const int t_end = min(L, t_begin + a.split_tokens);
 
     RowCtx c;
     c.kbase = reinterpret_cast<const char*>(a.k);
@@ -727,7 +772,8 @@ hipError_t launch_decode_d(const DecodeParams& p, int gc, dim3 grid, hipStream_t
 hipError_t launch_decode(const DecodeParams& p, int head_dim, int gc, bool paged, int batch,
                          hipStream_t st) {
     const int nch = (p.H / p.Hkv) / gc;
-    dim3 grid(p.n_split_max, p.Hkv * nch, batch);
+    // paged: n_wg balanced workgroups per head chunk across the batch; contiguous: splits
+    dim3 grid(paged ? p.n_wg : p.n_split_max, p.Hkv * nch, paged ? 1 : batch);
     if (paged) {
         switch (head_dim) {
             case 64: return launch_decode_d<64, true>(p, gc, grid, st);

@@ -29,8 +29,10 @@ struct DecodeParams {
     int window;
     float scale, scale_log2;   // scale and scale * log2(e)
     float softcap, inv_softcap;
-    int split_tokens;          // logical tokens per workgroup
-    int n_split_max;           // grid.x
+    int split_tokens;          // contiguous: logical tokens per workgroup
+    int n_split_max;           // split partials per (sequence, head): workspace row stride
+    int batch;                 // paged: sequences
+    int n_wg;                  // paged: workgroups per head chunk (grid.x)
 };
 
 struct FwdParams {
