@@ -452,7 +452,7 @@ template <int D>
 struct F32Shape {
     static constexpr int NW = 4;
     static constexpr int BM = NW * 16;            // one 16-row query block per wave
-    static constexpr int BN = 32;
+    static constexpr int BN = D <= 128 ? 64 : 32; // keys per tile (staging registers bound D 256)
     static constexpr int LD = D + 1;              // LDS row stride (floats)
     static constexpr int CH = BN * D / 4 / 256;   // float4 chunks per thread per tile (K or V)
     static constexpr int NKB = BN / 16;
@@ -529,16 +529,17 @@ __global__ void __launch_bounds__(256) fwd_f32_kernel(FwdParams a) {
         const int ks = kt * S::BN;
         const bool masked = tile_needs_mask(a, tr, ks, S::BN);
 
+        // NKB independent accumulation chains, interleaved
         float4_t st[S::NKB];
 #pragma unroll
-        for (int kb = 0; kb < S::NKB; ++kb) {
-            st[kb] = float4_t{0.f, 0.f, 0.f, 0.f};
+        for (int kb = 0; kb < S::NKB; ++kb) st[kb] = float4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int c = 0; c < S::DC; ++c) {
+        for (int c = 0; c < S::DC; ++c)
+#pragma unroll
+            for (int kb = 0; kb < S::NKB; ++kb) {
                 const float kf = k_lds[(16 * kb + ln) * S::LD + 4 * c + lg];
                 st[kb] = __builtin_amdgcn_mfma_f32_16x16x4f32(kf, qf[c], st[kb], 0, 0, 0);
             }
-        }
         float mx = -INFINITY;
 #pragma unroll
         for (int kb = 0; kb < S::NKB; ++kb)
@@ -567,13 +568,14 @@ __global__ void __launch_bounds__(256) fwd_f32_kernel(FwdParams a) {
                 st[kb][i] = p;
                 l_part += p;
             }
-        // O^T += V^T P^T, four keys {16kb + 4g + i : g} per product
+        // O^T += V^T P^T, four keys {16kb + 4g + i : g} per product; the NDB output blocks
+        // are independent chains, interleaved
 #pragma unroll
-        for (int db = 0; db < S::NDB; ++db)
+        for (int kb = 0; kb < S::NKB; ++kb)
 #pragma unroll
-            for (int kb = 0; kb < S::NKB; ++kb)
+            for (int i = 0; i < 4; ++i)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
+                for (int db = 0; db < S::NDB; ++db) {
                     const float vf = v_lds[(16 * kb + 4 * lg + i) * S::LD + 16 * db + ln];
                     acc_o[db] = __builtin_amdgcn_mfma_f32_16x16x4f32(vf, st[kb][i], acc_o[db], 0, 0, 0);
                 }
