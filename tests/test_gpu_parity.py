@@ -226,6 +226,24 @@ def test_paged_q8_relative_accuracy(dev, lens, H, Hkv, D, vf):
     assert maxabs(got, want) < 5e-5 * np.abs(want).max()
 
 
+@pytest.mark.parametrize("lens,H,Hkv,D", [
+    ([33, 4000, 1, 700, 16], 32, 2, 64),               # sixteen query heads per KV head
+    ([1, 32768], 8, 2, 128),                            # one token next to a 32K sequence
+    ([(7 * i) % 200 + 1 for i in range(40)], 8, 4, 128),  # forty short sequences
+])
+def test_paged_q8_batch_balance(dev, lens, H, Hkv, D):
+    """The paged kernel shares its workgroups out over the batch by length: skewed and wide
+    batches must still cover every token of every sequence exactly once."""
+    say("paged balance lens=%s H=%d Hkv=%d D=%d" % (lens[:6], H, Hkv, D))
+    mp = max((max(lens) + 15) // 16, 4)
+    d = synth.paged_inputs(synth.seed_of(5) + 77 + len(lens), len(lens), H, Hkv, D, lens, n_poison=5,
+                           max_pages=mp)
+    got = run_paged(dev, d)
+    want = paged_oracle(d)
+    assert np.all(np.isfinite(got))
+    assert maxabs(got, want) < 5e-5 * max(1.0, np.abs(want).max())
+
+
 @pytest.fixture(scope="module")
 def c5_inputs():
     """The batch-8, 32/8-head, head_dim 128 int8 paged workload with kv_len ~ U[16384, 32768]."""
