@@ -11,7 +11,8 @@
 // A workgroup owns GC <= 8 query heads that share one KV head (the K/V rows are read once
 // for all of them) and a contiguous logical token range.  Each of its NW waves streams
 // blocks of 16 tokens through a private ring of RING LDS slots filled by global->LDS DMA
-// (RING-1 blocks in flight, no staging registers, no barrier between waves).
+// (every slot is requested at the start and refilled as soon as its block has been
+// processed; no staging registers, no barrier between waves).
 //
 // Both products run as f16 MFMAs with f32 accumulation while keeping f32 accuracy: every
 // f32 operand x (the scaled query, and the softmax weight p) is split as
@@ -543,7 +544,7 @@ __global__ void __launch_bounds__((DecShape<D, PAGED>::NT)) decode_split_kernel(
     const int nb = first < t_end ? (t_end - first + STRIDE - 1) / STRIDE : 0;
     const DmaLane<D, PAGED> dl = dma_lane<D, PAGED>(lane, (uint32_t)((PAGED ? a.Hkv : 1) * S::RB), a.Hkv);
 #pragma unroll
-    for (int k = 0; k < S::RING - 1; ++k)
+    for (int k = 0; k < S::RING; ++k)
         if (k < nb) dma_block<D, PAGED>(ring + k * S::SLOT, c, dl, first + k * STRIDE, t_end, lane);
 
     // ---- Qx: B operand of the QK product.  Column n = lane % 16 holds part n & 1 of head
@@ -597,12 +598,6 @@ __global__ void __launch_bounds__((DecShape<D, PAGED>::NT)) decode_split_kernel(
     A.e = PAGED ? -126 : 0;
 
     for (int k = 0; k < nb; ++k) {
-        const int kn = k + S::RING - 1;
-        if (kn < nb) {
-            // slot kn % RING was read in the previous iteration: those reads must be done
-            wait_lds_reads();
-            dma_block<D, PAGED>(ring + (kn % S::RING) * S::SLOT, c, dl, first + kn * STRIDE, t_end, lane);
-        }
         // block k has landed once no more than (blocks issued after it) * NDMA loads remain
         const int after = min(S::RING - 1, nb - 1 - k);
         if (after >= 3) wait_vmem_at_most<3 * S::NDMA>();
@@ -612,6 +607,12 @@ __global__ void __launch_bounds__((DecShape<D, PAGED>::NT)) decode_split_kernel(
         const int tb = first + k * STRIDE;
         process_block<D, PAGED, CAP>(ring + (k % S::RING) * S::SLOT, tb, t_end, tb + kTB <= t_end,
                                      cap_log2, qbias, qx, A, lane);
+        const int kn = k + S::RING;
+        if (kn < nb) {
+            // the slot of block k is refilled once this wave's reads of it are done
+            wait_lds_reads();
+            dma_block<D, PAGED>(ring + (k % S::RING) * S::SLOT, c, dl, first + kn * STRIDE, t_end, lane);
+        }
     }
 
     // ---- finish the wave: pair sums (hi + lo columns), row sums over the 16-lane rows ------
