@@ -227,14 +227,14 @@ class Forward(Workload):
             self.S, self.H, self.Hkv, self.D, self.causal, self.W, self.cap = 2048, 16, 8, 256, True, 512, 50.0
             q, k, v = synth.prefill_inputs(synth.seed_of(3), 2048, 2048, 16, 8, 256, "f16")
             self.kind = "mfma"
-            self.kernel = "fwd_f16_kernel<256, 1, 8, 2, true>"
+            self.kernel = "fwd_f16_kernel<256, 1, 8, 2, 64, true>"
             self.desc = {"workload": "causal GQA prefill, f16, 2048 tokens, 16/8 heads, head_dim "
                                      "256, sliding window 512, softcap 50, scale 1/16"}
         else:
             self.S, self.H, self.Hkv, self.D, self.causal, self.W, self.cap = 2304, 16, 16, 64, False, 0, 0.0
             q, k, v = synth.vision_inputs(synth.seed_of(4), 2304, 16, 64)
             self.kind = "mfma"
-            self.kernel = "fwd_f16_kernel<64, 1, 4, 3, false>"
+            self.kernel = "fwd_f16_kernel<64, 1, 3, 2, 96, false>"
             self.desc = {"workload": "bidirectional vision attention, f16 [16, 2304, 64] "
                                      "head-major, scale 1/8"}
         self.vision = name == "vision_f16"

@@ -92,20 +92,20 @@ __device__ __forceinline__ float score_transform(const FwdParams& a, float s) {
 //          lane j points at V[key_0 + j/4][d_0 + 4 (j%4)] and lane i receives
 //          V[key_0 + k][d_0 + i] for k = 0..3, which is the transposed operand.
 
-template <int D, int QB_, int NW_, int NS_>
+template <int D, int QB_, int NW_, int NS_, int BN_>
 struct F16Shape {
     static constexpr int NW = NW_;                // waves per workgroup
     static constexpr int QB = QB_;                // 16-row query blocks per wave
     static constexpr int NS = NS_;                // LDS ring stages
     static constexpr int NT = 64 * NW;
     static constexpr int BM = NW * QB * 16;       // query rows per workgroup
-    static constexpr int BN = 64;                 // keys per tile
+    static constexpr int BN = BN_;                // keys per tile (a multiple of 32)
     static constexpr int TILE = BN * D * 2;       // bytes of one K (or V) tile
     static constexpr int LI = TILE / 1024 / NW;   // 1 KB DMA loads per wave per tile, K or V
     static constexpr int DC = D / 32;             // 32-wide k chunks of the QK^T product
     static constexpr int NDB = D / 16;            // 16-row d blocks of O^T
     static constexpr int NKB = BN / 16;           // 16-key blocks of S^T
-    static_assert(LI >= 1 && LI * 1024 * NW == TILE, "tile split");
+    static_assert(LI >= 1 && LI * 1024 * NW == TILE && BN % 32 == 0, "tile split");
 };
 
 // Physical 16-byte chunk of logical chunk c in K row r / V row r.
@@ -136,18 +136,18 @@ __device__ __forceinline__ void dma16(const void* gptr, const void* lds_base) {
 
 // Per-lane byte offsets of the DMA loads of one tile: load j of this wave covers LDS bytes
 // [(j * NW + w) * 1024, +1024); lane l's 16 bytes hold chunk p of row r of the tile.
-template <int D, int QB, int NW, int NS>
+template <int D, int QB, int NW, int NS, int BN>
 struct DmaLane {
-    using S = F16Shape<D, QB, NW, NS>;
+    using S = F16Shape<D, QB, NW, NS, BN>;
     int r[S::LI];            // tile row (key offset) of load j
     uint32_t kg[S::LI];      // byte offset of the K chunk from the tile's first key row
     uint32_t vg[S::LI];      // same for V
 };
 
-template <int D, int QB, int NW, int NS>
-__device__ __forceinline__ void dma_lane_init(DmaLane<D, QB, NW, NS>& L, const FwdParams& a, int w,
+template <int D, int QB, int NW, int NS, int BN>
+__device__ __forceinline__ void dma_lane_init(DmaLane<D, QB, NW, NS, BN>& L, const FwdParams& a, int w,
                                               int lane) {
-    using S = F16Shape<D, QB, NW, NS>;
+    using S = F16Shape<D, QB, NW, NS, BN>;
 #pragma unroll
     for (int j = 0; j < S::LI; ++j) {
         const int byte = (j * NW + w) * 1024 + 16 * lane;
@@ -159,11 +159,11 @@ __device__ __forceinline__ void dma_lane_init(DmaLane<D, QB, NW, NS>& L, const F
 }
 
 // DMA one K tile and one V tile (keys ks .. ks+BN-1, clamped to kv_len) into an LDS stage.
-template <int D, int QB, int NW, int NS>
+template <int D, int QB, int NW, int NS, int BN>
 __device__ __forceinline__ void f16_dma_tile(const FwdParams& a, const char* kg, const char* vg,
-                                             const DmaLane<D, QB, NW, NS>& L, int ks, int w,
+                                             const DmaLane<D, QB, NW, NS, BN>& L, int ks, int w,
                                              int lane, char* k_dst, char* v_dst) {
-    using S = F16Shape<D, QB, NW, NS>;
+    using S = F16Shape<D, QB, NW, NS, BN>;
     const long row_bytes = a.k_row * 2;
     if (ks + S::BN <= a.kv_len) {
         const char* kt = kg + ks * row_bytes;
@@ -195,9 +195,9 @@ __device__ __forceinline__ half4_t lds_read_tr16(const char* p) {
     return __builtin_bit_cast(half4_t, v);
 }
 
-template <int D, int QB, int NW, int NS, bool CAP>
+template <int D, int QB, int NW, int NS, int BN, bool CAP>
 __global__ void __launch_bounds__(64 * NW) fwd_f16_kernel(FwdParams a) {
-    using S = F16Shape<D, QB, NW, NS>;
+    using S = F16Shape<D, QB, NW, NS, BN>;
     __shared__ __attribute__((aligned(1024))) char k_lds[NS][S::TILE];
     __shared__ __attribute__((aligned(1024))) char v_lds[NS][S::TILE];
 
@@ -217,14 +217,14 @@ __global__ void __launch_bounds__(64 * NW) fwd_f16_kernel(FwdParams a) {
     const char* kg = reinterpret_cast<const char*>(reinterpret_cast<const _Float16*>(a.k) + (long)kvh * a.k_head);
     const char* vg = reinterpret_cast<const char*>(reinterpret_cast<const _Float16*>(a.v) + (long)kvh * a.k_head);
 
-    DmaLane<D, QB, NW, NS> dl;
+    DmaLane<D, QB, NW, NS, BN> dl;
     dma_lane_init(dl, a, w, lane);
 
     // prologue: tiles kt0 .. kt0 + NS - 2 in flight
 #pragma unroll
     for (int st0 = 0; st0 < NS - 1; ++st0)
         if (tr.kt0 + st0 < tr.kt1)
-            f16_dma_tile<D, QB, NW, NS>(a, kg, vg, dl, (tr.kt0 + st0) * S::BN, w, lane, k_lds[st0], v_lds[st0]);
+            f16_dma_tile<D, QB, NW, NS, BN>(a, kg, vg, dl, (tr.kt0 + st0) * S::BN, w, lane, k_lds[st0], v_lds[st0]);
 
     // ---- Q fragments (B operand of S^T = K Q^T) --------------------------------------------
     half8_t qf[S::QB][S::DC];
@@ -303,7 +303,7 @@ __global__ void __launch_bounds__(64 * NW) fwd_f16_kernel(FwdParams a) {
             const int nxt = kt + NS - 1;
             if (nxt < tr.kt1) {
                 const int sn = (stage + NS - 1) % NS;
-                f16_dma_tile<D, QB, NW, NS>(a, kg, vg, dl, nxt * S::BN, w, lane, k_lds[sn], v_lds[sn]);
+                f16_dma_tile<D, QB, NW, NS, BN>(a, kg, vg, dl, nxt * S::BN, w, lane, k_lds[sn], v_lds[sn]);
             }
         }
         const char* kl = k_lds[stage];
@@ -597,21 +597,24 @@ __global__ void __launch_bounds__(256) fwd_f32_kernel(FwdParams a) {
     }
 }
 
-// Tile configuration per head_dim: 16-row blocks per wave, waves per workgroup, LDS stages.
+// Tile configuration per head_dim: 16-row blocks per wave, waves per workgroup, LDS stages,
+// keys per tile.  head_dim 64 uses three waves (48 query rows) and 96-key tiles: 48 KB of
+// LDS per workgroup, three workgroups per compute unit, and a 2304-row, 16-head vision
+// call comes to 768 workgroups, three per compute unit, with no tail.
 template <int D> struct F16Cfg;
-template <> struct F16Cfg<64> { static constexpr int QB = 1, NW = 4, NS = 3; };
-template <> struct F16Cfg<128> { static constexpr int QB = 1, NW = 4, NS = 2; };
-template <> struct F16Cfg<256> { static constexpr int QB = 1, NW = 8, NS = 2; };
+template <> struct F16Cfg<64> { static constexpr int QB = 1, NW = 3, NS = 2, BN = 96; };
+template <> struct F16Cfg<128> { static constexpr int QB = 1, NW = 4, NS = 2, BN = 64; };
+template <> struct F16Cfg<256> { static constexpr int QB = 1, NW = 8, NS = 2, BN = 64; };
 
 template <int D>
 hipError_t launch_d(const FwdParams& p, int dtype, hipStream_t st) {
     const dim3 grid(p.n_qblocks * p.H);
     if (dtype == 1) {
-        constexpr int QB = F16Cfg<D>::QB, NW = F16Cfg<D>::NW, NS = F16Cfg<D>::NS;
+        constexpr int QB = F16Cfg<D>::QB, NW = F16Cfg<D>::NW, NS = F16Cfg<D>::NS, BN = F16Cfg<D>::BN;
         if (p.softcap > 0.f)
-            hipLaunchKernelGGL((fwd_f16_kernel<D, QB, NW, NS, true>), grid, dim3(64 * NW), 0, st, p);
+            hipLaunchKernelGGL((fwd_f16_kernel<D, QB, NW, NS, BN, true>), grid, dim3(64 * NW), 0, st, p);
         else
-            hipLaunchKernelGGL((fwd_f16_kernel<D, QB, NW, NS, false>), grid, dim3(64 * NW), 0, st, p);
+            hipLaunchKernelGGL((fwd_f16_kernel<D, QB, NW, NS, BN, false>), grid, dim3(64 * NW), 0, st, p);
     } else {
         hipLaunchKernelGGL(fwd_f32_kernel<D>, grid, dim3(256), 0, st, p);
     }
