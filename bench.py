@@ -6,8 +6,9 @@
 A step is one call of the workload's entry point over one batch of synthetic input
 (inputs already resident in HBM).  The headline workload is single-token decode over a
 contiguous f16 KV cache (32 query / 8 KV heads, head_dim 128, kv_len 4096); the other
-four workloads (f32 causal prefill, f16 windowed+softcapped GQA prefill, f16 vision,
-batched paged int8 decode) are measured on the same JSON line under "workloads".
+workloads (f32 causal prefill, f16 windowed+softcapped GQA prefill, f16 vision, batched
+paged int8 decode, and f16 chunked prefill against a cache whose length is read on the
+device) are measured on the same JSON line under "workloads".
 
 Timing: W untimed steps, then K steps between HIP events recorded on the stream the
 kernels run on, after a device synchronisation on both sides.  Every workload rotates
@@ -44,7 +45,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="decode_f16",
                     choices=["decode_f16", "prefill_f32", "prefill_f16", "vision_f16",
-                             "decode_paged_q8", "all"])
+                             "decode_paged_q8", "prefill_chunk_f16", "all"])
     ap.add_argument("--only-headline", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true",
@@ -230,6 +231,15 @@ class Forward(Workload):
             self.kernel = "fwd_f16_kernel<256, 1, 8, 2, 64, true>"
             self.desc = {"workload": "causal GQA prefill, f16, 2048 tokens, 16/8 heads, head_dim "
                                      "256, sliding window 512, softcap 50, scale 1/16"}
+        elif name == "prefill_chunk_f16":
+            self.S, self.H, self.Hkv, self.D, self.causal, self.W, self.cap = 512, 16, 8, 128, True, 0, 0.0
+            self.L = 4096
+            q, k, v = synth.prefill_inputs(synth.seed_of(3) + 61, 512, 4096, 16, 8, 128, "f16")
+            self.kind = "mfma"
+            self.kernel = "fwd_f16_kernel<128, 1, 4, 2, 64, false>"
+            self.desc = {"workload": "chunked causal prefill against a cache, f16, 512 new tokens "
+                                     "after 3584 cached (kv length 4096 read on the device), "
+                                     "16/8 heads, head_dim 128, scale 1/sqrt(128)"}
         else:
             self.S, self.H, self.Hkv, self.D, self.causal, self.W, self.cap = 2304, 16, 16, 64, False, 0, 0.0
             q, k, v = synth.vision_inputs(synth.seed_of(4), 2304, 16, 64)
@@ -238,6 +248,9 @@ class Forward(Workload):
             self.desc = {"workload": "bidirectional vision attention, f16 [16, 2304, 64] "
                                      "head-major, scale 1/8"}
         self.vision = name == "vision_f16"
+        self.chunk = name == "prefill_chunk_f16"
+        if not self.chunk:
+            self.L = self.S
         self.scale = 1.0 / math.sqrt(self.D)
         self.np_in = (q, k, v)
         tq, tk, tv = (torch.from_numpy(np.ascontiguousarray(x)).to(dev) for x in (q, k, v))
@@ -246,10 +259,11 @@ class Forward(Workload):
         self.copies = [(tq, tk, tv)] + [(tq.clone(), tk.clone(), tv.clone())
                                         for _ in range(self.nc - 1)]
         self.o = torch.empty_like(tq)
+        self.kv_len = torch.tensor([self.L], dtype=torch.int32, device=dev)
         self.desc["input_copies"] = self.nc
 
     def live_pairs(self):
-        S = L = self.S
+        S, L = self.S, self.L
         if not self.causal:
             return S * L
         tot = 0
@@ -263,6 +277,10 @@ class Forward(Workload):
         q, k, v = self.copies[i % self.nc]
         if self.vision:
             self.ta.attn_vision(q, k, v, self.o, scale=self.scale)
+        elif self.chunk:
+            self.ta.attn_prefill_device_kv_len(q, k, v, self.o, self.kv_len, causal=self.causal,
+                                               scale=self.scale, sliding_window=self.W,
+                                               attn_softcap=self.cap)
         else:
             self.ta.attn_prefill(q, k, v, self.o, causal=self.causal, scale=self.scale,
                                  sliding_window=self.W, attn_softcap=self.cap)
@@ -279,7 +297,7 @@ class Forward(Workload):
             q, k, v = (np.transpose(x, (1, 0, 2)) for x in (q, k, v))
         out = []
         for i in rows:
-            hi = i + 1 if self.causal else k.shape[0]
+            hi = self.L - self.S + i + 1 if self.causal else k.shape[0]
             out.append(oracle.attention(q[None, i:i + 1], k[None, :hi], v[None, :hi],
                                         causal=self.causal, window=self.W, softcap=self.cap,
                                         scale=self.scale, threads=threads)[0, 0])
@@ -304,7 +322,7 @@ class Forward(Workload):
         return self._oracle_rows(self.cpu_rows(), threads)
 
 
-ALL = ["decode_f16", "prefill_f32", "prefill_f16", "vision_f16", "decode_paged_q8"]
+ALL = ["decode_f16", "prefill_f32", "prefill_f16", "vision_f16", "decode_paged_q8", "prefill_chunk_f16"]
 
 
 def make(name, dev):

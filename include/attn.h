@@ -82,6 +82,28 @@ int attn_prefill(const void *q, const void *k, const void *v, void *o, int dtype
                  void *stream);
 
 /*
+ * Chunked prefill against a cache whose length is read on the device (doppler
+ * attention.js: kvLenSource = 1 takes kvLen from a buffer; run.js: a chunk of numTokens
+ * new queries starts at startPos = currentSeqLen against kvLen = currentSeqLen +
+ * numTokens cached keys).  The same computation as attn_prefill with kv_len = *kv_len,
+ * for callers that capture the launch once (a HIP graph) and replay it as the cache grows.
+ *
+ *   q, o       : [seq_len, num_heads, head_dim]        token-major, dtype
+ *   k, v       : [max_kv_len, num_kv_heads, head_dim]  capacity of the cache; rows at or
+ *                past *kv_len are never read
+ *   kv_len     : DEVICE pointer to one int32 L, read by the kernel when it runs; query row
+ *                i sits at position L - seq_len + i.  Contract: seq_len <= L <= max_kv_len.
+ *                Outside it every output row is NaN (loud, not silent).
+ *   Other arguments and host-side checks as attn_prefill (with max_kv_len in place of
+ *   kv_len); kv_len must be non-null and 4-byte aligned.
+ */
+int attn_prefill_device_kv_len(const void *q, const void *k, const void *v, void *o, int dtype,
+                               int seq_len, int max_kv_len, const int32_t *kv_len,
+                               int num_heads, int num_kv_heads, int head_dim, int causal,
+                               int sliding_window, float attn_softcap, float scale,
+                               void *stream);
+
+/*
  * Bidirectional vision-tower self-attention (rullama 0.5.0, src/backend/dispatch/
  * attention.rs, vision_attention_chained and the head-major flash variant
  * vision_attention_flash_sub_hpd_chained): no mask, every patch sees every patch.

@@ -24,8 +24,9 @@ def declared_functions():
 
 def test_header_declares_the_boundary():
     names = declared_functions()
-    for n in ("attn_prefill", "attn_vision", "attn_decode", "attn_decode_paged_q8",
-              "attn_decode_workspace_bytes", "attn_last_error", "attn_set_decode_split"):
+    for n in ("attn_prefill", "attn_prefill_device_kv_len", "attn_vision", "attn_decode",
+              "attn_decode_paged_q8", "attn_decode_workspace_bytes", "attn_last_error",
+              "attn_set_decode_split"):
         assert n in names
 
 
@@ -103,6 +104,31 @@ def decode(**kw):
 ])
 def test_decode_validation(kw, code, msg):
     assert decode(**kw) == code
+    assert msg in ta.attn_last_error()
+
+
+def prefill_dev(**kw):
+    a = dict(q=P, k=P, v=P, o=P, dtype=1, seq_len=16, max_kv_len=64, kl=P, H=4, Hkv=2, D=128,
+             causal=1, W=0, cap=0.0, scale=0.125)
+    a.update(kw)
+    return ta.lib().attn_prefill_device_kv_len(a["q"], a["k"], a["v"], a["o"], a["dtype"],
+                                               a["seq_len"], a["max_kv_len"], a["kl"], a["H"],
+                                               a["Hkv"], a["D"], a["causal"], a["W"], a["cap"],
+                                               a["scale"], None)
+
+
+@pytest.mark.parametrize("kw,code,msg", [
+    (dict(kl=None), ta.ATTN_ERR_INVALID_ARG, "kv_len must not be null"),
+    (dict(kl=P + 2), ta.ATTN_ERR_INVALID_ARG, "kv_len must be 4-byte aligned"),
+    (dict(o=MIS), ta.ATTN_ERR_INVALID_ARG, "16-byte aligned"),
+    (dict(max_kv_len=0), ta.ATTN_ERR_INVALID_ARG, "invalid max_kv_len 0"),
+    (dict(seq_len=65), ta.ATTN_ERR_INVALID_ARG, "seq_len 65 must be in [1, max_kv_len = 64]"),
+    (dict(dtype=3), ta.ATTN_ERR_INVALID_ARG, "dtype"),
+    (dict(D=96), ta.ATTN_ERR_UNSUPPORTED, "head_dim"),
+    (dict(scale=float("nan")), ta.ATTN_ERR_INVALID_ARG, "scale"),
+])
+def test_prefill_device_kv_len_validation(kw, code, msg):
+    assert prefill_dev(**kw) == code
     assert msg in ta.attn_last_error()
 
 

@@ -393,6 +393,84 @@ def test_prefill_full_workload_sampled_rows(dev, c3_inputs):
         assert np.array_equal(got[0, h], v[0, h // G])
 
 
+# ---- chunked prefill against a cache whose length is read on the device -----------------
+
+def run_prefill_dev_len(dev, q, kcap, vcap, L, causal, W=0, cap=0.0):
+    S, H, D = q.shape
+    qd, kd, vd = to_dev(q, dev), to_dev(kcap, dev), to_dev(vcap, dev)
+    od = torch.empty_like(qd)
+    kl = torch.tensor([L], dtype=torch.int32, device=dev)
+    ta.attn_prefill_device_kv_len(qd, kd, vd, od, kl, causal=causal, scale=1 / math.sqrt(D),
+                                  sliding_window=W, attn_softcap=cap)
+    torch.cuda.synchronize()
+    return od.cpu().numpy()
+
+
+@pytest.mark.parametrize("dtype,D,W,cap", [
+    ("f16", 64, 0, 0.0), ("f16", 128, 0, 0.0), ("f16", 256, 100, 50.0), ("f16", 128, 33, 0.0),
+    ("f32", 64, 0, 0.0), ("f32", 128, 0, 20.0),
+])
+def test_prefill_device_kv_len(dev, dtype, D, W, cap):
+    """A 77-query chunk against a 400-row cache at lengths 77 (no history), 250 and 400: the
+    oracle on the first L keys, and bit-identical to attn_prefill with kv_len = L."""
+    say("prefill device kv_len %s D=%d W=%d cap=%g" % (dtype, D, W, cap))
+    S, Lmax, H, Hkv = 77, 400, 4, 2
+    q, k, v = synth.prefill_inputs(synth.seed_of(3) + 31 + D, S, Lmax, H, Hkv, D, dtype)
+    tol = TOL_F16 if dtype == "f16" else TOL_F32
+    for L in (77, 250, 400):
+        got = run_prefill_dev_len(dev, q, k, v, L, True, W, cap)
+        want = oracle.attention(q[None], k[None, :L], v[None, :L], causal=True, window=W,
+                                softcap=cap, scale=1 / math.sqrt(D))[0]
+        assert np.all(np.isfinite(got))
+        assert maxabs(got, want) < tol, L
+        ref = run_prefill(dev, q, k[:L], v[:L], True, W, cap)
+        assert np.array_equal(got, ref), L
+
+
+def test_prefill_device_kv_len_graph_replays(dev):
+    """One captured launch replayed as the cache grows: every replay equals the eager call
+    with that length (bitwise), including two replays at the same length."""
+    say("prefill device kv_len graph replays")
+    S, Lmax, H, Hkv, D = 64, 1024, 8, 4, 128
+    q, k, v = synth.prefill_inputs(synth.seed_of(3) + 41, S, Lmax, H, Hkv, D, "f16")
+    qd, kd, vd = to_dev(q, dev), to_dev(k, dev), to_dev(v, dev)
+    od = torch.empty_like(qd)
+    kl = torch.tensor([Lmax], dtype=torch.int32, device=dev)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        ta.attn_prefill_device_kv_len(qd, kd, vd, od, kl, causal=True, scale=1 / math.sqrt(D))
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=side):
+        ta.attn_prefill_device_kv_len(qd, kd, vd, od, kl, causal=True, scale=1 / math.sqrt(D))
+    torch.cuda.synchronize()
+    for L in (64, 300, 300, 1024, 700):
+        kl.fill_(L)
+        od.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = od.cpu().numpy()
+        ref = run_prefill(dev, q, k[:L], v[:L], True)
+        assert np.array_equal(got, ref), L
+    rows = [0, 31, 63]
+    want = prefill_oracle_rows(q, k[:700], v[:700], rows, True)
+    assert maxabs(got[rows], want) < TOL_F16
+
+
+def test_prefill_device_kv_len_out_of_contract_gives_nan(dev):
+    say("prefill device kv_len out of contract")
+    S, Lmax, H, Hkv, D = 40, 100, 2, 1, 64
+    q, k, v = synth.prefill_inputs(synth.seed_of(3) + 51, S, Lmax, H, Hkv, D, "f16")
+    for L in (39, 0, 101):
+        got = run_prefill_dev_len(dev, q, k, v, L, True)
+        assert np.all(np.isnan(got)), L
+    got = run_prefill_dev_len(dev, q, k, v, 40, True)
+    assert np.all(np.isfinite(got))
+
+
 def test_prefill_softcap_is_applied(dev):
     say("prefill softcap sensitivity")
     q, k, v = synth.prefill_inputs(synth.seed_of(3) + 11, 160, 160, 2, 1, 128, "f16")

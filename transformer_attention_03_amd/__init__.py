@@ -42,6 +42,7 @@ def lib() -> ctypes.CDLL:
         L = ctypes.CDLL(LIB_PATH)
         vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
         L.attn_prefill.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, i, i, f, f, vp]
+        L.attn_prefill_device_kv_len.argtypes = [vp, vp, vp, vp, i, i, i, vp, i, i, i, i, i, f, f, vp]
         L.attn_vision.argtypes = [vp, vp, vp, vp, i, i, i, f, vp]
         L.attn_decode.argtypes = [vp, vp, vp, vp, i, i, i, i, i, f, f, vp, sz, vp]
         L.attn_decode_paged_q8.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i,
@@ -51,8 +52,8 @@ def lib() -> ctypes.CDLL:
         L.attn_set_decode_split.argtypes = [i]
         L.attn_last_error.argtypes = []
         L.attn_last_error.restype = ctypes.c_char_p
-        for name in ("attn_prefill", "attn_vision", "attn_decode", "attn_decode_paged_q8",
-                     "attn_set_decode_split"):
+        for name in ("attn_prefill", "attn_prefill_device_kv_len", "attn_vision", "attn_decode",
+                     "attn_decode_paged_q8", "attn_set_decode_split"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -104,6 +105,24 @@ def attn_prefill(q, k, v, o, *, causal: bool, scale: float, sliding_window: int 
     _check(lib().attn_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _dtype_code(q), S, L, H, Hkv,
                               D, 1 if causal else 0, int(sliding_window), float(attn_softcap),
                               float(scale), _stream(q, stream)))
+
+
+def attn_prefill_device_kv_len(q, k, v, o, kv_len, *, causal: bool, scale: float,
+                               sliding_window: int = 0, attn_softcap: float = 0.0, stream=None):
+    """q, o: [seq_len, num_heads, head_dim]; k, v: [max_kv_len, num_kv_heads, head_dim];
+    kv_len: int32 device tensor of one element, read when the kernel runs."""
+    _need_contig(q, k, v, o)
+    S, H, D = q.shape
+    Lmax, Hkv, Dk = k.shape
+    if Dk != D or v.shape != k.shape or o.shape != q.shape or o.dtype != q.dtype:
+        raise ValueError("shape/dtype mismatch")
+    import torch
+    if kv_len.dtype != torch.int32 or kv_len.numel() != 1 or kv_len.device != q.device:
+        raise ValueError("kv_len must be one int32 element on the device of q")
+    _check(lib().attn_prefill_device_kv_len(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _dtype_code(q), S,
+                                            Lmax, _ptr(kv_len), H, Hkv, D, 1 if causal else 0,
+                                            int(sliding_window), float(attn_softcap), float(scale),
+                                            _stream(q, stream)))
 
 
 def attn_vision(q, k, v, o, *, scale: float, stream=None):

@@ -178,8 +178,9 @@ int launch_status(hipError_t e, const char* what) {
 int run_fwd(const void* q, const void* k, const void* v, void* o, int dtype, int seq_len, int kv_len,
             int H, int Hkv, int D, int causal, int window, float softcap, float scale, long q_row,
             long q_head, long k_row, long k_head, long o_row, long o_head, void* stream,
-            const char* what) {
+            const char* what, const int32_t* kv_len_dev = nullptr) {
     ta03::FwdParams p;
+    p.kv_len_dev = kv_len_dev;
     p.q = q; p.k = k; p.v = v; p.o = o;
     p.q_row = q_row; p.q_head = q_head;
     p.k_row = k_row; p.k_head = k_head;
@@ -222,6 +223,35 @@ int attn_prefill(const void* q, const void* k, const void* v, void* o, int dtype
     return run_fwd(q, k, v, o, dtype, seq_len, kv_len, num_heads, num_kv_heads, head_dim, causal,
                    sliding_window, attn_softcap, scale, num_heads * hd, hd, num_kv_heads * hd, hd,
                    num_heads * hd, hd, stream, "attn_prefill");
+}
+
+int attn_prefill_device_kv_len(const void* q, const void* k, const void* v, void* o, int dtype,
+                               int seq_len, int max_kv_len, const int32_t* kv_len, int num_heads,
+                               int num_kv_heads, int head_dim, int causal, int sliding_window,
+                               float attn_softcap, float scale, void* stream) {
+    if (dtype != ATTN_F32 && dtype != ATTN_F16)
+        return fail(ATTN_ERR_INVALID_ARG, "attn_prefill_device_kv_len: dtype %d is neither ATTN_F32 nor ATTN_F16", dtype);
+    TRY(check_ptr(q, "q"));
+    TRY(check_ptr(k, "k"));
+    TRY(check_ptr(v, "v"));
+    TRY(check_ptr(o, "o"));
+    if (!kv_len) return fail(ATTN_ERR_INVALID_ARG, "attn_prefill_device_kv_len: kv_len must not be null");
+    if (!aligned(kv_len, 4)) return fail(ATTN_ERR_INVALID_ARG, "attn_prefill_device_kv_len: kv_len must be 4-byte aligned");
+    if (max_kv_len < 1)
+        return fail(ATTN_ERR_INVALID_ARG, "attn_prefill_device_kv_len: invalid max_kv_len %d (must be >= 1)", max_kv_len);
+    if (seq_len < 1 || seq_len > max_kv_len)
+        return fail(ATTN_ERR_INVALID_ARG, "attn_prefill_device_kv_len: seq_len %d must be in [1, max_kv_len = %d]",
+                    seq_len, max_kv_len);
+    if (causal != 0 && causal != 1)
+        return fail(ATTN_ERR_INVALID_ARG, "attn_prefill_device_kv_len: causal must be 0 or 1");
+    TRY(check_heads(num_heads, num_kv_heads, head_dim));
+    TRY(check_scalars(sliding_window, attn_softcap, scale));
+    if ((long)max_kv_len * num_kv_heads * head_dim > kMaxElems || (long)seq_len * num_heads * head_dim > kMaxElems)
+        return fail(ATTN_ERR_INVALID_ARG, "attn_prefill_device_kv_len: tensor too large");
+    const long hd = head_dim;
+    return run_fwd(q, k, v, o, dtype, seq_len, max_kv_len, num_heads, num_kv_heads, head_dim, causal,
+                   sliding_window, attn_softcap, scale, num_heads * hd, hd, num_kv_heads * hd, hd,
+                   num_heads * hd, hd, stream, "attn_prefill_device_kv_len", kv_len);
 }
 
 int attn_vision(const void* q, const void* k, const void* v, void* o, int num_patches, int num_heads,

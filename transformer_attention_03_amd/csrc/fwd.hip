@@ -62,6 +62,25 @@ __device__ __forceinline__ bool visible(const FwdParams& a, int key, int pos) {
     return (key < a.kv_len) & ((a.causal == 0) | (key <= pos)) & ((a.window <= 0) | (pos - key < a.window));
 }
 
+// kv length from device memory (chunked prefill against a cache whose length is only known
+// on the device, e.g. under graph replay): a.kv_len then holds the capacity of K/V.  A
+// length outside [seq_len, capacity] is out of contract: the workgroup writes NaN to its
+// rows and returns false.
+template <typename T, int D>
+__device__ __forceinline__ bool resolve_kv_len(FwdParams& a, int head, int q0, int bm) {
+    if (a.kv_len_dev == nullptr) return true;
+    const int L = *a.kv_len_dev;
+    if (L >= a.seq_len && L <= a.kv_len) {
+        a.kv_len = L;
+        return true;
+    }
+    T* og = reinterpret_cast<T*>(a.o) + (long)head * a.o_head;
+    const int rows = min(bm, a.seq_len - q0);
+    for (int i = threadIdx.x; i < rows * D; i += blockDim.x)
+        og[(long)(q0 + i / D) * a.o_row + i % D] = (T)__builtin_nanf("");
+    return false;
+}
+
 // Work item for this workgroup: XCD-aware (consecutive work ids land on one XCD, so the
 // query blocks of a head share that XCD's L2) and heaviest causal blocks first.
 __device__ __forceinline__ void work_item(const FwdParams& a, int& head, int& qblock) {
@@ -211,6 +230,7 @@ __global__ void __launch_bounds__(64 * NW) fwd_f16_kernel(FwdParams a) {
     work_item(a, head, qblock);
     const int kvh = head / (a.H / a.Hkv);
     const int q0 = qblock * S::BM;
+    if (!resolve_kv_len<_Float16, D>(a, head, q0, S::BM)) return;
     const TileRange tr = tile_range(a, q0, S::BM, S::BN);
 
     const _Float16* qg = reinterpret_cast<const _Float16*>(a.q) + (long)head * a.q_head;
@@ -476,6 +496,7 @@ __global__ void __launch_bounds__(256) fwd_f32_kernel(FwdParams a) {
     work_item(a, head, qblock);
     const int kvh = head / (a.H / a.Hkv);
     const int q0 = qblock * S::BM;
+    if (!resolve_kv_len<float, D>(a, head, q0, S::BM)) return;
     const TileRange tr = tile_range(a, q0, S::BM, S::BN);
 
     const float* qg = reinterpret_cast<const float*>(a.q) + (long)head * a.q_head;

@@ -49,6 +49,7 @@ struct FwdParams {
     float scale, scale_log2;
     float softcap, inv_softcap;
     int n_qblocks;             // query blocks per head
+    const int32_t* kv_len_dev; // optional: the kv length, read on the device (kv_len is then its maximum)
 };
 
 hipError_t launch_decode(const DecodeParams& p, int head_dim, int gc, bool paged, int batch,
