@@ -7,8 +7,9 @@ A step is one call of the workload's entry point over one batch of synthetic inp
 (inputs already resident in HBM).  The headline workload is single-token decode over a
 contiguous f16 KV cache (32 query / 8 KV heads, head_dim 128, kv_len 4096); the other
 workloads (f32 causal prefill, f16 windowed+softcapped GQA prefill, f16 vision, batched
-paged int8 decode, and f16 chunked prefill against a cache whose length is read on the
-device) are measured on the same JSON line under "workloads".
+paged int8 decode, f16 chunked prefill against a cache whose length is read on the device,
+and f16 decode over a ring-buffer cache) are measured on the same JSON line under
+"workloads".
 
 Timing: W untimed steps, then K steps between HIP events recorded on the stream the
 kernels run on, after a device synchronisation on both sides.  Every workload rotates
@@ -45,7 +46,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="decode_f16",
                     choices=["decode_f16", "prefill_f32", "prefill_f16", "vision_f16",
-                             "decode_paged_q8", "prefill_chunk_f16", "all"])
+                             "decode_paged_q8", "prefill_chunk_f16", "decode_ring_f16", "all"])
     ap.add_argument("--only-headline", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true",
@@ -83,7 +84,7 @@ def log(msg):
 class DecodeF16(Workload):
     name = "decode_f16"
     kind = "hbm"
-    kernel = "decode_split_kernel<128, 4, false, false>"
+    kernel = "decode_split_kernel<128, 4, false, false, false>"
 
     def __init__(self, dev, H=32, Hkv=8, D=128, L=4096):
         import numpy as np
@@ -137,10 +138,38 @@ class DecodeF16(Workload):
                                 scale=self.scale, threads=threads)
 
 
+class DecodeRing(DecodeF16):
+    """Decode over a ring-buffer cache: a 4096-row ring holding the newest 4096 of 10000
+    tokens (position t at row t % 4096), the same bytes as the contiguous decode."""
+    name = "decode_ring_f16"
+    kernel = "decode_split_kernel<128, 4, false, false, true>"
+
+    def __init__(self, dev, total=10000):
+        super().__init__(dev)
+        import numpy as np
+        import torch
+        self.T = total
+        shift = (total - self.L) % self.L     # visible token j sits at row (T - R + j) % R
+        k = torch.from_numpy(np.ascontiguousarray(np.roll(self.k_np, shift, axis=1))).to(dev)
+        v = torch.from_numpy(np.ascontiguousarray(np.roll(self.v_np, shift, axis=1))).to(dev)
+        self.ks = [k.clone() for _ in range(self.nc)]
+        self.vs = [v.clone() for _ in range(self.nc)]
+        self.desc = dict(self.desc)
+        self.desc["workload"] = ("single-token decode over a ring-buffer f16 cache [8, 4096, 128] "
+                                 "holding the newest 4096 of 10000 tokens (row t mod 4096), f32 q "
+                                 "[32, 128], GQA 32/8, scale 1/sqrt(128)")
+        self.desc["ring_len"], self.desc["total_len"] = self.L, total
+
+    def step(self, i):
+        j = i % self.nc
+        self.ta.attn_decode_ring(self.q, self.ks[j], self.vs[j], self.o, self.ws, total_len=self.T,
+                                 scale=self.scale)
+
+
 class PagedQ8(Workload):
     name = "decode_paged_q8"
     kind = "hbm"
-    kernel = "decode_split_kernel<128, 4, true, false>"
+    kernel = "decode_split_kernel<128, 4, true, false, false>"
 
     def __init__(self, dev):
         import numpy as np
@@ -322,7 +351,8 @@ class Forward(Workload):
         return self._oracle_rows(self.cpu_rows(), threads)
 
 
-ALL = ["decode_f16", "prefill_f32", "prefill_f16", "vision_f16", "decode_paged_q8", "prefill_chunk_f16"]
+ALL = ["decode_f16", "prefill_f32", "prefill_f16", "vision_f16", "decode_paged_q8", "prefill_chunk_f16",
+       "decode_ring_f16"]
 
 
 def make(name, dev):
@@ -330,6 +360,8 @@ def make(name, dev):
         return DecodeF16(dev)
     if name == "decode_paged_q8":
         return PagedQ8(dev)
+    if name == "decode_ring_f16":
+        return DecodeRing(dev)
     return Forward(dev, name)
 
 

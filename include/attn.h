@@ -134,6 +134,28 @@ int attn_decode(const float *q, const void *k, const void *v, float *o,
                 void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * Single-token decode over a ring-buffer f16 cache that keeps the newest tokens of a
+ * sliding-window layer (doppler attention.js / run.js: kvLayout = 1 "ring" for a
+ * SlidingWindowKVCache, kvStart = totalSeqLen - kvLen with kvLen clipped to the window).
+ * The pages name the layout but not its index map; the reading adopted here is the plain
+ * one: the token at absolute position t lives at row t mod ring_len.
+ *
+ *   q, o      : float32 [num_heads, head_dim]
+ *   k, v      : float16 [num_kv_heads, ring_len, head_dim]  (head-major ring)
+ *   total_len : tokens seen so far (>= 1); the query sits at position total_len - 1
+ *   sliding_window : W, 0 <= W <= ring_len; the query sees the newest E tokens,
+ *               E = W if W > 0 else ring_len, i.e. positions [max(0, total_len - E),
+ *               total_len - 1].  Rows holding other positions are never read.
+ *   workspace : as attn_decode, sized by attn_decode_workspace_bytes(1, num_heads,
+ *               num_kv_heads, head_dim, ring_len).
+ *   Other arguments, checks and errors as attn_decode; W > ring_len is ATTN_ERR_INVALID_ARG.
+ */
+int attn_decode_ring(const float *q, const void *k, const void *v, float *o,
+                     int num_heads, int num_kv_heads, int head_dim, int ring_len,
+                     int total_len, int sliding_window, float attn_softcap, float scale,
+                     void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * Batched single-token decode over a paged, symmetric-int8 KV cache with float32 query
  * (doppler attention.js: kvLayout paged with pageSize and kvPageTable, kvLenSource = 1
  * reading kvLen from a buffer; executeAttentionTieredQuant: packed int8 K/V with separate

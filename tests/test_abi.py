@@ -25,8 +25,8 @@ def declared_functions():
 def test_header_declares_the_boundary():
     names = declared_functions()
     for n in ("attn_prefill", "attn_prefill_device_kv_len", "attn_vision", "attn_decode",
-              "attn_decode_paged_q8", "attn_decode_workspace_bytes", "attn_last_error",
-              "attn_set_decode_split"):
+              "attn_decode_ring", "attn_decode_paged_q8", "attn_decode_workspace_bytes",
+              "attn_last_error", "attn_set_decode_split"):
         assert n in names
 
 
@@ -129,6 +129,30 @@ def prefill_dev(**kw):
 ])
 def test_prefill_device_kv_len_validation(kw, code, msg):
     assert prefill_dev(**kw) == code
+    assert msg in ta.attn_last_error()
+
+
+def ring(**kw):
+    a = dict(q=P, k=P, v=P, o=P, H=32, Hkv=8, D=128, R=4096, T=40000, W=0, cap=0.0, scale=0.088,
+             ws=P, wsb=1 << 30)
+    a.update(kw)
+    return ta.lib().attn_decode_ring(a["q"], a["k"], a["v"], a["o"], a["H"], a["Hkv"], a["D"],
+                                     a["R"], a["T"], a["W"], a["cap"], a["scale"], a["ws"],
+                                     a["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,code,msg", [
+    (dict(v=None), ta.ATTN_ERR_INVALID_ARG, "v must not be null"),
+    (dict(R=0), ta.ATTN_ERR_INVALID_ARG, "invalid ring_len 0"),
+    (dict(T=0), ta.ATTN_ERR_INVALID_ARG, "invalid total_len 0"),
+    (dict(W=4097), ta.ATTN_ERR_INVALID_ARG, "sliding_window 4097 exceeds ring_len 4096"),
+    (dict(W=-1), ta.ATTN_ERR_INVALID_ARG, "sliding_window"),
+    (dict(D=48), ta.ATTN_ERR_UNSUPPORTED, "head_dim"),
+    (dict(ws=None), ta.ATTN_ERR_WORKSPACE, "workspace must not be null"),
+    (dict(wsb=64), ta.ATTN_ERR_WORKSPACE, "smaller than"),
+])
+def test_decode_ring_validation(kw, code, msg):
+    assert ring(**kw) == code
     assert msg in ta.attn_last_error()
 
 

@@ -138,6 +138,74 @@ def test_decode_repeat_is_deterministic_and_counters_reset(dev):
     assert torch.equal(o1, o2)
 
 
+# ---- ring-buffer cache of a sliding-window layer -----------------------------------------
+
+def ring_cache(x, total, R, span):
+    """The ring a cache of R rows holds after `total` tokens: position t at row t % R for the
+    newest min(total, R) positions.  Rows of positions outside the newest `span` (and rows
+    never written) hold NaN, so a stray read shows up in the output."""
+    Hkv, _, D = x.shape
+    ring = np.full((Hkv, R, D), np.nan, dtype=x.dtype)
+    for t in range(max(0, total - span), total):
+        ring[:, t % R] = x[:, t]
+    return ring
+
+
+def run_decode_ring(dev, q, kr, vr, total, W=0, cap=0.0):
+    H, D = q.shape
+    Hkv, R, _ = kr.shape
+    qd, kd, vd = to_dev(q, dev), to_dev(kr, dev), to_dev(vr, dev)
+    od = torch.empty((H, D), dtype=torch.float32, device=dev)
+    ws = ta.decode_workspace(1, H, Hkv, D, R, dev)
+    ta.attn_decode_ring(qd, kd, vd, od, ws, total_len=total, scale=1 / math.sqrt(D),
+                        sliding_window=W, attn_softcap=cap)
+    torch.cuda.synchronize()
+    assert int(ws[-256:].sum().item()) == 0
+    return od.cpu().numpy()
+
+
+@pytest.mark.parametrize("H,Hkv,D,R,total,W,cap", [
+    (8, 2, 128, 512, 512, 0, 0.0),         # full ring, no wrap
+    (8, 2, 128, 512, 1300, 0, 0.0),        # wrapped
+    (8, 2, 128, 512, 1300, 200, 0.0),      # window shorter than the ring
+    (4, 4, 64, 100, 37, 0, 0.0),           # ring not yet full
+    (16, 2, 256, 333, 5000, 333, 0.0),     # capacity not a multiple of 16
+    (8, 8, 128, 1000, 7777, 0, 30.0),      # softcap
+    (6, 3, 64, 48, 49, 17, 0.0),           # one step past a full ring, short window
+    (32, 8, 128, 4096, 9000, 0, 0.0),      # 4096-token ring, 9000 tokens seen
+])
+def test_decode_ring(dev, H, Hkv, D, R, total, W, cap):
+    """Oracle over the visible positions of the logical cache, and bit-identical to
+    attn_decode over the same positions stored contiguously."""
+    say("decode ring H=%d Hkv=%d D=%d R=%d total=%d W=%d cap=%g" % (H, Hkv, D, R, total, W, cap))
+    q, k, v = synth.decode_inputs(synth.seed_of(2) + 71 + R, H, Hkv, D, total)
+    span = W if W > 0 else R
+    lo = max(0, total - span)
+    got = run_decode_ring(dev, q, ring_cache(k, total, R, span), ring_cache(v, total, R, span),
+                          total, W, cap)
+    assert np.all(np.isfinite(got))
+    want = decode_oracle(q, k[:, lo:total], v[:, lo:total], cap=cap)
+    assert maxabs(got, want) < TOL_F16
+    ref, _ = run_decode(dev, q, np.ascontiguousarray(k[:, lo:total]),
+                        np.ascontiguousarray(v[:, lo:total]), cap=cap)
+    assert np.array_equal(got, ref)
+
+
+def test_decode_ring_split_sizes_agree(dev):
+    say("decode ring split sizes")
+    H, Hkv, D, R, total = 8, 2, 128, 1000, 3333
+    q, k, v = synth.decode_inputs(synth.seed_of(2) + 81, H, Hkv, D, total)
+    kr, vr = ring_cache(k, total, R, R), ring_cache(v, total, R, R)
+    want = decode_oracle(q, k[:, total - R:], v[:, total - R:])
+    try:
+        for t in (16, 48, 256, 1024):
+            ta.attn_set_decode_split(t)
+            got = run_decode_ring(dev, q, kr, vr, total)
+            assert maxabs(got, want) < TOL_F16, t
+    finally:
+        ta.attn_set_decode_split(0)
+
+
 def test_decode_softcap_is_applied(dev):
     """With q scaled x8 and c = 5 the capped and uncapped results differ by >> tolerance."""
     say("decode softcap sensitivity")

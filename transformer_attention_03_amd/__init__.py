@@ -45,6 +45,7 @@ def lib() -> ctypes.CDLL:
         L.attn_prefill_device_kv_len.argtypes = [vp, vp, vp, vp, i, i, i, vp, i, i, i, i, i, f, f, vp]
         L.attn_vision.argtypes = [vp, vp, vp, vp, i, i, i, f, vp]
         L.attn_decode.argtypes = [vp, vp, vp, vp, i, i, i, i, i, f, f, vp, sz, vp]
+        L.attn_decode_ring.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, f, f, vp, sz, vp]
         L.attn_decode_paged_q8.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i,
                                            f, f, vp, sz, vp]
         L.attn_decode_workspace_bytes.argtypes = [i, i, i, i, i]
@@ -53,7 +54,7 @@ def lib() -> ctypes.CDLL:
         L.attn_last_error.argtypes = []
         L.attn_last_error.restype = ctypes.c_char_p
         for name in ("attn_prefill", "attn_prefill_device_kv_len", "attn_vision", "attn_decode",
-                     "attn_decode_paged_q8", "attn_set_decode_split"):
+                     "attn_decode_ring", "attn_decode_paged_q8", "attn_set_decode_split"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -165,6 +166,21 @@ def attn_decode(q, k, v, o, workspace, *, scale: float, sliding_window: int = 0,
     _check(lib().attn_decode(_ptr(q), _ptr(k), _ptr(v), _ptr(o), H, Hkv, D, L,
                              int(sliding_window), float(attn_softcap), float(scale),
                              _ptr(workspace), ws_bytes, _stream(q, stream)))
+
+
+def attn_decode_ring(q, k, v, o, workspace, *, total_len: int, scale: float,
+                     sliding_window: int = 0, attn_softcap: float = 0.0, stream=None):
+    """q, o: float32 [num_heads, head_dim]; k, v: float16 ring [num_kv_heads, ring_len,
+    head_dim] holding position t at row t % ring_len; total_len tokens seen so far."""
+    _need_contig(q, k, v, o)
+    H, D = q.shape
+    Hkv, R, Dk = k.shape
+    if Dk != D or v.shape != k.shape or o.shape != q.shape:
+        raise ValueError("shape mismatch")
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(lib().attn_decode_ring(_ptr(q), _ptr(k), _ptr(v), _ptr(o), H, Hkv, D, R, int(total_len),
+                                  int(sliding_window), float(attn_softcap), float(scale),
+                                  _ptr(workspace), ws_bytes, _stream(q, stream)))
 
 
 def attn_decode_paged_q8(q, k_pages, v_pages, k_scales, v_scales, page_table, kv_lens, o,

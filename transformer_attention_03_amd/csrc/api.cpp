@@ -198,6 +198,39 @@ int run_fwd(const void* q, const void* k, const void* v, void* o, int dtype, int
     return launch_status(ta03::launch_fwd(p, D, dtype, reinterpret_cast<hipStream_t>(stream)), what);
 }
 
+// Contiguous or ring f16 decode: kv_len logical tokens (ring: at rows t mod ring), eff of
+// them visible (the newest), window as the kernel applies it.
+int run_decode_contiguous(const float* q, const void* k, const void* v, float* o, int num_heads,
+                          int num_kv_heads, int head_dim, int kv_len, int ring, int eff, int window,
+                          float attn_softcap, float scale, void* workspace, size_t workspace_bytes,
+                          void* stream, const char* what) {
+    const DecodePlan plan = plan_decode(1, num_heads, num_kv_heads, head_dim, eff, false);
+    const WorkspaceLayout wl = workspace_layout(1, num_heads, num_kv_heads, head_dim, plan);
+    if (plan.n_split > 1) {
+        if (!workspace) return fail(ATTN_ERR_WORKSPACE, "%s: workspace must not be null", what);
+        if (!aligned(workspace, 256)) return fail(ATTN_ERR_WORKSPACE, "%s: workspace must be 256-byte aligned", what);
+        if (workspace_bytes < wl.total)
+            return fail(ATTN_ERR_WORKSPACE, "%s: workspace of %zu bytes is smaller than the %zu required", what,
+                        workspace_bytes, wl.total);
+    }
+    if (plan.n_split > 65535 * 32) return fail(ATTN_ERR_INVALID_ARG, "%s: grid too large", what);
+    ta03::DecodeParams d{};
+    d.q = q; d.k = k; d.v = v; d.o = o;
+    char* ws = reinterpret_cast<char*>(workspace);
+    d.part_o = reinterpret_cast<float*>(ws + wl.o_off);
+    d.part_m = reinterpret_cast<float*>(ws + wl.m_off);
+    d.part_l = reinterpret_cast<float*>(ws + wl.l_off);
+    d.tickets = reinterpret_cast<uint32_t*>(ws + wl.t_off);
+    d.H = num_heads; d.Hkv = num_kv_heads; d.kv_len = kv_len; d.ring = ring;
+    d.num_pages = 0; d.max_pages = 0;
+    fill_scalars(d, window, attn_softcap, scale);
+    d.split_tokens = plan.split_tokens;
+    d.n_split_max = plan.n_split;
+    return launch_status(ta03::launch_decode(d, head_dim, plan.gc, false, 1,
+                                             reinterpret_cast<hipStream_t>(stream)),
+                         what);
+}
+
 }  // namespace
 
 extern "C" {
@@ -299,32 +332,36 @@ int attn_decode(const float* q, const void* k, const void* v, float* o, int num_
     if ((long)kv_len * num_kv_heads * head_dim > kMaxElems)
         return fail(ATTN_ERR_INVALID_ARG, "attn_decode: tensor too large");
     const int eff = (sliding_window > 0 && sliding_window < kv_len) ? sliding_window : kv_len;
-    const DecodePlan plan = plan_decode(1, num_heads, num_kv_heads, head_dim, eff, false);
-    const WorkspaceLayout wl = workspace_layout(1, num_heads, num_kv_heads, head_dim, plan);
-    if (plan.n_split > 1) {
-        if (!workspace) return fail(ATTN_ERR_WORKSPACE, "attn_decode: workspace must not be null");
-        if (!aligned(workspace, 256)) return fail(ATTN_ERR_WORKSPACE, "attn_decode: workspace must be 256-byte aligned");
-        if (workspace_bytes < wl.total)
-            return fail(ATTN_ERR_WORKSPACE, "attn_decode: workspace of %zu bytes is smaller than the %zu required",
-                        workspace_bytes, wl.total);
-    }
-    if (plan.n_split > 65535 * 32)
-        return fail(ATTN_ERR_INVALID_ARG, "attn_decode: grid too large");
-    ta03::DecodeParams d{};
-    d.q = q; d.k = k; d.v = v; d.o = o;
-    char* ws = reinterpret_cast<char*>(workspace);
-    d.part_o = reinterpret_cast<float*>(ws + wl.o_off);
-    d.part_m = reinterpret_cast<float*>(ws + wl.m_off);
-    d.part_l = reinterpret_cast<float*>(ws + wl.l_off);
-    d.tickets = reinterpret_cast<uint32_t*>(ws + wl.t_off);
-    d.H = num_heads; d.Hkv = num_kv_heads; d.kv_len = kv_len;
-    d.num_pages = 0; d.max_pages = 0;
-    fill_scalars(d, sliding_window, attn_softcap, scale);
-    d.split_tokens = plan.split_tokens;
-    d.n_split_max = plan.n_split;
-    return launch_status(ta03::launch_decode(d, head_dim, plan.gc, false, 1,
-                                             reinterpret_cast<hipStream_t>(stream)),
-                         "attn_decode");
+    return run_decode_contiguous(q, k, v, o, num_heads, num_kv_heads, head_dim, kv_len, 0, eff,
+                                 sliding_window, attn_softcap, scale, workspace, workspace_bytes,
+                                 stream, "attn_decode");
+}
+
+int attn_decode_ring(const float* q, const void* k, const void* v, float* o, int num_heads,
+                     int num_kv_heads, int head_dim, int ring_len, int total_len, int sliding_window,
+                     float attn_softcap, float scale, void* workspace, size_t workspace_bytes,
+                     void* stream) {
+    TRY(check_ptr(q, "q"));
+    TRY(check_ptr(k, "k"));
+    TRY(check_ptr(v, "v"));
+    TRY(check_ptr(o, "o"));
+    TRY(check_heads(num_heads, num_kv_heads, head_dim));
+    if (ring_len < 1) return fail(ATTN_ERR_INVALID_ARG, "attn_decode_ring: invalid ring_len %d (must be >= 1)", ring_len);
+    if (total_len < 1)
+        return fail(ATTN_ERR_INVALID_ARG, "attn_decode_ring: invalid total_len %d (must be >= 1)", total_len);
+    TRY(check_scalars(sliding_window, attn_softcap, scale));
+    if (sliding_window > ring_len)
+        return fail(ATTN_ERR_INVALID_ARG,
+                    "attn_decode_ring: sliding_window %d exceeds ring_len %d (the ring holds the newest ring_len tokens)",
+                    sliding_window, ring_len);
+    if ((long)ring_len * num_kv_heads * head_dim > kMaxElems)
+        return fail(ATTN_ERR_INVALID_ARG, "attn_decode_ring: tensor too large");
+    // visible keys: the newest E = (W > 0 ? W : ring_len) tokens
+    const int span = sliding_window > 0 ? sliding_window : ring_len;
+    const int eff = total_len < span ? total_len : span;
+    return run_decode_contiguous(q, k, v, o, num_heads, num_kv_heads, head_dim, total_len, ring_len,
+                                 eff, span, attn_softcap, scale, workspace, workspace_bytes, stream,
+                                 "attn_decode_ring");
 }
 
 int attn_decode_paged_q8(const float* q, const int8_t* k_pages, const int8_t* v_pages, const float* k_scales,

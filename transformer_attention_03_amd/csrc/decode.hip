@@ -157,14 +157,24 @@ struct RowCtx {
     const int* pages;      // paged: physical pages of this split, from logical page page0
     int page0;
     int Hkv, kvh, kv_len;
+    int ring, ring_base;   // ring: capacity R, and a multiple of R at or below the split's
+                           // first token (the split spans at most R tokens)
 };
 
+// Ring slot of token t (t - ring_base lies in [0, 2R)).
+__device__ __forceinline__ int ring_slot(const RowCtx& c, int t) {
+    const int tp = t - c.ring_base;
+    return tp >= c.ring ? tp - c.ring : tp;
+}
+
 // Row index (token t of this KV head) in rows of D elements.
-template <bool PAGED>
+template <bool PAGED, bool RING>
 __device__ __forceinline__ size_t row_index(const RowCtx& c, int t) {
     if constexpr (PAGED) {
         const int pg = c.pages[(t >> 4) - c.page0];
         return ((size_t)pg * 16 + (t & 15)) * c.Hkv + c.kvh;
+    } else if constexpr (RING) {
+        return (size_t)c.kvh * c.ring + ring_slot(c, t);
     } else {
         return (size_t)c.kvh * c.kv_len + t;
     }
@@ -219,18 +229,22 @@ __device__ __forceinline__ DmaLane<D, PAGED> dma_lane(int lane, uint32_t rs, int
 
 // DMA the block of tokens tb .. tb+15 into a ring slot (row r of a tile = token tb + r,
 // swizzled chunks; scale areas: row r at 4r, repeated for lanes 16-63).  A full block (and,
-// paged, one whose 16 tokens share a page) takes the uniform-base path; otherwise every
-// lane resolves its own row, and tokens at or past t_end fetch the row of token t_end - 1.
-template <int D, bool PAGED>
+// paged, one whose 16 tokens share a page; ring, one that does not wrap) takes the
+// uniform-base path; otherwise every lane resolves its own row, and tokens at or past t_end
+// fetch the row of token t_end - 1.
+template <int D, bool PAGED, bool RING>
 __device__ __forceinline__ void dma_block(char* slot, const RowCtx& c, const DmaLane<D, PAGED>& L,
                                           int tb, int t_end, int lane) {
     using S = DecShape<D, PAGED>;
-    const bool full = tb + kTB <= t_end && (!PAGED || (tb & 15) == 0);
+    const int slot0 = RING ? ring_slot(c, tb) : 0;
+    const bool full = tb + kTB <= t_end && (!PAGED || (tb & 15) == 0) && (!RING || slot0 + kTB <= c.ring);
     if (full) {
         size_t row0;
         if constexpr (PAGED) {
             const int pg = __builtin_amdgcn_readfirstlane(c.pages[(tb >> 4) - c.page0]);
             row0 = (size_t)pg * 16 * c.Hkv + c.kvh;
+        } else if constexpr (RING) {
+            row0 = (size_t)c.kvh * c.ring + slot0;
         } else {
             row0 = (size_t)c.kvh * c.kv_len + tb;
         }
@@ -250,12 +264,12 @@ __device__ __forceinline__ void dma_block(char* slot, const RowCtx& c, const Dma
         for (int i = 0; i < S::TD; ++i) {
             const int p = 1024 * i + 16 * lane;
             const int r = p / S::RB, cpos = (p % S::RB) / 16;
-            const size_t ri = row_index<PAGED>(c, min(tb + r, t_end - 1));
+            const size_t ri = row_index<PAGED, RING>(c, min(tb + r, t_end - 1));
             dma16(c.kbase + ri * S::RB + 16 * (cpos ^ ksw<S::RPL>(r)), slot + 1024 * i);
             dma16(c.vbase + ri * S::RB + 16 * (cpos ^ vsw<S::RPL>(r)), slot + S::TILE + 1024 * i);
         }
         if constexpr (PAGED) {
-            const size_t ri = row_index<PAGED>(c, min(tb + (lane & 15), t_end - 1));
+            const size_t ri = row_index<PAGED, RING>(c, min(tb + (lane & 15), t_end - 1));
             dma4(c.kscales + ri, slot + 2 * S::TILE);
             dma4(c.vscales + ri, slot + 2 * S::TILE + 256);
         }
@@ -431,8 +445,9 @@ __device__ __forceinline__ void process_block(const char* slot, int tb, int t_en
     }
 }
 
-template <int D, int GC, bool PAGED, bool CAP>
+template <int D, int GC, bool PAGED, bool CAP, bool RING>
 __global__ void __launch_bounds__((DecShape<D, PAGED>::NT)) decode_split_kernel(DecodeParams a) {
+    static_assert(!(PAGED && RING), "a ring cache is contiguous f16");
     using S = DecShape<D, PAGED>;
     constexpr int NW = S::NW;
     constexpr int NT = S::NT;
@@ -529,6 +544,8 @@ __global__ void __launch_bounds__((DecShape<D, PAGED>::NT)) decode_split_kernel(
     c.Hkv = a.Hkv;
     c.kvh = kvh;
     c.kv_len = a.kv_len;
+    c.ring = RING ? a.ring : 0;
+    c.ring_base = RING ? (t_begin / a.ring) * a.ring : 0;
     if constexpr (PAGED) {
         // the physical pages of this split, fetched once (clamped into range)
         const int32_t* ptab = a.page_table + (size_t)b * a.max_pages;
@@ -545,7 +562,7 @@ __global__ void __launch_bounds__((DecShape<D, PAGED>::NT)) decode_split_kernel(
     const DmaLane<D, PAGED> dl = dma_lane<D, PAGED>(lane, (uint32_t)((PAGED ? a.Hkv : 1) * S::RB), a.Hkv);
 #pragma unroll
     for (int k = 0; k < S::RING; ++k)
-        if (k < nb) dma_block<D, PAGED>(ring + k * S::SLOT, c, dl, first + k * STRIDE, t_end, lane);
+        if (k < nb) dma_block<D, PAGED, RING>(ring + k * S::SLOT, c, dl, first + k * STRIDE, t_end, lane);
 
     // ---- Qx: B operand of the QK product.  Column n = lane % 16 holds part n & 1 of head
     // n / 2 (hi, lo); k = d = 32 kc + 8 (lane / 16) + e, with e in the element order of the
@@ -611,7 +628,7 @@ __global__ void __launch_bounds__((DecShape<D, PAGED>::NT)) decode_split_kernel(
         if (kn < nb) {
             // the slot of block k is refilled once this wave's reads of it are done
             wait_lds_reads();
-            dma_block<D, PAGED>(ring + (k % S::RING) * S::SLOT, c, dl, first + kn * STRIDE, t_end, lane);
+            dma_block<D, PAGED, RING>(ring + (k % S::RING) * S::SLOT, c, dl, first + kn * STRIDE, t_end, lane);
         }
     }
 
@@ -749,14 +766,14 @@ __global__ void __launch_bounds__((DecShape<D, PAGED>::NT)) decode_split_kernel(
     }
 }
 
-template <int D, bool PAGED, bool CAP>
+template <int D, bool PAGED, bool CAP, bool RING>
 hipError_t launch_decode_c(const DecodeParams& p, int gc, dim3 grid, hipStream_t st) {
     const dim3 block(DecShape<D, PAGED>::NT);
     switch (gc) {
-        case 1: hipLaunchKernelGGL((decode_split_kernel<D, 1, PAGED, CAP>), grid, block, 0, st, p); break;
-        case 2: hipLaunchKernelGGL((decode_split_kernel<D, 2, PAGED, CAP>), grid, block, 0, st, p); break;
-        case 4: hipLaunchKernelGGL((decode_split_kernel<D, 4, PAGED, CAP>), grid, block, 0, st, p); break;
-        case 8: hipLaunchKernelGGL((decode_split_kernel<D, 8, PAGED, CAP>), grid, block, 0, st, p); break;
+        case 1: hipLaunchKernelGGL((decode_split_kernel<D, 1, PAGED, CAP, RING>), grid, block, 0, st, p); break;
+        case 2: hipLaunchKernelGGL((decode_split_kernel<D, 2, PAGED, CAP, RING>), grid, block, 0, st, p); break;
+        case 4: hipLaunchKernelGGL((decode_split_kernel<D, 4, PAGED, CAP, RING>), grid, block, 0, st, p); break;
+        case 8: hipLaunchKernelGGL((decode_split_kernel<D, 8, PAGED, CAP, RING>), grid, block, 0, st, p); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
@@ -764,8 +781,13 @@ hipError_t launch_decode_c(const DecodeParams& p, int gc, dim3 grid, hipStream_t
 
 template <int D, bool PAGED>
 hipError_t launch_decode_d(const DecodeParams& p, int gc, dim3 grid, hipStream_t st) {
-    return p.softcap > 0.f ? launch_decode_c<D, PAGED, true>(p, gc, grid, st)
-                           : launch_decode_c<D, PAGED, false>(p, gc, grid, st);
+    if constexpr (!PAGED) {
+        if (p.ring > 0)
+            return p.softcap > 0.f ? launch_decode_c<D, false, true, true>(p, gc, grid, st)
+                                   : launch_decode_c<D, false, false, true>(p, gc, grid, st);
+    }
+    return p.softcap > 0.f ? launch_decode_c<D, PAGED, true, false>(p, gc, grid, st)
+                           : launch_decode_c<D, PAGED, false, false>(p, gc, grid, st);
 }
 
 }  // namespace

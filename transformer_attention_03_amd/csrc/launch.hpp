@@ -24,7 +24,8 @@ struct DecodeParams {
     float* part_l;             // [B][H][n_split_max]
     uint32_t* tickets;         // [B][Hkv * head_chunks], zero between calls
     int H, Hkv;
-    int kv_len;                // contiguous cache length (unused when paged)
+    int kv_len;                // contiguous cache length (unused when paged); ring: tokens so far
+    int ring;                  // ring cache capacity in tokens (token t at row t mod ring); 0 = none
     int num_pages, max_pages;
     int window;
     float scale, scale_log2;   // scale and scale * log2(e)
