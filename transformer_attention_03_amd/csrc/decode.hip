@@ -228,7 +228,7 @@ __device__ __forceinline__ DmaLane<D, PAGED> dma_lane(int lane, uint32_t rs, int
 }
 
 // DMA the block of tokens tb .. tb+15 into a ring slot (row r of a tile = token tb + r,
-// swizzled chunks; scale areas: row r at 4r, repeated for lanes 16-63).  A full block (and,
+// swizzled chunks; scale areas: row r at 4r).  A full block (and,
 // paged, one whose 16 tokens share a page; ring, one that does not wrap) takes the
 // uniform-base path; otherwise every lane resolves its own row, and tokens at or past t_end
 // fetch the row of token t_end - 1.
@@ -256,8 +256,11 @@ __device__ __forceinline__ void dma_block(char* slot, const RowCtx& c, const Dma
             dma16s(vb, L.v[i], slot + S::TILE + 1024 * i);
         }
         if constexpr (PAGED) {
-            dma4s(c.kscales + row0, L.sc, slot + 2 * S::TILE);
-            dma4s(c.vscales + row0, L.sc, slot + 2 * S::TILE + 256);
+            // 16 lanes carry the block's 16 scales (the instruction still counts once per wave)
+            if (lane < 16) {
+                dma4s(c.kscales + row0, L.sc, slot + 2 * S::TILE);
+                dma4s(c.vscales + row0, L.sc, slot + 2 * S::TILE + 256);
+            }
         }
     } else {
 #pragma unroll
@@ -269,9 +272,11 @@ __device__ __forceinline__ void dma_block(char* slot, const RowCtx& c, const Dma
             dma16(c.vbase + ri * S::RB + 16 * (cpos ^ vsw<S::RPL>(r)), slot + S::TILE + 1024 * i);
         }
         if constexpr (PAGED) {
-            const size_t ri = row_index<PAGED, RING>(c, min(tb + (lane & 15), t_end - 1));
-            dma4(c.kscales + ri, slot + 2 * S::TILE);
-            dma4(c.vscales + ri, slot + 2 * S::TILE + 256);
+            if (lane < 16) {
+                const size_t ri = row_index<PAGED, RING>(c, min(tb + lane, t_end - 1));
+                dma4(c.kscales + ri, slot + 2 * S::TILE);
+                dma4(c.vscales + ri, slot + 2 * S::TILE + 256);
+            }
         }
     }
 }
