@@ -328,6 +328,70 @@ def test_paged_q8_full_workload(dev, c5_inputs):
     assert maxabs(got, want) < TOL_F16
 
 
+def replay_matches_eager(launch, out, replays=3):
+    """Capture `launch` once in a HIP graph and replay it several times, with eager work and
+    synchronisations in between: every replay equals the eager result bitwise (the split
+    merge's arrival counters reset themselves inside the kernel, with no memset node)."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        launch()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    eager = out.clone()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=side):
+        launch()
+    torch.cuda.synchronize()
+    for _ in range(replays):
+        out.fill_(float("nan"))
+        launch()                 # an eager call between replays
+        torch.cuda.synchronize()
+        out.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager)
+    return eager.cpu().numpy()
+
+
+def test_decode_graph_replays(dev):
+    say("decode graph replays")
+    q, k, v = synth.decode_inputs(synth.seed_of(2) + 91, 32, 8, 128, 4096)
+    qd, kd, vd = to_dev(q, dev), to_dev(k, dev), to_dev(v, dev)
+    o = torch.empty((32, 128), dtype=torch.float32, device=dev)
+    ws = ta.decode_workspace(1, 32, 8, 128, 4096, dev)
+    got = replay_matches_eager(lambda: ta.attn_decode(qd, kd, vd, o, ws, scale=1 / math.sqrt(128)), o)
+    assert maxabs(got, decode_oracle(q, k, v)) < TOL_F16
+
+
+def test_decode_ring_graph_replays(dev):
+    say("decode ring graph replays")
+    H, Hkv, D, R, total = 16, 4, 128, 1024, 2500
+    q, k, v = synth.decode_inputs(synth.seed_of(2) + 92, H, Hkv, D, total)
+    qd = to_dev(q, dev)
+    kd, vd = to_dev(ring_cache(k, total, R, R), dev), to_dev(ring_cache(v, total, R, R), dev)
+    o = torch.empty((H, D), dtype=torch.float32, device=dev)
+    ws = ta.decode_workspace(1, H, Hkv, D, R, dev)
+    got = replay_matches_eager(lambda: ta.attn_decode_ring(qd, kd, vd, o, ws, total_len=total,
+                                                           scale=1 / math.sqrt(D)), o)
+    assert maxabs(got, decode_oracle(q, k[:, total - R:], v[:, total - R:])) < TOL_F16
+
+
+def test_paged_graph_replays(dev):
+    say("paged graph replays")
+    lens = [3000, 77, 1500, 4096]
+    d = synth.paged_inputs(synth.seed_of(5) + 93, 4, 16, 4, 128, lens, n_poison=8)
+    t = paged_to_dev(d, dev)
+    B, H, D = d["q"].shape
+    o = torch.empty((B, H, D), dtype=torch.float32, device=dev)
+    ws = ta.decode_workspace(B, H, 4, D, d["page_table"].shape[1] * 16, dev)
+    got = replay_matches_eager(lambda: ta.attn_decode_paged_q8(
+        t["q"], t["k_pages"], t["v_pages"], t["k_scales"], t["v_scales"], t["page_table"],
+        t["kv_lens"], o, ws, scale=1 / math.sqrt(D)), o)
+    assert maxabs(got, paged_oracle(d)) < TOL_F16
+
+
 def test_paged_permutation_is_bit_identical(dev):
     say("paged permutation bit identity")
     lens = [2000, 1234, 17, 4096]
