@@ -240,11 +240,18 @@ __global__ void __launch_bounds__(64 * NW) fwd_f16_kernel(FwdParams a) {
     DmaLane<D, QB, NW, NS, BN> dl;
     dma_lane_init(dl, a, w, lane);
 
+    // Tiles are visited from a starting point that depends on the query block, so that the
+    // workgroups of one head do not all fetch the same tile at the same moment (each would
+    // then wait for the same cold line); any visiting order gives the same softmax.
+    const int nt = tr.kt1 - tr.kt0;
+    const int rot = nt > 1 ? (int)(((long)qblock * nt) / a.n_qblocks) : 0;
+    auto tile_key = [&](int t) { int u = t - tr.kt0 + rot; u -= u >= nt ? nt : 0; return (tr.kt0 + u) * S::BN; };
+
     // prologue: tiles kt0 .. kt0 + NS - 2 in flight
 #pragma unroll
     for (int st0 = 0; st0 < NS - 1; ++st0)
         if (tr.kt0 + st0 < tr.kt1)
-            f16_dma_tile<D, QB, NW, NS, BN>(a, kg, vg, dl, (tr.kt0 + st0) * S::BN, w, lane, k_lds[st0], v_lds[st0]);
+            f16_dma_tile<D, QB, NW, NS, BN>(a, kg, vg, dl, tile_key(tr.kt0 + st0), w, lane, k_lds[st0], v_lds[st0]);
 
     // ---- Q fragments (B operand of S^T = K Q^T) --------------------------------------------
     half8_t qf[S::QB][S::DC];
@@ -323,12 +330,12 @@ __global__ void __launch_bounds__(64 * NW) fwd_f16_kernel(FwdParams a) {
             const int nxt = kt + NS - 1;
             if (nxt < tr.kt1) {
                 const int sn = (stage + NS - 1) % NS;
-                f16_dma_tile<D, QB, NW, NS, BN>(a, kg, vg, dl, nxt * S::BN, w, lane, k_lds[sn], v_lds[sn]);
+                f16_dma_tile<D, QB, NW, NS, BN>(a, kg, vg, dl, tile_key(nxt), w, lane, k_lds[sn], v_lds[sn]);
             }
         }
         const char* kl = k_lds[stage];
         const char* vl = v_lds[stage];
-        const int ks = kt * S::BN;
+        const int ks = tile_key(kt);
         const bool masked = tile_needs_mask(a, tr, ks, S::BN);
 
         // ---- S^T = K Q^T -----------------------------------------------------------------
