@@ -8,7 +8,8 @@ A step is one call of the workload's entry point over one batch of synthetic inp
 contiguous f16 KV cache (32 query / 8 KV heads, head_dim 128, kv_len 4096); the other
 workloads (f32 causal prefill, f16 windowed+softcapped GQA prefill, f16 vision, batched
 paged int8 decode, f16 chunked prefill against a cache whose length is read on the device,
-and f16 decode over a ring-buffer cache) are measured on the same JSON line under
+f16 decode over a ring-buffer cache, and tiered decode over an int8 paged cold tier plus an
+f16 ring hot tier) are measured on the same JSON line under
 "workloads".
 
 Timing: W untimed steps, then K steps between HIP events recorded on the stream the
@@ -46,7 +47,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="decode_f16",
                     choices=["decode_f16", "prefill_f32", "prefill_f16", "vision_f16",
-                             "decode_paged_q8", "prefill_chunk_f16", "decode_ring_f16", "all"])
+                             "decode_paged_q8", "prefill_chunk_f16", "decode_ring_f16",
+                             "decode_tiered_q8", "all"])
     ap.add_argument("--only-headline", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true",
@@ -236,6 +238,74 @@ class PagedQ8(Workload):
         return [self._oracle_b(b, threads) for b in range(8)]
 
 
+class Tiered(Workload):
+    """Tiered decode of one sequence: 28672 old positions in an int8 paged cold tier
+    (16-token pages placed by a seeded permutation) and the newest 4096 in a 4096-row f16
+    ring (hot tier, seeded start row), 32/8 heads, head_dim 128."""
+    name = "decode_tiered_q8"
+    kind = "hbm"
+    kernel = "decode_tiered_kernel<128, 4, false>"
+
+    def __init__(self, dev, cold=28672, hot=4096, R=4096, hot_start=1234):
+        import numpy as np
+        import torch
+
+        import synth
+        import transformer_attention_03_amd as ta
+        self.ta, self.torch = ta, torch
+        self.cold, self.hot = cold, hot
+        t = synth.tiered_inputs(synth.seed_of(6), 32, 8, 128, cold, hot, R, hot_start, n_poison=64)
+        self.t = t
+        c = t["cold"]
+        dv = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to(dev)
+        self.q, self.pt = dv(t["q"]), dv(c["page_table"][0])
+        per = c["k_pages"].nbytes * 2 + c["k_scales"].nbytes * 2 + t["ring_k"].nbytes * 2
+        self.nc = n_copies(per)
+        first = tuple(dv(x) for x in (t["ring_k"], t["ring_v"], c["k_pages"], c["v_pages"],
+                                       c["k_scales"], c["v_scales"]))
+        self.copies = [first] + [tuple(x.clone() for x in first) for _ in range(self.nc - 1)]
+        self.o = torch.empty((32, 128), dtype=torch.float32, device=dev)
+        self.ws = ta.decode_workspace(1, 32, 8, 128, cold + hot, dev)
+        self.hot_start = hot_start
+        self.desc = {"workload": "tiered single-token decode: 28672 positions in an int8 paged cold "
+                                 "tier (16-token pages, seeded permutation) + the newest 4096 in an "
+                                 "f16 ring [8, 4096, 128], f32 q [32, 128], GQA 32/8, scale 1/sqrt(128)",
+                     "batch": 1, "num_heads": 32, "num_kv_heads": 8, "head_dim": 128,
+                     "cold_len": cold, "hot_len": hot, "hot_window": R, "hot_start": hot_start,
+                     "cold_dtype": "int8", "hot_dtype": "f16", "q_dtype": "f32",
+                     "input_copies": self.nc}
+
+    def step(self, i):
+        hk, hv, kp, vp, ks, vs = self.copies[i % self.nc]
+        self.ta.attn_decode_tiered_q8(self.q, hk, hv, kp, vp, ks, vs, self.pt, self.o, self.ws,
+                                      cold_len=self.cold, hot_len=self.hot, hot_start=self.hot_start,
+                                      scale=1 / math.sqrt(128))
+
+    def units(self):
+        b = (self.cold * 8 * (128 + 128 + 4 + 4) + ((self.cold + 15) // 16) * 4
+             + self.hot * 8 * 128 * 2 * 2 + 2 * 32 * 128 * 4)
+        return b, "bytes"
+
+    def _oracle(self, threads):
+        import numpy as np
+
+        import oracle
+        t, c = self.t, self.t["cold"]
+        k = np.concatenate([oracle.dequant_i8(c["k_q"][0], c["k_s"][0]), t["hot_k"].astype(np.float64)])
+        v = np.concatenate([oracle.dequant_i8(c["v_q"][0], c["v_s"][0]), t["hot_v"].astype(np.float64)])
+        return oracle.attention(t["q"][None, None], k[None], v[None], causal=True,
+                                scale=1 / math.sqrt(128), threads=threads)[0, 0]
+
+    def check(self):
+        import numpy as np
+        self.step(0)
+        self.torch.cuda.synchronize()
+        return float(np.abs(self.o.cpu().numpy() - self._oracle(None)).max())
+
+    def cpu_run(self, threads):
+        return self._oracle(threads)
+
+
 class Forward(Workload):
     """Prefill (token-major) or vision (head-major) forward."""
 
@@ -352,7 +422,7 @@ class Forward(Workload):
 
 
 ALL = ["decode_f16", "prefill_f32", "prefill_f16", "vision_f16", "decode_paged_q8", "prefill_chunk_f16",
-       "decode_ring_f16"]
+       "decode_ring_f16", "decode_tiered_q8"]
 
 
 def make(name, dev):
@@ -362,6 +432,8 @@ def make(name, dev):
         return PagedQ8(dev)
     if name == "decode_ring_f16":
         return DecodeRing(dev)
+    if name == "decode_tiered_q8":
+        return Tiered(dev)
     return Forward(dev, name)
 
 

@@ -186,6 +186,45 @@ int attn_decode_paged_q8(const float *q, const int8_t *k_pages, const int8_t *v_
                          void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * Single-token decode over a tiered cache of one sequence (doppler attention.js:
+ * executeAttentionTieredQuant, with coldLen, hotLen, hotWindow, hotStart; run.js passes
+ * the tiers of a 'tiered' KV cache): the oldest cold_len positions sit in a paged
+ * symmetric-int8 cold tier with separate K and V scales, the newest hot_len positions in an
+ * f16 ring (the hot tier).  One online softmax runs over both tiers.
+ *
+ *   q, o           : float32 [num_heads, head_dim]
+ *   hot_k, hot_v   : float16 [num_kv_heads, hot_window, head_dim]; position p in
+ *                    [cold_len, cold_len + hot_len) lives at row (hot_start + p - cold_len)
+ *                    mod hot_window (the pages give hotStart and hotWindow but print no index
+ *                    formula; this is the plain reading).  Unused if hot_len == 0.
+ *   cold_k_pages,
+ *   cold_v_pages   : int8 [num_pages, page_size, num_kv_heads, head_dim]
+ *   cold_k_scales,
+ *   cold_v_scales  : float32 [num_pages, page_size, num_kv_heads]; value = q8 * scale
+ *   cold_page_table: int32 [max_pages]; logical page i (positions 16 i .. 16 i + 15) ->
+ *                    physical page.  Unused if cold_len == 0.
+ *   page_size      : 16
+ *   The query sits at position cold_len + hot_len - 1 and sees the newest W positions
+ *   (W = sliding_window, 0 = all), across both tiers.  Rows holding other positions, and
+ *   page-table entries past ceil(cold_len / 16), are never read; out-of-range page-table
+ *   entries are clamped into [0, num_pages).
+ *   Requires head_dim in {64, 128} (256: ATTN_ERR_UNSUPPORTED), hot_len <= hot_window,
+ *   0 <= hot_start < hot_window when hot_len > 0, cold_len <= max_pages * page_size, and
+ *   cold_len + hot_len >= 1; otherwise ATTN_ERR_INVALID_ARG before any HIP call.
+ *   workspace: as for attn_decode, sized by attn_decode_workspace_bytes(1, num_heads,
+ *   num_kv_heads, head_dim, cold_len + hot_len).
+ */
+int attn_decode_tiered_q8(const float *q, const void *hot_k, const void *hot_v,
+                          const int8_t *cold_k_pages, const int8_t *cold_v_pages,
+                          const float *cold_k_scales, const float *cold_v_scales,
+                          const int32_t *cold_page_table, float *o,
+                          int num_heads, int num_kv_heads, int head_dim,
+                          int cold_len, int hot_len, int hot_window, int hot_start,
+                          int page_size, int num_pages, int max_pages,
+                          int sliding_window, float attn_softcap, float scale,
+                          void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * Workspace bytes needed by attn_decode (batch = 1) and attn_decode_paged_q8 for the
  * given shape (split partials and arrival counters).  Returns 0 for invalid sizes.
  * Honours the calling thread's split override (attn_set_decode_split).

@@ -15,7 +15,7 @@ Generator (counter based, so any slice can be drawn independently):
   * values are drawn in float64, rounded to float32, then to float16 with
     round-to-nearest-even where a tensor is stored in f16.
   * stream seed = seed_c * 256 + tensor_id, with tensor ids Q=1, K=2, V=3,
-    kv lengths=4, page permutation=5, alternative permutation=6.
+    kv lengths=4, page permutation=5, alternative permutation=6, hot-tier K=7, hot-tier V=8.
 """
 from __future__ import annotations
 
@@ -32,6 +32,7 @@ _M2 = np.uint64(0x94D049BB133111EB)
 _CHUNK = 1 << 22
 
 TID_Q, TID_K, TID_V, TID_KVLEN, TID_PERM, TID_PERM_ALT = 1, 2, 3, 4, 5, 6
+TID_HOT_K, TID_HOT_V = 7, 8
 PAGE = 16
 
 
@@ -277,3 +278,33 @@ def paged_inputs(seed_c, batch, h, hkv, d, kv_lens, n_poison=64, alt_perm=False,
                                           n_poison=n_poison, max_pages=max_pages)
     return dict(q=q, k_q=kq, k_s=ks, v_q=vq, v_s=vs, k_pages=kp, v_pages=vp,
                 k_scales=ksp, v_scales=vsp, page_table=table, kv_lens=kv_lens)
+
+
+def tiered_inputs(seed_c, h, hkv, d, cold_len, hot_len, hot_window, hot_start, n_poison=16):
+    """One sequence of a tiered cache.  Positions [0, cold_len) are the cold tier: drawn,
+    quantised to int8 and paged exactly as paged_inputs does for a batch of one (an empty
+    tier is one poison page).  Positions [cold_len, cold_len + hot_len) are the hot tier:
+    f16 rows [hot_len, hkv, d] (token-major), laid into rings [hkv, hot_window, d] with
+    position p at row (hot_start + p - cold_len) % hot_window; rows holding no position are
+    NaN.  q is f32 [h, d]."""
+    if cold_len > 0:
+        cold = paged_inputs(seed_c, 1, h, hkv, d, [cold_len], n_poison=n_poison)
+    else:
+        cold = dict(q=normal_f32(stream_seed(seed_c, TID_Q), (1, h, d)),
+                    k_q=[np.zeros((0, hkv, d), np.int8)], k_s=[np.zeros((0, hkv), np.float32)],
+                    v_q=[np.zeros((0, hkv, d), np.int8)], v_s=[np.zeros((0, hkv), np.float32)],
+                    k_pages=np.full((1, PAGE, hkv, d), -128, np.int8),
+                    v_pages=np.full((1, PAGE, hkv, d), -128, np.int8),
+                    k_scales=np.full((1, PAGE, hkv), np.nan, np.float32),
+                    v_scales=np.full((1, PAGE, hkv), np.nan, np.float32),
+                    page_table=np.zeros((1, 1), np.int32), kv_lens=np.zeros(1, np.int32))
+    hot_k = normal_f16(stream_seed(seed_c, TID_HOT_K), (hot_len, hkv, d))
+    hot_v = normal_f16(stream_seed(seed_c, TID_HOT_V), (hot_len, hkv, d))
+    ring_k = np.full((hkv, hot_window, d), np.nan, np.float16)
+    ring_v = np.full((hkv, hot_window, d), np.nan, np.float16)
+    rows = (hot_start + np.arange(hot_len)) % hot_window
+    ring_k[:, rows] = np.transpose(hot_k, (1, 0, 2))
+    ring_v[:, rows] = np.transpose(hot_v, (1, 0, 2))
+    return dict(q=cold["q"][0], cold=cold, hot_k=hot_k, hot_v=hot_v, ring_k=ring_k, ring_v=ring_v,
+                cold_len=int(cold_len), hot_len=int(hot_len), hot_start=int(hot_start))
+

@@ -25,7 +25,8 @@ def declared_functions():
 def test_header_declares_the_boundary():
     names = declared_functions()
     for n in ("attn_prefill", "attn_prefill_device_kv_len", "attn_vision", "attn_decode",
-              "attn_decode_ring", "attn_decode_paged_q8", "attn_decode_workspace_bytes",
+              "attn_decode_ring", "attn_decode_paged_q8", "attn_decode_tiered_q8",
+              "attn_decode_workspace_bytes",
               "attn_last_error", "attn_set_decode_split"):
         assert n in names
 
@@ -179,6 +180,43 @@ def paged(**kw):
 def test_paged_validation(kw, code, msg):
     assert paged(**kw) == code
     assert msg in ta.attn_last_error()
+
+
+def tiered(**kw):
+    a = dict(q=P, hk=P, hv=P, kp=P, vp=P, ks=P, vs=P, pt=P, o=P, H=32, Hkv=8, D=128, cold=20000,
+             hot=1000, R=1024, hs=0, ps=16, npg=2000, mp=1300, W=0, cap=0.0, scale=0.088, ws=P,
+             wsb=1 << 30)
+    a.update(kw)
+    return ta.lib().attn_decode_tiered_q8(a["q"], a["hk"], a["hv"], a["kp"], a["vp"], a["ks"],
+                                          a["vs"], a["pt"], a["o"], a["H"], a["Hkv"], a["D"],
+                                          a["cold"], a["hot"], a["R"], a["hs"], a["ps"],
+                                          a["npg"], a["mp"], a["W"], a["cap"], a["scale"],
+                                          a["ws"], a["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,code,msg", [
+    (dict(hk=None), ta.ATTN_ERR_INVALID_ARG, "hot_k must not be null"),
+    (dict(pt=MIS), ta.ATTN_ERR_INVALID_ARG, "cold_page_table must be 16-byte aligned"),
+    (dict(D=256), ta.ATTN_ERR_UNSUPPORTED, "requires head_dim in {64, 128}"),
+    (dict(cold=-1), ta.ATTN_ERR_INVALID_ARG, "must be >= 0"),
+    (dict(cold=0, hot=0), ta.ATTN_ERR_INVALID_ARG, "cold_len + hot_len"),
+    (dict(hot=1025), ta.ATTN_ERR_INVALID_ARG, "hot_len 1025 exceeds hot_window 1024"),
+    (dict(hs=1024), ta.ATTN_ERR_INVALID_ARG, "hot_start 1024"),
+    (dict(cold=20801), ta.ATTN_ERR_INVALID_ARG, "exceeds max_pages * page_size"),
+    (dict(ps=8), ta.ATTN_ERR_UNSUPPORTED, "page_size"),
+    (dict(W=-3), ta.ATTN_ERR_INVALID_ARG, "sliding_window"),
+    (dict(ws=None), ta.ATTN_ERR_WORKSPACE, "workspace must not be null"),
+    (dict(wsb=4096), ta.ATTN_ERR_WORKSPACE, "smaller than"),
+])
+def test_tiered_validation(kw, code, msg):
+    assert tiered(**kw) == code
+    assert msg in ta.attn_last_error()
+
+
+def test_tiered_tiers_may_be_empty_and_null():
+    """A tier with no positions needs no pointers: validation passes up to the workspace."""
+    assert tiered(hot=0, hk=None, hv=None, ws=None) == ta.ATTN_ERR_WORKSPACE
+    assert tiered(cold=0, kp=None, vp=None, ks=None, vs=None, pt=None, ws=None) == ta.ATTN_ERR_WORKSPACE
 
 
 def test_workspace_bytes():

@@ -392,6 +392,112 @@ def test_paged_graph_replays(dev):
     assert maxabs(got, paged_oracle(d)) < TOL_F16
 
 
+# =============================================================================================
+# tiered decode: int8 paged cold tier + f16 ring hot tier, one online softmax
+# =============================================================================================
+
+def run_tiered(dev, t, W=0, cap=0.0, ws=None):
+    c = t["cold"]
+    H, D = t["q"].shape
+    Hkv = t["ring_k"].shape[0]
+    d = {k: to_dev(v, dev) for k, v in (("q", t["q"]), ("hk", t["ring_k"]), ("hv", t["ring_v"]),
+                                          ("kp", c["k_pages"]), ("vp", c["v_pages"]),
+                                          ("ks", c["k_scales"]), ("vs", c["v_scales"]),
+                                          ("pt", c["page_table"][0]))}
+    o = torch.empty((H, D), dtype=torch.float32, device=dev)
+    if ws is None:
+        ws = ta.decode_workspace(1, H, Hkv, D, t["cold_len"] + t["hot_len"], dev)
+    ta.attn_decode_tiered_q8(d["q"], d["hk"], d["hv"], d["kp"], d["vp"], d["ks"], d["vs"], d["pt"],
+                             o, ws, cold_len=t["cold_len"], hot_len=t["hot_len"],
+                             hot_start=t["hot_start"], scale=1 / math.sqrt(D), sliding_window=W,
+                             attn_softcap=cap)
+    torch.cuda.synchronize()
+    assert int(ws[-256:].sum().item()) == 0
+    return o.cpu().numpy()
+
+
+def tiered_oracle(t, W=0, cap=0.0):
+    """Oracle over the logical sequence: the dequantised cold rows followed by the hot f16
+    rows (never reads the page table or the ring)."""
+    c = t["cold"]
+    H, D = t["q"].shape
+    k = np.concatenate([oracle.dequant_i8(c["k_q"][0], c["k_s"][0]), t["hot_k"].astype(np.float64)])
+    v = np.concatenate([oracle.dequant_i8(c["v_q"][0], c["v_s"][0]), t["hot_v"].astype(np.float64)])
+    return oracle.attention(t["q"][None, None], k[None], v[None], causal=True, window=W, softcap=cap,
+                            scale=1 / math.sqrt(D))[0, 0]
+
+
+def poison_outside_window(t, W):
+    """NaN in every stored row of a position the window hides (cold: its K and V scales; hot:
+    its ring rows), so that a read of one shows up in the output."""
+    total = t["cold_len"] + t["hot_len"]
+    lo = max(0, total - W) if W > 0 else 0
+    c = t["cold"]
+    for p in range(min(lo, t["cold_len"])):
+        pg = c["page_table"][0][p // 16]
+        c["k_scales"][pg, p % 16] = np.nan
+        c["v_scales"][pg, p % 16] = np.nan
+    R = t["ring_k"].shape[1]
+    for p in range(t["cold_len"], lo):
+        r = (t["hot_start"] + p - t["cold_len"]) % R
+        t["ring_k"][:, r] = np.nan
+        t["ring_v"][:, r] = np.nan
+
+
+@pytest.mark.parametrize("H,Hkv,D,cold,hot,R,hs,W,cap", [
+    (8, 2, 128, 1000, 300, 512, 100, 0, 0.0),
+    (32, 8, 128, 5000, 512, 512, 0, 0, 0.0),      # full hot ring
+    (8, 2, 64, 37, 5, 64, 60, 0, 0.0),            # the hot tier wraps the ring end
+    (4, 4, 64, 0, 50, 64, 20, 0, 0.0),            # empty cold tier
+    (8, 2, 128, 777, 0, 16, 0, 0, 0.0),           # empty hot tier
+    (8, 2, 128, 3000, 400, 500, 123, 1000, 0.0),  # window over both tiers
+    (8, 2, 128, 3000, 400, 500, 123, 300, 0.0),   # window inside the hot tier
+    (8, 8, 128, 2000, 256, 256, 7, 0, 30.0),      # softcap
+    (16, 2, 128, 17, 1, 8, 3, 0, 0.0),            # a few tokens
+    (24, 4, 64, 9000, 1000, 1024, 1000, 0, 0.0),  # six query heads per KV head
+])
+def test_tiered_q8(dev, H, Hkv, D, cold, hot, R, hs, W, cap):
+    say("tiered H=%d Hkv=%d D=%d cold=%d hot=%d R=%d hs=%d W=%d cap=%g" % (H, Hkv, D, cold, hot, R, hs, W, cap))
+    t = synth.tiered_inputs(synth.seed_of(6) + cold + 7 * hot, H, Hkv, D, cold, hot, R, hs, n_poison=5)
+    if W > 0:
+        poison_outside_window(t, W)
+    got = run_tiered(dev, t, W, cap)
+    want = tiered_oracle(t, W, cap)
+    assert np.all(np.isfinite(got))
+    assert maxabs(got, want) < TOL_F16
+    # int8 and f16 rows enter the products exactly: f32-level agreement
+    assert maxabs(got, want) < 5e-5 * np.abs(want).max()
+
+
+def test_tiered_split_sizes_agree(dev):
+    say("tiered split sizes")
+    t = synth.tiered_inputs(synth.seed_of(6) + 31, 8, 2, 128, 2500, 700, 1000, 900, n_poison=5)
+    want = tiered_oracle(t)
+    try:
+        for ts in (16, 48, 256, 1024, 4096):
+            ta.attn_set_decode_split(ts)
+            got = run_tiered(dev, t)
+            assert maxabs(got, want) < 5e-5 * np.abs(want).max(), ts
+    finally:
+        ta.attn_set_decode_split(0)
+
+
+def test_tiered_graph_replays(dev):
+    say("tiered graph replays")
+    t = synth.tiered_inputs(synth.seed_of(6) + 33, 16, 4, 128, 3000, 600, 1024, 500, n_poison=5)
+    c = t["cold"]
+    d = {k: to_dev(v, dev) for k, v in (("q", t["q"]), ("hk", t["ring_k"]), ("hv", t["ring_v"]),
+                                          ("kp", c["k_pages"]), ("vp", c["v_pages"]),
+                                          ("ks", c["k_scales"]), ("vs", c["v_scales"]),
+                                          ("pt", c["page_table"][0]))}
+    o = torch.empty((16, 128), dtype=torch.float32, device=dev)
+    ws = ta.decode_workspace(1, 16, 4, 128, 3600, dev)
+    got = replay_matches_eager(lambda: ta.attn_decode_tiered_q8(
+        d["q"], d["hk"], d["hv"], d["kp"], d["vp"], d["ks"], d["vs"], d["pt"], o, ws, cold_len=3000,
+        hot_len=600, hot_start=500, scale=1 / math.sqrt(128)), o)
+    assert maxabs(got, tiered_oracle(t)) < 5e-5 * np.abs(tiered_oracle(t)).max()
+
+
 def test_paged_permutation_is_bit_identical(dev):
     say("paged permutation bit identity")
     lens = [2000, 1234, 17, 4096]

@@ -13,7 +13,7 @@ import math
 import os
 
 __all__ = [
-    "AttnError", "lib", "attn_prefill", "attn_vision", "attn_decode", "attn_decode_paged_q8",
+    "AttnError", "lib", "attn_prefill", "attn_vision", "attn_decode", "attn_decode_paged_q8", "attn_decode_tiered_q8",
     "attn_decode_workspace_bytes", "attn_set_decode_split", "attn_last_error", "decode_workspace",
     "ATTN_OK", "ATTN_ERR_INVALID_ARG", "ATTN_ERR_UNSUPPORTED", "ATTN_ERR_WORKSPACE",
     "ATTN_ERR_LAUNCH", "ATTN_F32", "ATTN_F16", "LIB_PATH",
@@ -48,13 +48,16 @@ def lib() -> ctypes.CDLL:
         L.attn_decode_ring.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, f, f, vp, sz, vp]
         L.attn_decode_paged_q8.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i,
                                            f, f, vp, sz, vp]
+        L.attn_decode_tiered_q8.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i,
+                                            i, i, i, f, f, vp, sz, vp]
         L.attn_decode_workspace_bytes.argtypes = [i, i, i, i, i]
         L.attn_decode_workspace_bytes.restype = sz
         L.attn_set_decode_split.argtypes = [i]
         L.attn_last_error.argtypes = []
         L.attn_last_error.restype = ctypes.c_char_p
         for name in ("attn_prefill", "attn_prefill_device_kv_len", "attn_vision", "attn_decode",
-                     "attn_decode_ring", "attn_decode_paged_q8", "attn_set_decode_split"):
+                     "attn_decode_ring", "attn_decode_paged_q8", "attn_decode_tiered_q8",
+                     "attn_set_decode_split"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -203,3 +206,31 @@ def attn_decode_paged_q8(q, k_pages, v_pages, k_scales, v_scales, page_table, kv
         _ptr(q), _ptr(k_pages), _ptr(v_pages), _ptr(k_scales), _ptr(v_scales), _ptr(page_table),
         _ptr(kv_lens), _ptr(o), B, H, Hkv, D, ps, P, page_table.shape[1], int(sliding_window),
         float(attn_softcap), float(scale), _ptr(workspace), ws_bytes, _stream(q, stream)))
+
+
+def attn_decode_tiered_q8(q, hot_k, hot_v, cold_k_pages, cold_v_pages, cold_k_scales,
+                          cold_v_scales, cold_page_table, o, workspace, *, cold_len: int,
+                          hot_len: int, hot_start: int, scale: float, sliding_window: int = 0,
+                          attn_softcap: float = 0.0, stream=None):
+    """q, o: float32 [num_heads, head_dim]; hot_k, hot_v: float16 ring [num_kv_heads,
+    hot_window, head_dim] holding position p >= cold_len at row (hot_start + p - cold_len) %
+    hot_window; cold pages int8 [num_pages, 16, num_kv_heads, head_dim], scales float32
+    [num_pages, 16, num_kv_heads], page table int32 [max_pages] for positions < cold_len."""
+    _need_contig(q, hot_k, hot_v, cold_k_pages, cold_v_pages, cold_k_scales, cold_v_scales,
+                 cold_page_table, o)
+    H, D = q.shape
+    Hkv, R, Dk = hot_k.shape
+    P, ps, Hkv2, Dc = cold_k_pages.shape
+    if Dk != D or Dc != D or Hkv2 != Hkv or hot_v.shape != hot_k.shape or o.shape != q.shape:
+        raise ValueError("shape mismatch")
+    if cold_v_pages.shape != cold_k_pages.shape or cold_k_scales.shape != (P, ps, Hkv) or \
+            cold_v_scales.shape != (P, ps, Hkv) or cold_page_table.dim() != 1:
+        raise ValueError("cold tier: pages [P, 16, Hkv, D], scales [P, 16, Hkv], table [max_pages]")
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(lib().attn_decode_tiered_q8(
+        _ptr(q), _ptr(hot_k), _ptr(hot_v), _ptr(cold_k_pages), _ptr(cold_v_pages),
+        _ptr(cold_k_scales), _ptr(cold_v_scales), _ptr(cold_page_table), _ptr(o), H, Hkv, D,
+        int(cold_len), int(hot_len), R, int(hot_start), ps, P, cold_page_table.shape[0],
+        int(sliding_window), float(attn_softcap), float(scale), _ptr(workspace), ws_bytes,
+        _stream(q, stream)))
+

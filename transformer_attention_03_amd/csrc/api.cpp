@@ -150,14 +150,21 @@ WorkspaceLayout workspace_layout(int batch, int num_heads, int num_kv_heads, int
     return w;
 }
 
-size_t workspace_bytes_for(int batch, int num_heads, int num_kv_heads, int head_dim, int max_len) {
-    size_t best = 0;
+// Split partials per (sequence, head) that a workspace sized for max_len holds: the larger
+// of the contiguous and paged plans, and at least two (a tiered cache has two tiers).
+int workspace_row_splits(int batch, int num_heads, int num_kv_heads, int head_dim, int max_len) {
+    int n = 2;
     for (bool paged : {false, true}) {
         const DecodePlan p = plan_decode(batch, num_heads, num_kv_heads, head_dim, max_len, paged);
-        const size_t t = workspace_layout(batch, num_heads, num_kv_heads, head_dim, p).total;
-        if (t > best) best = t;
+        if (p.n_split > n) n = p.n_split;
     }
-    return best;
+    return n;
+}
+
+size_t workspace_bytes_for(int batch, int num_heads, int num_kv_heads, int head_dim, int max_len) {
+    DecodePlan p = plan_decode(batch, num_heads, num_kv_heads, head_dim, max_len, false);
+    p.n_split = workspace_row_splits(batch, num_heads, num_kv_heads, head_dim, max_len);
+    return workspace_layout(batch, num_heads, num_kv_heads, head_dim, p).total;
 }
 
 const float kLog2e = 1.4426950408889634f;
@@ -430,6 +437,117 @@ int attn_decode_paged_q8(const float* q, const int8_t* k_pages, const int8_t* v_
     return launch_status(ta03::launch_decode(d, head_dim, plan.gc, true, batch,
                                              reinterpret_cast<hipStream_t>(stream)),
                          "attn_decode_paged_q8");
+}
+
+int attn_decode_tiered_q8(const float* q, const void* hot_k, const void* hot_v, const int8_t* cold_k_pages,
+                          const int8_t* cold_v_pages, const float* cold_k_scales, const float* cold_v_scales,
+                          const int32_t* cold_page_table, float* o, int num_heads, int num_kv_heads, int head_dim,
+                          int cold_len, int hot_len, int hot_window, int hot_start, int page_size, int num_pages,
+                          int max_pages, int sliding_window, float attn_softcap, float scale, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+    const char* what = "attn_decode_tiered_q8";
+    TRY(check_ptr(q, "q"));
+    TRY(check_ptr(o, "o"));
+    TRY(check_heads(num_heads, num_kv_heads, head_dim));
+    if (head_dim == 256)
+        return fail(ATTN_ERR_UNSUPPORTED, "%s: head_dim 256 is not built; requires head_dim in {64, 128}", what);
+    TRY(check_scalars(sliding_window, attn_softcap, scale));
+    if (cold_len < 0 || hot_len < 0)
+        return fail(ATTN_ERR_INVALID_ARG, "%s: cold_len (%d) and hot_len (%d) must be >= 0", what, cold_len, hot_len);
+    if ((long)cold_len + hot_len < 1 || (long)cold_len + hot_len > 0x7fffffffL - 16)
+        return fail(ATTN_ERR_INVALID_ARG, "%s: cold_len + hot_len must be in [1, 2^31 - 17]", what);
+    if (hot_len > 0) {
+        TRY(check_ptr(hot_k, "hot_k"));
+        TRY(check_ptr(hot_v, "hot_v"));
+        if (hot_window < hot_len)
+            return fail(ATTN_ERR_INVALID_ARG, "%s: hot_len %d exceeds hot_window %d", what, hot_len, hot_window);
+        if (hot_start < 0 || hot_start >= hot_window)
+            return fail(ATTN_ERR_INVALID_ARG, "%s: hot_start %d must be in [0, hot_window %d)", what, hot_start,
+                        hot_window);
+        if ((long)hot_window * num_kv_heads * head_dim > kMaxElems)
+            return fail(ATTN_ERR_INVALID_ARG, "%s: hot tier too large", what);
+    }
+    if (cold_len > 0) {
+        TRY(check_ptr(cold_k_pages, "cold_k_pages"));
+        TRY(check_ptr(cold_v_pages, "cold_v_pages"));
+        TRY(check_ptr(cold_k_scales, "cold_k_scales"));
+        TRY(check_ptr(cold_v_scales, "cold_v_scales"));
+        TRY(check_ptr(cold_page_table, "cold_page_table"));
+        if (page_size != 16)
+            return fail(ATTN_ERR_UNSUPPORTED, "%s: page_size %d is not built; requires page_size 16", what, page_size);
+        if (num_pages < 1 || max_pages < 1)
+            return fail(ATTN_ERR_INVALID_ARG, "%s: num_pages and max_pages must be >= 1", what);
+        if ((long)max_pages * page_size < cold_len)
+            return fail(ATTN_ERR_INVALID_ARG, "%s: cold_len %d exceeds max_pages * page_size = %ld", what, cold_len,
+                        (long)max_pages * page_size);
+        if ((long)num_pages * page_size * num_kv_heads * head_dim > kMaxElems)
+            return fail(ATTN_ERR_INVALID_ARG, "%s: cold tier too large", what);
+    }
+    const int total = cold_len + hot_len;
+    const int k_lo = (sliding_window > 0 && total > sliding_window) ? total - sliding_window : 0;
+    const int cold_vis = cold_len > k_lo ? cold_len - k_lo : 0;
+    const int hot_vis = total - (k_lo > cold_len ? k_lo : cold_len);
+    // One split size for both tiers: about one round of resident workgroups (the kernel's
+    // LDS is sized for the f16 body, the larger one), in whole rounds of 16-token blocks per
+    // wave, at most the paged page-slice limit; the thread's split override wins.  The split
+    // count must fit the workspace row that attn_decode_workspace_bytes(1, ...,
+    // cold_len + hot_len) sized.
+    DecodePlan plan = plan_decode(1, num_heads, num_kv_heads, head_dim, cold_vis + hot_vis, false);
+    const int stride = workspace_row_splits(1, num_heads, num_kv_heads, head_dim, total);
+    const int max_split = ta03::decode_max_split_tokens_paged();
+    int ts = g_split_override;
+    if (ts <= 0) {
+        int per_cu = ta03::decode_workgroups_per_cu(head_dim, false);
+        const int per_cu_paged = ta03::decode_workgroups_per_cu(head_dim, true);
+        if (per_cu_paged < per_cu) per_cu = per_cu_paged;
+        const long chunks = (long)num_kv_heads * plan.nch;
+        const long n_target = (256L * per_cu + chunks - 1) / chunks;
+        const int unit = ta03::decode_waves(head_dim, true) * ta03::decode_tokens_per_block();
+        const long per = ((long)cold_vis + hot_vis + n_target - 1) / n_target;
+        ts = (int)(((per + unit - 1) / unit) * unit);
+    }
+    if (ts > max_split) ts = max_split;
+    auto splits = [&](int t) { return (cold_vis + t - 1) / t + (hot_vis + t - 1) / t; };
+    while (splits(ts) > stride && ts < max_split) ts += 16;
+    if (splits(ts) > stride)
+        return fail(ATTN_ERR_UNSUPPORTED, "%s: %d splits needed but the workspace row holds %d", what, splits(ts),
+                    stride);
+    plan.n_split = stride;
+    const WorkspaceLayout wl = workspace_layout(1, num_heads, num_kv_heads, head_dim, plan);
+    if (!workspace) return fail(ATTN_ERR_WORKSPACE, "%s: workspace must not be null", what);
+    if (!aligned(workspace, 256)) return fail(ATTN_ERR_WORKSPACE, "%s: workspace must be 256-byte aligned", what);
+    if (workspace_bytes < wl.total)
+        return fail(ATTN_ERR_WORKSPACE, "%s: workspace of %zu bytes is smaller than the %zu required", what,
+                    workspace_bytes, wl.total);
+    if ((long)num_kv_heads * plan.nch > 65535) return fail(ATTN_ERR_INVALID_ARG, "%s: grid too large", what);
+    ta03::DecodeParams d{};
+    d.q = q;
+    d.k = cold_k_pages; d.v = cold_v_pages;
+    d.k_scales = cold_k_scales; d.v_scales = cold_v_scales;
+    d.page_table = cold_page_table; d.o = o;
+    char* ws = reinterpret_cast<char*>(workspace);
+    d.part_o = reinterpret_cast<float*>(ws + wl.o_off);
+    d.part_m = reinterpret_cast<float*>(ws + wl.m_off);
+    d.part_l = reinterpret_cast<float*>(ws + wl.l_off);
+    d.tickets = reinterpret_cast<uint32_t*>(ws + wl.t_off);
+    d.H = num_heads; d.Hkv = num_kv_heads;
+    d.kv_len = total;
+    d.ring = hot_len > 0 ? hot_window : 1;
+    d.num_pages = num_pages; d.max_pages = max_pages;
+    fill_scalars(d, sliding_window, attn_softcap, scale);
+    d.split_tokens = ts;
+    d.n_split_max = stride;
+    d.batch = 1;
+    d.hot_k = hot_k; d.hot_v = hot_v;
+    // position p of the hot tier lives at row (hot_start + p - cold_len) mod hot_window
+    d.ring_off = hot_len > 0 ? (int)((((long)hot_start - cold_len) % hot_window + hot_window) % hot_window) : 0;
+    d.tier_cold_len = cold_len;
+    d.tier_cold_splits = (cold_vis + ts - 1) / ts;
+    d.tier_k_lo = k_lo;
+    d.tier_cold_tokens = ts;
+    return launch_status(ta03::launch_decode_tiered(d, head_dim, plan.gc, splits(ts),
+                                                    reinterpret_cast<hipStream_t>(stream)),
+                         what);
 }
 
 const char* attn_last_error(void) { return g_err; }

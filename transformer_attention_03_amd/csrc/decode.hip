@@ -450,107 +450,45 @@ __device__ __forceinline__ void process_block(const char* slot, int tb, int t_en
     }
 }
 
+// Where a split's K/V rows come from: the cache (or tier) pointers, and for a ring its
+// capacity and index offset (position t lives at row (t + ring_off) mod ring).
+struct TierSrc {
+    const void* k;
+    const void* v;
+    const float* ks;
+    const float* vs;
+    int ring, ring_off;
+};
+
+// One split: stream tokens [t_begin, t_end) of KV head kvh through the waves, merge the
+// waves, and either write the output (a single split) or publish the split's partial
+// (m, l, o) for the last-arriving workgroup.  LDS is the caller's, so that one kernel can
+// host splits of two cache layouts.
 template <int D, int GC, bool PAGED, bool CAP, bool RING>
-__global__ void __launch_bounds__((DecShape<D, PAGED>::NT)) decode_split_kernel(DecodeParams a) {
-    static_assert(!(PAGED && RING), "a ring cache is contiguous f16");
+__device__ __forceinline__ void split_partial(const DecodeParams& a, const TierSrc& src, char* rings,
+                                              float (*lds_m)[GC], float (*lds_l)[GC], int* lds_pages,
+                                              half8_t (*lds_qx)[64], float (*lds_qs)[64], int b,
+                                              int split, int n_live, int t_begin, int t_end, int kvh,
+                                              int h0) {
     using S = DecShape<D, PAGED>;
     constexpr int NW = S::NW;
     constexpr int NT = S::NT;
-    static_assert(GC >= 1 && GC <= 8, "heads per workgroup");
-    // per-wave DMA rings; the wave-merge buffer lds_o reuses this memory afterwards
-    __shared__ __attribute__((aligned(1024))) char rings[NW * S::WAVE_LDS];
-    __shared__ float lds_m[NW][GC];
-    __shared__ float lds_l[NW][GC];
-    __shared__ int lds_pages[PAGED ? kMaxSplitTokens / 16 + 1 : 1];
-    __shared__ int lds_last;
-    __shared__ half8_t lds_qx[S::KC][64];
-    __shared__ float lds_qs[S::KC][64];
-    float(*lds_o)[GC][D] = reinterpret_cast<float(*)[GC][D]>(rings);                    // [NW][GC][D]
-    static_assert(sizeof(float) * NW * GC * D <= NW * S::WAVE_LDS, "merge buffer fits in the rings");
-
     const int lane = threadIdx.x & 63;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int G = a.H / a.Hkv;
-    const int nch = G / GC;
-    const int kvh = blockIdx.y / nch;
-    const int h0 = kvh * G + (blockIdx.y % nch) * GC;
-
-    // ---- key range of this sequence, and of this split --------------------------------
-    int b, split, n_live, t_begin, t_end, L;
-    if constexpr (PAGED) {
-        // Balanced splits over the whole batch: workgroup x of this head chunk takes split s
-        // of sequence b, where sequence i gets lb_i = ceil(len_i / kMaxSplitTokens) splits
-        // plus its share, by length, of the remaining workgroups (at most one block round per
-        // wave less than a split).  Every workgroup derives the same assignment from kv_lens.
-        const int max_len = a.max_pages * 16;
-        auto eff_of = [&](int li) {
-            const bool valid = li >= 1 && li <= max_len;
-            return valid ? ((a.window > 0 && li > a.window) ? a.window : li) : 0;
-        };
-        long tot = 0;
-        int lb_sum = 0;
-        for (int i = 0; i < a.batch; ++i) {
-            const int e = eff_of(a.kv_lens[i]);
-            tot += e;
-            lb_sum += e > 0 ? (e + kMaxSplitTokens - 1) / kMaxSplitTokens : 1;
-        }
-        const int extra = max(0, (int)gridDim.x - lb_sum);
-        const int p = blockIdx.x;
-        int cum = 0, nb_b = 0;
-        b = -1;
-        for (int i = 0; i < a.batch; ++i) {
-            const int e = eff_of(a.kv_lens[i]);
-            const int lb = e > 0 ? (e + kMaxSplitTokens - 1) / kMaxSplitTokens : 1;
-            int n = lb + (tot > 0 ? (int)((long)extra * e / tot) : 0);
-            n = min(n, max(lb, (e + NW * kTB - 1) / (NW * kTB)));
-            n = min(n, a.n_split_max);
-            if (p < cum + n) {
-                b = i;
-                nb_b = n;
-                break;
-            }
-            cum += n;
-        }
-        if (b < 0) return;                        // more workgroups than splits
-        split = p - cum;
-        L = a.kv_lens[b];
-        if (L < 1 || L > max_len) {
-            // out of contract: the row becomes NaN; nothing else is read
-            if (split == 0)
-                for (int i = threadIdx.x; i < GC * D; i += NT)
-                    a.o[((size_t)b * a.H + h0 + i / D) * D + (i % D)] = __builtin_nanf("");
-            return;
-        }
-        const int k_lo = (a.window > 0 && L > a.window) ? L - a.window : 0;
-        const int eff = L - k_lo;
-        const int tsplit = (((eff + nb_b - 1) / nb_b) + 15) & ~15;   // <= kMaxSplitTokens
-        n_live = (eff + tsplit - 1) / tsplit;
-        if (split >= n_live) return;
-        t_begin = k_lo + split * tsplit;
-        t_end = min(L, t_begin + tsplit);
-    } else {
-        split = blockIdx.x;
-        b = blockIdx.z;
-        L = a.kv_len;
-        const int k_lo = (a.window > 0 && L > a.window) ? L - a.window : 0;
-        n_live = (L - k_lo + a.split_tokens - 1) / a.split_tokens;
-        if (split >= n_live) return;
-        t_begin = k_lo + split * a.split_tokens;
-        t_end = min(L, t_begin + a.split_tokens);
-    }
+    float(*lds_o)[GC][D] = reinterpret_cast<float(*)[GC][D]>(rings);                    // [NW][GC][D]
 
     RowCtx c;
-    c.kbase = reinterpret_cast<const char*>(a.k);
-    c.vbase = reinterpret_cast<const char*>(a.v);
-    c.kscales = a.k_scales;
-    c.vscales = a.v_scales;
+    c.kbase = reinterpret_cast<const char*>(src.k);
+    c.vbase = reinterpret_cast<const char*>(src.v);
+    c.kscales = src.ks;
+    c.vscales = src.vs;
     c.pages = lds_pages;
     c.page0 = t_begin >> 4;
     c.Hkv = a.Hkv;
     c.kvh = kvh;
     c.kv_len = a.kv_len;
-    c.ring = RING ? a.ring : 0;
-    c.ring_base = RING ? (t_begin / a.ring) * a.ring : 0;
+    c.ring = RING ? src.ring : 0;
+    c.ring_base = RING ? ((t_begin + src.ring_off) / src.ring) * src.ring - src.ring_off : 0;
     if constexpr (PAGED) {
         // the physical pages of this split, fetched once (clamped into range)
         const int32_t* ptab = a.page_table + (size_t)b * a.max_pages;
@@ -686,8 +624,16 @@ __global__ void __launch_bounds__((DecShape<D, PAGED>::NT)) decode_split_kernel(
             }
         }
     }
-    if (n_live == 1) return;
+}
 
+// The last-arriving workgroup of a (sequence, head chunk) merges its n_live split partials
+// (log-sum-exp), CS splits at a time through LDS.
+template <int D, int GC, int NT, int CS>
+__device__ __forceinline__ void merge_splits(const DecodeParams& a, char* rings, int* lds_last, int b,
+                                             int h0, int n_live) {
+    const int lane = threadIdx.x & 63;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const size_t part_base = (size_t)b * a.H + h0;
     // ---- last-arriving workgroup merges all splits of this (sequence, head chunk) --------
     // The partials are device-scope stores (written through the XCD's L2) and every
     // thread waits for its stores to complete before the barrier, so when the counter is
@@ -700,16 +646,15 @@ __global__ void __launch_bounds__((DecShape<D, PAGED>::NT)) decode_split_kernel(
         const uint32_t prev = __hip_atomic_fetch_add(ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         const int last = (prev == (uint32_t)(n_live - 1));
         if (last) __hip_atomic_store(ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        lds_last = last;
+        *lds_last = last;
     }
     __syncthreads();
-    if (!lds_last) return;
+    if (!*lds_last) return;
 
     // The split partials (device-scope data) are pulled into LDS by DMA, CS splits at a
     // time, and folded per (head, d) pair into a running maximum, weighted sum and
     // normaliser.  Compact loops: this code runs once per (sequence, head chunk), on a
     // compute unit that has not executed it before.
-    constexpr int CS = merge_chunk<D, GC, PAGED>();
     float* lds_po = reinterpret_cast<float*>(rings);          // [GC][CS][D]
     float* lds_pm = lds_po + GC * CS * D;                      // [GC][CS]
     float* lds_pl = lds_pm + GC * CS;                          // [GC][CS]
@@ -771,6 +716,154 @@ __global__ void __launch_bounds__((DecShape<D, PAGED>::NT)) decode_split_kernel(
     }
 }
 
+template <int D, int GC, bool PAGED, bool CAP, bool RING>
+__global__ void __launch_bounds__((DecShape<D, PAGED>::NT)) decode_split_kernel(DecodeParams a) {
+    static_assert(!(PAGED && RING), "a ring cache is contiguous f16");
+    using S = DecShape<D, PAGED>;
+    constexpr int NW = S::NW;
+    constexpr int NT = S::NT;
+    static_assert(GC >= 1 && GC <= 8, "heads per workgroup");
+    // per-wave DMA rings; the wave-merge buffer lds_o reuses this memory afterwards
+    __shared__ __attribute__((aligned(1024))) char rings[NW * S::WAVE_LDS];
+    __shared__ float lds_m[NW][GC];
+    __shared__ float lds_l[NW][GC];
+    __shared__ int lds_pages[PAGED ? kMaxSplitTokens / 16 + 1 : 1];
+    __shared__ int lds_last;
+    __shared__ half8_t lds_qx[S::KC][64];
+    __shared__ float lds_qs[S::KC][64];
+    static_assert(sizeof(float) * NW * GC * D <= NW * S::WAVE_LDS, "merge buffer fits in the rings");
+
+    const int lane = threadIdx.x & 63;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int G = a.H / a.Hkv;
+    const int nch = G / GC;
+    const int kvh = blockIdx.y / nch;
+    const int h0 = kvh * G + (blockIdx.y % nch) * GC;
+
+    // ---- key range of this sequence, and of this split --------------------------------
+    int b, split, n_live, t_begin, t_end, L;
+    if constexpr (PAGED) {
+        // Balanced splits over the whole batch: workgroup x of this head chunk takes split s
+        // of sequence b, where sequence i gets lb_i = ceil(len_i / kMaxSplitTokens) splits
+        // plus its share, by length, of the remaining workgroups (at most one block round per
+        // wave less than a split).  Every workgroup derives the same assignment from kv_lens.
+        const int max_len = a.max_pages * 16;
+        auto eff_of = [&](int li) {
+            const bool valid = li >= 1 && li <= max_len;
+            return valid ? ((a.window > 0 && li > a.window) ? a.window : li) : 0;
+        };
+        long tot = 0;
+        int lb_sum = 0;
+        for (int i = 0; i < a.batch; ++i) {
+            const int e = eff_of(a.kv_lens[i]);
+            tot += e;
+            lb_sum += e > 0 ? (e + kMaxSplitTokens - 1) / kMaxSplitTokens : 1;
+        }
+        const int extra = max(0, (int)gridDim.x - lb_sum);
+        const int p = blockIdx.x;
+        int cum = 0, nb_b = 0;
+        b = -1;
+        for (int i = 0; i < a.batch; ++i) {
+            const int e = eff_of(a.kv_lens[i]);
+            const int lb = e > 0 ? (e + kMaxSplitTokens - 1) / kMaxSplitTokens : 1;
+            int n = lb + (tot > 0 ? (int)((long)extra * e / tot) : 0);
+            n = min(n, max(lb, (e + NW * kTB - 1) / (NW * kTB)));
+            n = min(n, a.n_split_max);
+            if (p < cum + n) {
+                b = i;
+                nb_b = n;
+                break;
+            }
+            cum += n;
+        }
+        if (b < 0) return;                        // more workgroups than splits
+        split = p - cum;
+        L = a.kv_lens[b];
+        if (L < 1 || L > max_len) {
+            // out of contract: the row becomes NaN; nothing else is read
+            if (split == 0)
+                for (int i = threadIdx.x; i < GC * D; i += NT)
+                    a.o[((size_t)b * a.H + h0 + i / D) * D + (i % D)] = __builtin_nanf("");
+            return;
+        }
+        const int k_lo = (a.window > 0 && L > a.window) ? L - a.window : 0;
+        const int eff = L - k_lo;
+        const int tsplit = (((eff + nb_b - 1) / nb_b) + 15) & ~15;   // <= kMaxSplitTokens
+        n_live = (eff + tsplit - 1) / tsplit;
+        if (split >= n_live) return;
+        t_begin = k_lo + split * tsplit;
+        t_end = min(L, t_begin + tsplit);
+    } else {
+        split = blockIdx.x;
+        b = blockIdx.z;
+        L = a.kv_len;
+        const int k_lo = (a.window > 0 && L > a.window) ? L - a.window : 0;
+        n_live = (L - k_lo + a.split_tokens - 1) / a.split_tokens;
+        if (split >= n_live) return;
+        t_begin = k_lo + split * a.split_tokens;
+        t_end = min(L, t_begin + a.split_tokens);
+    }
+
+    const TierSrc src{a.k, a.v, a.k_scales, a.v_scales, RING ? a.ring : 0, 0};
+    split_partial<D, GC, PAGED, CAP, RING>(a, src, rings, lds_m, lds_l, lds_pages, lds_qx, lds_qs, b, split,
+                                           n_live, t_begin, t_end, kvh, h0);
+    if (n_live == 1) return;
+    merge_splits<D, GC, NT, merge_chunk<D, GC, PAGED>()>(a, rings, &lds_last, b, h0, n_live);
+}
+
+// Tiered decode of one sequence: positions [0, cold_len) sit in an int8 paged cold tier,
+// positions [cold_len, kv_len) in an f16 ring (the hot tier).  Workgroups [0, n_cold) take
+// splits of the cold tier with the int8 body, the rest splits of the hot tier with the f16
+// ring body; all of them publish partials of one online softmax and the last to arrive
+// merges them, exactly as for a single-layout cache.  LDS is sized for the larger body.
+template <int D, int GC, bool CAP>
+constexpr int tier_ring_bytes() {
+    using SP = DecShape<D, true>;
+    using SF = DecShape<D, false>;
+    return SP::NW * SP::WAVE_LDS > SF::NW * SF::WAVE_LDS ? SP::NW * SP::WAVE_LDS : SF::NW * SF::WAVE_LDS;
+}
+
+template <int D, int GC, bool CAP>
+__global__ void __launch_bounds__((DecShape<D, true>::NT)) decode_tiered_kernel(DecodeParams a) {
+    using SP = DecShape<D, true>;
+    using SF = DecShape<D, false>;
+    static_assert(SP::NT == SF::NT && SP::NW == SF::NW, "one block shape for both tiers");
+    constexpr int NT = SP::NT;
+    constexpr int RB = tier_ring_bytes<D, GC, CAP>();
+    __shared__ __attribute__((aligned(1024))) char rings[RB];
+    __shared__ float lds_m[SP::NW][GC];
+    __shared__ float lds_l[SP::NW][GC];
+    __shared__ int lds_pages[kMaxSplitTokens / 16 + 1];
+    __shared__ int lds_last;
+    __shared__ half8_t lds_qx[SP::KC][64];
+    __shared__ float lds_qs[SP::KC][64];
+    static_assert(sizeof(float) * SP::NW * GC * D <= RB, "merge buffer fits in the rings");
+    constexpr int CS = (RB / 4) / (GC * (D + 2)) > kMaxSplits ? kMaxSplits : (RB / 4) / (GC * (D + 2));
+
+    const int G = a.H / a.Hkv;
+    const int nch = G / GC;
+    const int kvh = blockIdx.y / nch;
+    const int h0 = kvh * G + (blockIdx.y % nch) * GC;
+    const int n_live = gridDim.x;
+    const int split = blockIdx.x;
+    if (split < a.tier_cold_splits) {
+        const int t_begin = a.tier_k_lo + split * a.tier_cold_tokens;
+        const int t_end = min(a.tier_cold_len, t_begin + a.tier_cold_tokens);
+        const TierSrc src{a.k, a.v, a.k_scales, a.v_scales, 0, 0};
+        split_partial<D, GC, true, CAP, false>(a, src, rings, lds_m, lds_l, lds_pages, lds_qx, lds_qs, 0,
+                                               split, n_live, t_begin, t_end, kvh, h0);
+    } else {
+        const int t_begin = max(a.tier_k_lo, a.tier_cold_len) + (split - a.tier_cold_splits) * a.split_tokens;
+        const int t_end = min(a.kv_len, t_begin + a.split_tokens);
+        const TierSrc src{a.hot_k, a.hot_v, nullptr, nullptr, a.ring, a.ring_off};
+        split_partial<D, GC, false, CAP, true>(a, src, rings, lds_m, lds_l, lds_pages, lds_qx, lds_qs, 0,
+                                               split, n_live, t_begin, t_end, kvh, h0);
+    }
+    if (n_live == 1) return;
+    merge_splits<D, GC, NT, CS>(a, rings, &lds_last, 0, h0, n_live);
+}
+
+
 template <int D, bool PAGED, bool CAP, bool RING>
 hipError_t launch_decode_c(const DecodeParams& p, int gc, dim3 grid, hipStream_t st) {
     const dim3 block(DecShape<D, PAGED>::NT);
@@ -814,6 +907,40 @@ hipError_t launch_decode(const DecodeParams& p, int head_dim, int gc, bool paged
             case 128: return launch_decode_d<128, false>(p, gc, grid, st);
             case 256: return launch_decode_d<256, false>(p, gc, grid, st);
         }
+    }
+    return hipErrorInvalidValue;
+}
+
+namespace {
+
+template <int D, bool CAP>
+hipError_t launch_tiered_c(const DecodeParams& p, int gc, dim3 grid, hipStream_t st) {
+    const dim3 block(DecShape<D, true>::NT);
+    switch (gc) {
+        case 1: hipLaunchKernelGGL((decode_tiered_kernel<D, 1, CAP>), grid, block, 0, st, p); break;
+        case 2: hipLaunchKernelGGL((decode_tiered_kernel<D, 2, CAP>), grid, block, 0, st, p); break;
+        case 4: hipLaunchKernelGGL((decode_tiered_kernel<D, 4, CAP>), grid, block, 0, st, p); break;
+        case 8: hipLaunchKernelGGL((decode_tiered_kernel<D, 8, CAP>), grid, block, 0, st, p); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_tiered_d(const DecodeParams& p, int gc, dim3 grid, hipStream_t st) {
+    return p.softcap > 0.f ? launch_tiered_c<D, true>(p, gc, grid, st) : launch_tiered_c<D, false>(p, gc, grid, st);
+}
+
+}  // namespace
+
+hipError_t launch_decode_tiered(const DecodeParams& p, int head_dim, int gc, int n_splits, hipStream_t st) {
+    const int nch = (p.H / p.Hkv) / gc;
+    const dim3 grid(n_splits, p.Hkv * nch, 1);
+    // head_dim 256: the int8 body runs eight waves and the f16 body four, so the two tiers
+    // cannot share one block shape; the host rejects it
+    switch (head_dim) {
+        case 64: return launch_tiered_d<64>(p, gc, grid, st);
+        case 128: return launch_tiered_d<128>(p, gc, grid, st);
     }
     return hipErrorInvalidValue;
 }

@@ -34,6 +34,16 @@ struct DecodeParams {
     int n_split_max;           // split partials per (sequence, head): workspace row stride
     int batch;                 // paged: sequences
     int n_wg;                  // paged: workgroups per head chunk (grid.x)
+    // tiered (one sequence): k, v, k_scales, v_scales, page_table hold the int8 paged cold
+    // tier with positions [0, tier_cold_len); hot_k, hot_v the f16 ring [Hkv][ring][D] with
+    // position t at row (t + ring_off) mod ring; kv_len = all positions
+    const void* hot_k;
+    const void* hot_v;
+    int ring_off;
+    int tier_cold_len;
+    int tier_cold_splits;      // workgroups [0, tier_cold_splits) take cold splits
+    int tier_k_lo;             // first visible position
+    int tier_cold_tokens;      // tokens per cold split (split_tokens: per hot split)
 };
 
 struct FwdParams {
@@ -61,6 +71,8 @@ int decode_max_heads_per_workgroup();
 int decode_workgroups_per_cu(int head_dim, bool paged);
 int decode_max_splits();
 int decode_max_split_tokens_paged();
+// tiered decode: grid (n_splits, Hkv * head chunks)
+hipError_t launch_decode_tiered(const DecodeParams& p, int head_dim, int gc, int n_splits, hipStream_t st);
 
 // dtype: 0 f32, 1 f16
 hipError_t launch_fwd(const FwdParams& p, int head_dim, int dtype, hipStream_t st);
