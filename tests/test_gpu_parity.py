@@ -631,6 +631,24 @@ def test_prefill_full_workload_sampled_rows(dev, c3_inputs):
         assert np.array_equal(got[0, h], v[0, h // G])
 
 
+@pytest.mark.parametrize("S,L,H,Hkv,D,W", [
+    (1024, 1024, 16, 8, 128, 0),     # 256 workgroups of 64 rows: the unsplit configuration
+    (64, 4096, 4, 2, 128, 0),        # a short chunk after a long cache: four key groups
+    (100, 3000, 2, 1, 64, 700),      # key groups with a window and a ragged chunk
+])
+def test_prefill_both_configurations(dev, S, L, H, Hkv, D, W):
+    """Grids that fill the device run 64-row workgroups; smaller ones run 32-row workgroups
+    whose waves split the keys four ways and merge in LDS.  Both against the oracle on
+    sampled rows (first, last, a tile edge, the middle)."""
+    say("prefill configuration S=%d L=%d H=%d Hkv=%d D=%d W=%d" % (S, L, H, Hkv, D, W))
+    q, k, v = synth.prefill_inputs(synth.seed_of(3) + S + L, S, L, H, Hkv, D, "f16")
+    got = run_prefill(dev, q, k, v, True, W, 0.0)
+    assert np.all(np.isfinite(got))
+    rows = sorted(set([0, 1, 31, 32, S // 2, S - 2, S - 1]))
+    want = prefill_oracle_rows(q, k, v, rows, True, W, 0.0)
+    assert maxabs(got[rows], want) < TOL_F16
+
+
 # ---- chunked prefill against a cache whose length is read on the device -----------------
 
 def run_prefill_dev_len(dev, q, kcap, vcap, L, causal, W=0, cap=0.0):

@@ -197,7 +197,7 @@ int run_fwd(const void* q, const void* k, const void* v, void* o, int dtype, int
     p.causal = causal; p.window = window;
     p.scale = scale; p.scale_log2 = scale * kLog2e;
     p.softcap = softcap; p.inv_softcap = softcap > 0.f ? 1.0f / softcap : 0.f;
-    const int bm = ta03::fwd_block_rows(D, dtype);
+    const int bm = ta03::fwd_block_rows(D, dtype, seq_len, H);
     p.n_qblocks = (seq_len + bm - 1) / bm;
     if ((long)p.n_qblocks * H > 0x7fffffffL)
         return fail(ATTN_ERR_INVALID_ARG, "%s: grid of %ld workgroups exceeds the device limit", what,

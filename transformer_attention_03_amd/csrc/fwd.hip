@@ -111,13 +111,15 @@ __device__ __forceinline__ float score_transform(const FwdParams& a, float s) {
 //          lane j points at V[key_0 + j/4][d_0 + 4 (j%4)] and lane i receives
 //          V[key_0 + k][d_0 + i] for k = 0..3, which is the transposed operand.
 
-template <int D, int QB_, int NW_, int NS_, int BN_>
+template <int D, int QB_, int NW_, int NS_, int BN_, int KS_ = 1>
 struct F16Shape {
     static constexpr int NW = NW_;                // waves per workgroup
     static constexpr int QB = QB_;                // 16-row query blocks per wave
     static constexpr int NS = NS_;                // LDS ring stages
+    static constexpr int KS = KS_;                // key groups: waves that share query rows
+    static constexpr int NWQ = NW / KS;           // waves per key group
     static constexpr int NT = 64 * NW;
-    static constexpr int BM = NW * QB * 16;       // query rows per workgroup
+    static constexpr int BM = NWQ * QB * 16;      // query rows per workgroup
     static constexpr int BN = BN_;                // keys per tile (a multiple of 32)
     static constexpr int TILE = BN * D * 2;       // bytes of one K (or V) tile
     static constexpr int LI = TILE / 1024 / NW;   // 1 KB DMA loads per wave per tile, K or V
@@ -214,17 +216,25 @@ __device__ __forceinline__ half4_t lds_read_tr16(const char* p) {
     return __builtin_bit_cast(half4_t, v);
 }
 
-template <int D, int QB, int NW, int NS, int BN, bool CAP>
+// Key groups (KS > 1, for grids too small to fill the device): the NW waves form KS groups
+// of NW / KS waves; the groups hold the same query rows and each iteration brings in KS
+// tiles, one per group, so every wave walks 1 / KS of the keys.  At the end the groups'
+// online-softmax states (running max, row sum, unnormalised output) are merged through LDS
+// by log-sum-exp and the first group writes the rows.
+template <int D, int QB, int NW, int NS, int BN, int KS, bool CAP>
 __global__ void __launch_bounds__(64 * NW) fwd_f16_kernel(FwdParams a) {
-    using S = F16Shape<D, QB, NW, NS, BN>;
-    __shared__ __attribute__((aligned(1024))) char k_lds[NS][S::TILE];
-    __shared__ __attribute__((aligned(1024))) char v_lds[NS][S::TILE];
+    using S = F16Shape<D, QB, NW, NS, BN, KS>;
+    static_assert(KS == 1 || (NS == 2 && QB == 1 && NW % KS == 0), "key groups: two stages, one row block per wave");
+    __shared__ __attribute__((aligned(1024))) char k_lds[NS][KS][S::TILE];
+    __shared__ __attribute__((aligned(1024))) char v_lds[NS][KS][S::TILE];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int ln = lane & 15;          // query column of the S^T / O^T blocks; A-tile row
     const int lg = lane >> 4;          // lane group 0..3
+    const int qw = KS == 1 ? w : w % S::NWQ;     // query block of this wave
+    const int kg = KS == 1 ? 0 : w / S::NWQ;     // key group of this wave
 
     int head, qblock;
     work_item(a, head, qblock);
@@ -234,7 +244,7 @@ __global__ void __launch_bounds__(64 * NW) fwd_f16_kernel(FwdParams a) {
     const TileRange tr = tile_range(a, q0, S::BM, S::BN);
 
     const _Float16* qg = reinterpret_cast<const _Float16*>(a.q) + (long)head * a.q_head;
-    const char* kg = reinterpret_cast<const char*>(reinterpret_cast<const _Float16*>(a.k) + (long)kvh * a.k_head);
+    const char* kg_ptr = reinterpret_cast<const char*>(reinterpret_cast<const _Float16*>(a.k) + (long)kvh * a.k_head);
     const char* vg = reinterpret_cast<const char*>(reinterpret_cast<const _Float16*>(a.v) + (long)kvh * a.k_head);
 
     DmaLane<D, QB, NW, NS, BN> dl;
@@ -247,11 +257,15 @@ __global__ void __launch_bounds__(64 * NW) fwd_f16_kernel(FwdParams a) {
     const int rot = nt > 1 ? (int)(((long)qblock * nt) / a.n_qblocks) : 0;
     auto tile_key = [&](int t) { int u = t - tr.kt0 + rot; u -= u >= nt ? nt : 0; return (tr.kt0 + u) * S::BN; };
 
-    // prologue: tiles kt0 .. kt0 + NS - 2 in flight
+    // prologue: the tiles of iterations 0 .. NS - 2 in flight (iteration i holds tiles
+    // kt0 + i KS + j, j < KS, one per key group)
 #pragma unroll
     for (int st0 = 0; st0 < NS - 1; ++st0)
-        if (tr.kt0 + st0 < tr.kt1)
-            f16_dma_tile<D, QB, NW, NS, BN>(a, kg, vg, dl, tile_key(tr.kt0 + st0), w, lane, k_lds[st0], v_lds[st0]);
+#pragma unroll
+        for (int j = 0; j < KS; ++j)
+            if (tr.kt0 + st0 * KS + j < tr.kt1)
+                f16_dma_tile<D, QB, NW, NS, BN>(a, kg_ptr, vg, dl, tile_key(tr.kt0 + st0 * KS + j), w, lane,
+                                                k_lds[st0][j], v_lds[st0][j]);
 
     // ---- Q fragments (B operand of S^T = K Q^T) --------------------------------------------
     half8_t qf[S::QB][S::DC];
@@ -260,7 +274,7 @@ __global__ void __launch_bounds__(64 * NW) fwd_f16_kernel(FwdParams a) {
     unsigned vspan[S::QB];
 #pragma unroll
     for (int qb = 0; qb < S::QB; ++qb) {
-        const int row = q0 + (w * S::QB + qb) * 16 + ln;
+        const int row = q0 + (qw * S::QB + qb) * 16 + ln;
         qpos[qb] = a.kv_len - a.seq_len + row;
         const int hi = a.causal ? min(qpos[qb], a.kv_len - 1) : a.kv_len - 1;
         const int lo = a.window > 0 ? max(0, qpos[qb] - a.window + 1) : 0;
@@ -320,21 +334,29 @@ __global__ void __launch_bounds__(64 * NW) fwd_f16_kernel(FwdParams a) {
     }
 
     int stage = 0;
-    for (int kt = tr.kt0; kt < tr.kt1; ++kt) {
-        // this tile's DMA (issued NS - 1 tiles ago) has landed for every wave, and every
-        // wave is done with the stage that the next DMA overwrites
-        if (kt + NS - 2 < tr.kt1) wait_vmem_at_most<2 * S::LI * (NS - 2)>();
-        else wait_vmem_at_most<0>();
+    for (int it = 0; it * KS < tr.kt1 - tr.kt0; ++it) {
+        // this iteration's DMA (issued NS - 1 iterations ago) has landed for every wave, and
+        // every wave is done with the stage that the next DMA overwrites
+        if constexpr (KS == 1) {
+            if (tr.kt0 + it + NS - 2 < tr.kt1) wait_vmem_at_most<2 * S::LI * (NS - 2)>();
+            else wait_vmem_at_most<0>();
+        } else {
+            wait_vmem_at_most<0>();
+        }
         __syncthreads();
         {
-            const int nxt = kt + NS - 1;
-            if (nxt < tr.kt1) {
-                const int sn = (stage + NS - 1) % NS;
-                f16_dma_tile<D, QB, NW, NS, BN>(a, kg, vg, dl, tile_key(nxt), w, lane, k_lds[sn], v_lds[sn]);
-            }
+            const int nxt = it + NS - 1;
+            const int sn = (stage + NS - 1) % NS;
+#pragma unroll
+            for (int j = 0; j < KS; ++j)
+                if (tr.kt0 + nxt * KS + j < tr.kt1)
+                    f16_dma_tile<D, QB, NW, NS, BN>(a, kg_ptr, vg, dl, tile_key(tr.kt0 + nxt * KS + j), w, lane,
+                                                    k_lds[sn][j], v_lds[sn][j]);
         }
-        const char* kl = k_lds[stage];
-        const char* vl = v_lds[stage];
+        const int kt = tr.kt0 + it * KS + kg;
+        if (KS == 1 || kt < tr.kt1) {
+        const char* kl = k_lds[stage][kg];
+        const char* vl = v_lds[stage][kg];
         const int ks = tile_key(kt);
         const bool masked = tile_needs_mask(a, tr, ks, S::BN);
 
@@ -449,7 +471,45 @@ __global__ void __launch_bounds__(64 * NW) fwd_f16_kernel(FwdParams a) {
                     acc_o[db][qb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf, pf[qb][c], acc_o[db][qb], 0, 0, 0);
             }
         }
+        }  // kt < kt1
         stage = (stage + 1 == NS) ? 0 : stage + 1;
+    }
+
+    if constexpr (KS > 1) {
+        // ---- merge the key groups: groups 1 .. KS-1 leave (m, l, O^T) in LDS per lane ------
+        constexpr int PS = 4 * S::NDB + 2;                       // floats per lane
+        static_assert(sizeof(float) * (KS - 1) * S::NWQ * 64 * PS <= sizeof(k_lds), "merge buffer fits");
+        float* buf = reinterpret_cast<float*>(&k_lds[0][0][0]);
+        __syncthreads();                                         // every wave is done with the tiles
+        if (kg > 0) {
+            float* mine = buf + (((kg - 1) * S::NWQ + qw) * 64 + lane) * PS;
+#pragma unroll
+            for (int db = 0; db < S::NDB; ++db)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) mine[4 * db + i] = acc_o[db][0][i];
+            mine[4 * S::NDB] = acc_l[0][0];
+            mine[4 * S::NDB + 1] = m_run[0];
+        }
+        __syncthreads();
+        if (kg > 0) return;
+        float mx = m_run[0];
+#pragma unroll
+        for (int g = 1; g < KS; ++g) mx = fmaxf(mx, buf[(((g - 1) * S::NWQ + qw) * 64 + lane) * PS + 4 * S::NDB + 1]);
+        const float f0 = fast_exp2(m_run[0] - mx);
+        float lsum = acc_l[0][0] * f0;
+#pragma unroll
+        for (int db = 0; db < S::NDB; ++db) acc_o[db][0] *= f0;
+#pragma unroll
+        for (int g = 1; g < KS; ++g) {
+            const float* other = buf + (((g - 1) * S::NWQ + qw) * 64 + lane) * PS;
+            const float fg = fast_exp2(other[4 * S::NDB + 1] - mx);
+            lsum += fg * other[4 * S::NDB];
+#pragma unroll
+            for (int db = 0; db < S::NDB; ++db)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) acc_o[db][0][i] += fg * other[4 * db + i];
+        }
+        acc_l[0] = float4_t{lsum, lsum, lsum, lsum};
     }
 
     // ---- epilogue: O = (O^T)^T / l ---------------------------------------------------------
@@ -458,7 +518,7 @@ __global__ void __launch_bounds__(64 * NW) fwd_f16_kernel(FwdParams a) {
     for (int qb = 0; qb < S::QB; ++qb) {
         const float l = acc_l[qb][0];
         const float inv = l != 0.f ? 1.0f / l : 0.f;
-        const int row = q0 + (w * S::QB + qb) * 16 + ln;
+        const int row = q0 + (qw * S::QB + qb) * 16 + ln;
         if (row < a.seq_len) {
 #pragma unroll
             for (int db = 0; db < S::NDB; ++db) {
@@ -630,19 +690,45 @@ __global__ void __launch_bounds__(256) fwd_f32_kernel(FwdParams a) {
 // LDS per workgroup, three workgroups per compute unit, and a 2304-row, 16-head vision
 // call comes to 768 workgroups, three per compute unit, with no tail.
 template <int D> struct F16Cfg;
-template <> struct F16Cfg<64> { static constexpr int QB = 1, NW = 3, NS = 2, BN = 96; };
-template <> struct F16Cfg<128> { static constexpr int QB = 1, NW = 4, NS = 2, BN = 64; };
-template <> struct F16Cfg<256> { static constexpr int QB = 1, NW = 8, NS = 2, BN = 64; };
+template <> struct F16Cfg<64> { static constexpr int QB = 1, NW = 3, NS = 2, BN = 96, KS = 1; };
+template <> struct F16Cfg<128> { static constexpr int QB = 1, NW = 4, NS = 2, BN = 64, KS = 1; };
+template <> struct F16Cfg<256> { static constexpr int QB = 1, NW = 8, NS = 2, BN = 64, KS = 1; };
+
+// Grids of fewer workgroups than compute units (a short chunk, few heads): 32 query rows
+// per workgroup and four key groups of two waves, 8 KB tiles (128 KB of LDS, one workgroup
+// per compute unit), so each compute unit runs eight waves that each walk a quarter of the
+// keys.  head_dim 256 keeps its configuration.
+template <int D> struct F16Small;
+template <> struct F16Small<64> { static constexpr int QB = 1, NW = 8, NS = 2, BN = 64, KS = 4; };
+template <> struct F16Small<128> { static constexpr int QB = 1, NW = 8, NS = 2, BN = 32, KS = 4; };
+constexpr int kComputeUnits = 256;
+
+template <int D>
+constexpr int std_rows() { return F16Cfg<D>::QB * (F16Cfg<D>::NW / F16Cfg<D>::KS) * 16; }
+
+bool use_small(int head_dim, int dtype, int seq_len, int H) {
+    if (dtype != 1 || (head_dim != 64 && head_dim != 128)) return false;
+    const int bm = head_dim == 64 ? std_rows<64>() : std_rows<128>();
+    return (long)((seq_len + bm - 1) / bm) * H < kComputeUnits;
+}
+
+template <int D, typename C>
+hipError_t launch_f16(const FwdParams& p, dim3 grid, hipStream_t st) {
+    if (p.softcap > 0.f)
+        hipLaunchKernelGGL((fwd_f16_kernel<D, C::QB, C::NW, C::NS, C::BN, C::KS, true>), grid, dim3(64 * C::NW), 0, st, p);
+    else
+        hipLaunchKernelGGL((fwd_f16_kernel<D, C::QB, C::NW, C::NS, C::BN, C::KS, false>), grid, dim3(64 * C::NW), 0, st, p);
+    return hipGetLastError();
+}
 
 template <int D>
 hipError_t launch_d(const FwdParams& p, int dtype, hipStream_t st) {
     const dim3 grid(p.n_qblocks * p.H);
     if (dtype == 1) {
-        constexpr int QB = F16Cfg<D>::QB, NW = F16Cfg<D>::NW, NS = F16Cfg<D>::NS, BN = F16Cfg<D>::BN;
-        if (p.softcap > 0.f)
-            hipLaunchKernelGGL((fwd_f16_kernel<D, QB, NW, NS, BN, true>), grid, dim3(64 * NW), 0, st, p);
-        else
-            hipLaunchKernelGGL((fwd_f16_kernel<D, QB, NW, NS, BN, false>), grid, dim3(64 * NW), 0, st, p);
+        if constexpr (D != 256) {
+            if (use_small(D, dtype, p.seq_len, p.H)) return launch_f16<D, F16Small<D>>(p, grid, st);
+        }
+        return launch_f16<D, F16Cfg<D>>(p, grid, st);
     } else {
         hipLaunchKernelGGL(fwd_f32_kernel<D>, grid, dim3(256), 0, st, p);
     }
@@ -651,12 +737,15 @@ hipError_t launch_d(const FwdParams& p, int dtype, hipStream_t st) {
 
 }  // namespace
 
-int fwd_block_rows(int head_dim, int dtype) {
+int fwd_block_rows(int head_dim, int dtype, int seq_len, int H) {
     if (dtype != 1) return F32Shape<64>::BM;
+    if (use_small(head_dim, dtype, seq_len, H))
+        return head_dim == 64 ? F16Small<64>::QB * (F16Small<64>::NW / F16Small<64>::KS) * 16
+                              : F16Small<128>::QB * (F16Small<128>::NW / F16Small<128>::KS) * 16;
     switch (head_dim) {
-        case 64: return F16Cfg<64>::QB * F16Cfg<64>::NW * 16;
-        case 128: return F16Cfg<128>::QB * F16Cfg<128>::NW * 16;
-        default: return F16Cfg<256>::QB * F16Cfg<256>::NW * 16;
+        case 64: return std_rows<64>();
+        case 128: return std_rows<128>();
+        default: return std_rows<256>();
     }
 }
 

@@ -76,6 +76,7 @@ hipError_t launch_decode_tiered(const DecodeParams& p, int head_dim, int gc, int
 
 // dtype: 0 f32, 1 f16
 hipError_t launch_fwd(const FwdParams& p, int head_dim, int dtype, hipStream_t st);
-int fwd_block_rows(int head_dim, int dtype);
+// query rows per workgroup for this call shape (the launcher picks the same configuration)
+int fwd_block_rows(int head_dim, int dtype, int seq_len, int H);
 
 }  // namespace ta03
