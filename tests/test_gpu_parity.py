@@ -435,8 +435,8 @@ def poison_outside_window(t, W):
     c = t["cold"]
     for p in range(min(lo, t["cold_len"])):
         pg = c["page_table"][0][p // 16]
-        c["k_scales"][pg, p % 16] = np.nan
-        c["v_scales"][pg, p % 16] = np.nan
+        c["k_scales"][pg, :, p % 16] = np.nan
+        c["v_scales"][pg, :, p % 16] = np.nan
     R = t["ring_k"].shape[1]
     for p in range(t["cold_len"], lo):
         r = (t["hot_start"] + p - t["cold_len"]) % R

@@ -70,15 +70,15 @@ def test_paged_layout_round_trips_and_is_poisoned():
             sl = t & 15
             assert np.array_equal(kp[ph, sl], d["k_q"][b][t])
             assert np.array_equal(vp[ph, sl], d["v_q"][b][t])
-            assert np.array_equal(ks[ph, sl], d["k_s"][b][t])
-            assert np.array_equal(vs[ph, sl], d["v_s"][b][t])
+            assert np.array_equal(ks[ph, :, sl], d["k_s"][b][t])
+            assert np.array_equal(vs[ph, :, sl], d["v_s"][b][t])
         for lp in range(n_live[b]):
             used.add(int(tab[b, lp]))
         assert np.all(tab[b, n_live[b]:] == -1)
         rem = int(L) % 16
         if rem:
             last = tab[b, n_live[b] - 1]
-            assert np.all(kp[last, rem:] == -128) and np.all(np.isnan(ks[last, rem:]))
+            assert np.all(kp[last, rem:] == -128) and np.all(np.isnan(ks[last, :, rem:]))
     assert len(used) == sum(n_live)
     poison = sorted(set(range(kp.shape[0])) - used)
     assert len(poison) == 5

@@ -180,6 +180,15 @@ __device__ __forceinline__ size_t row_index(const RowCtx& c, int t) {
     }
 }
 
+// Index of token t's scale for this KV head (paged).  Scales are stored head-major within a
+// page, [page][kv head][16], so the 16 scales a block needs are one contiguous 64-byte run
+// (a token-major [page][16][kv head] layout would make every KV head pull the whole page's
+// scale lines, all heads' scales, for its own 16).
+__device__ __forceinline__ size_t scale_index(const RowCtx& c, int t) {
+    const int pg = c.pages[(t >> 4) - c.page0];
+    return ((size_t)pg * c.Hkv + c.kvh) * 16 + (t & 15);
+}
+
 // The same DMAs with a uniform 64-bit base in SGPRs and a 32-bit per-lane offset.
 __device__ __forceinline__ uint64_t uniform_ptr(const void* p) {
     const uint64_t b = (uint64_t)(uintptr_t)p;
@@ -209,7 +218,7 @@ template <int D, bool PAGED>
 struct DmaLane {
     uint32_t k[DecShape<D, PAGED>::TD];
     uint32_t v[DecShape<D, PAGED>::TD];
-    uint32_t sc;           // paged: scale of row lane & 15
+    uint32_t sc;           // paged: scale of row lane & 15 (byte offset in the page's run of 16)
 };
 
 template <int D, bool PAGED>
@@ -223,7 +232,7 @@ __device__ __forceinline__ DmaLane<D, PAGED> dma_lane(int lane, uint32_t rs, int
         L.k[i] = r * rs + 16 * (cpos ^ ksw<S::RPL>(r));
         L.v[i] = r * rs + 16 * (cpos ^ vsw<S::RPL>(r));
     }
-    L.sc = (uint32_t)((lane & 15) * Hkv) * 4u;
+    L.sc = (uint32_t)(lane & 15) * 4u;
     return L;
 }
 
@@ -240,9 +249,11 @@ __device__ __forceinline__ void dma_block(char* slot, const RowCtx& c, const Dma
     const bool full = tb + kTB <= t_end && (!PAGED || (tb & 15) == 0) && (!RING || slot0 + kTB <= c.ring);
     if (full) {
         size_t row0;
+        size_t srow0 = 0;      // paged: first scale of the block ([page][kv head][16] layout)
         if constexpr (PAGED) {
             const int pg = __builtin_amdgcn_readfirstlane(c.pages[(tb >> 4) - c.page0]);
             row0 = (size_t)pg * 16 * c.Hkv + c.kvh;
+            srow0 = ((size_t)pg * c.Hkv + c.kvh) * 16;
         } else if constexpr (RING) {
             row0 = (size_t)c.kvh * c.ring + slot0;
         } else {
@@ -258,8 +269,8 @@ __device__ __forceinline__ void dma_block(char* slot, const RowCtx& c, const Dma
         if constexpr (PAGED) {
             // 16 lanes carry the block's 16 scales (the instruction still counts once per wave)
             if (lane < 16) {
-                dma4s(c.kscales + row0, L.sc, slot + 2 * S::TILE);
-                dma4s(c.vscales + row0, L.sc, slot + 2 * S::TILE + 256);
+                dma4s(c.kscales + srow0, L.sc, slot + 2 * S::TILE);
+                dma4s(c.vscales + srow0, L.sc, slot + 2 * S::TILE + 256);
             }
         }
     } else {
@@ -273,9 +284,9 @@ __device__ __forceinline__ void dma_block(char* slot, const RowCtx& c, const Dma
         }
         if constexpr (PAGED) {
             if (lane < 16) {
-                const size_t ri = row_index<PAGED, RING>(c, min(tb + lane, t_end - 1));
-                dma4(c.kscales + ri, slot + 2 * S::TILE);
-                dma4(c.vscales + ri, slot + 2 * S::TILE + 256);
+                const size_t si = scale_index(c, min(tb + lane, t_end - 1));
+                dma4(c.kscales + si, slot + 2 * S::TILE);
+                dma4(c.vscales + si, slot + 2 * S::TILE + 256);
             }
         }
     }
