@@ -211,7 +211,7 @@ int attn_decode_paged_q8(const float *q, const int8_t *k_pages, const int8_t *v_
  *   (W = sliding_window, 0 = all), across both tiers.  Rows holding other positions, and
  *   page-table entries past ceil(cold_len / 16), are never read; out-of-range page-table
  *   entries are clamped into [0, num_pages).
- *   Requires head_dim in {64, 128} (256: ATTN_ERR_UNSUPPORTED), hot_len <= hot_window,
+ *   Requires hot_len <= hot_window,
  *   0 <= hot_start < hot_window when hot_len > 0, cold_len <= max_pages * page_size, and
  *   cold_len + hot_len >= 1; otherwise ATTN_ERR_INVALID_ARG before any HIP call.
  *   workspace: as for attn_decode, sized by attn_decode_workspace_bytes(1, num_heads,

@@ -455,6 +455,8 @@ def poison_outside_window(t, W):
     (8, 8, 128, 2000, 256, 256, 7, 0, 30.0),      # softcap
     (16, 2, 128, 17, 1, 8, 3, 0, 0.0),            # a few tokens
     (24, 4, 64, 9000, 1000, 1024, 1000, 0, 0.0),  # six query heads per KV head
+    (8, 2, 256, 2500, 300, 333, 200, 0, 0.0),     # head_dim 256
+    (8, 4, 256, 1200, 100, 128, 127, 500, 20.0),  # head_dim 256, window over both tiers, softcap
 ])
 def test_tiered_q8(dev, H, Hkv, D, cold, hot, R, hs, W, cap):
     say("tiered H=%d Hkv=%d D=%d cold=%d hot=%d R=%d hs=%d W=%d cap=%g" % (H, Hkv, D, cold, hot, R, hs, W, cap))

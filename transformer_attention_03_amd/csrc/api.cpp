@@ -449,8 +449,6 @@ int attn_decode_tiered_q8(const float* q, const void* hot_k, const void* hot_v, 
     TRY(check_ptr(q, "q"));
     TRY(check_ptr(o, "o"));
     TRY(check_heads(num_heads, num_kv_heads, head_dim));
-    if (head_dim == 256)
-        return fail(ATTN_ERR_UNSUPPORTED, "%s: head_dim 256 is not built; requires head_dim in {64, 128}", what);
     TRY(check_scalars(sliding_window, attn_softcap, scale));
     if (cold_len < 0 || hot_len < 0)
         return fail(ATTN_ERR_INVALID_ARG, "%s: cold_len (%d) and hot_len (%d) must be >= 0", what, cold_len, hot_len);

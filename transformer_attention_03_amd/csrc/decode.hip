@@ -56,10 +56,12 @@ struct DecShape {
     static constexpr int TILE = kTB * RB;               // bytes of K (or of V) per block
     static constexpr int SCB = PAGED ? 512 : 0;         // K and V scales of a block
     static constexpr int SLOT = 2 * TILE + SCB;
-    // Eight waves with at least two slots each where that fits, else four waves; f16: as
-    // many slots per wave (up to four) as the budget allows; int8: two slots, so that two
-    // workgroups (sixteen waves) share a compute unit.
-    static constexpr int NW = (8 * 2 * SLOT <= kLdsBudget) ? 8 : 4;
+    // Eight waves with at least two slots each where that fits with room to spare, else
+    // four waves; f16: as many slots per wave (up to four) as the budget allows; int8: two
+    // slots, so that two workgroups (sixteen waves) share a compute unit.  (At head_dim 256
+    // eight int8 waves would fill the budget exactly; four waves with four slots use the
+    // same LDS and the block shape of the f16 body, so the tiered kernel can host both.)
+    static constexpr int NW = (8 * 2 * SLOT < kLdsBudget) ? 8 : 4;
     static constexpr int RING_FIT = kLdsBudget / (NW * SLOT) >= 4 ? 4 : kLdsBudget / (NW * SLOT);
     static constexpr int RING = PAGED && NW == 8 ? 2 : RING_FIT;
     static constexpr int NT = 64 * NW;
@@ -947,11 +949,10 @@ hipError_t launch_tiered_d(const DecodeParams& p, int gc, dim3 grid, hipStream_t
 hipError_t launch_decode_tiered(const DecodeParams& p, int head_dim, int gc, int n_splits, hipStream_t st) {
     const int nch = (p.H / p.Hkv) / gc;
     const dim3 grid(n_splits, p.Hkv * nch, 1);
-    // head_dim 256: the int8 body runs eight waves and the f16 body four, so the two tiers
-    // cannot share one block shape; the host rejects it
     switch (head_dim) {
         case 64: return launch_tiered_d<64>(p, gc, grid, st);
         case 128: return launch_tiered_d<128>(p, gc, grid, st);
+        case 256: return launch_tiered_d<256>(p, gc, grid, st);
     }
     return hipErrorInvalidValue;
 }
