@@ -98,3 +98,25 @@ def test_kv_lens_in_range():
     L = synth.paged_kv_lens(synth.seed_of(5), 1000, 16384, 32768)
     assert L.min() >= 16384 and L.max() <= 32768
     assert L.std() > 3000
+
+
+def test_tiered_inputs_place_the_hot_tier_in_the_ring():
+    """Hot position p (cold_len <= p < cold_len + hot_len) sits at ring row
+    (hot_start + p - cold_len) % hot_window; rows holding no position are NaN; the cold tier
+    is the paged layout of one sequence, and an empty cold tier is one poison page."""
+    t = synth.tiered_inputs(20261297, 4, 2, 16, 40, 13, 16, 9, n_poison=2)
+    assert t["ring_k"].shape == (2, 16, 16) and t["hot_k"].shape == (13, 2, 16)
+    for i in range(13):
+        r = (9 + i) % 16
+        assert np.array_equal(t["ring_k"][:, r], t["hot_k"][i])
+        assert np.array_equal(t["ring_v"][:, r], t["hot_v"][i])
+    used = {(9 + i) % 16 for i in range(13)}
+    for r in set(range(16)) - used:
+        assert np.all(np.isnan(t["ring_k"][:, r].astype(np.float32)))
+    c = t["cold"]
+    assert c["k_q"][0].shape == (40, 2, 16) and c["page_table"].shape == (1, 3)
+    assert c["k_scales"].shape == (c["k_pages"].shape[0], 2, 16)
+    e = synth.tiered_inputs(20261297, 4, 2, 16, 0, 5, 8, 0)
+    assert e["cold"]["k_pages"].shape == (1, 16, 2, 16) and np.all(np.isnan(e["cold"]["k_scales"]))
+    # the query is the same stream whether or not there is a cold tier
+    assert np.array_equal(e["q"], t["q"])
