@@ -163,11 +163,11 @@ int attn_decode_ring(const float *q, const void *k, const void *v, float *o,
  *
  *   q, o        : float32 [batch, num_heads, head_dim]
  *   k_pages,
- *   v_pages     : int8    [num_pages, page_size, num_kv_heads, head_dim]
+ *   v_pages     : int8    [num_pages, num_kv_heads, page_size, head_dim]
  *   k_scales,
- *   v_scales    : float32 [num_pages, num_kv_heads, page_size]; value = q8 * scale.  The
- *                 scales of one page are stored head-major, so the page_size scales one
- *                 KV head needs are contiguous.
+ *   v_scales    : float32 [num_pages, num_kv_heads, page_size]; value = q8 * scale.
+ *                 Pages and scales are head-major within a page, so the page_size rows
+ *                 and scales one KV head needs from a page are contiguous.
  *   page_table  : int32   [batch, max_pages_per_seq]; logical page -> physical page
  *   kv_lens     : int32   [batch], in DEVICE memory
  *   page_size   : 16
@@ -200,7 +200,7 @@ int attn_decode_paged_q8(const float *q, const int8_t *k_pages, const int8_t *v_
  *                    mod hot_window (the pages give hotStart and hotWindow but print no index
  *                    formula; this is the plain reading).  Unused if hot_len == 0.
  *   cold_k_pages,
- *   cold_v_pages   : int8 [num_pages, page_size, num_kv_heads, head_dim]
+ *   cold_v_pages   : int8 [num_pages, num_kv_heads, page_size, head_dim]
  *   cold_k_scales,
  *   cold_v_scales  : float32 [num_pages, num_kv_heads, page_size] (head-major within a
  *                    page, as attn_decode_paged_q8); value = q8 * scale

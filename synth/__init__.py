@@ -176,8 +176,8 @@ def build_pages(k_q, k_s, v_q, v_s, seed_perm: int, n_poison: int = 64, max_page
 
     k_q[b] : int8 [L_b, hkv, d]; k_s[b] : float32 [L_b, hkv]  (same for v).
     Returns (k_pages, v_pages, k_scales, v_scales, page_table):
-      pages  int8    [n_pages, 16, hkv, d]
-      scales float32 [n_pages, hkv, 16]  (head-major within a page)
+      pages  int8    [n_pages, hkv, 16, d]  (head-major within a page)
+      scales float32 [n_pages, hkv, 16]
       page_table int32 [B, max_pages]; entries past a sequence's last page are -1.
     Unreferenced pages and slots past kv_len in a last partial page hold int8 -128
     with scale NaN (poison), so a stray read turns an output row to NaN.
@@ -190,8 +190,8 @@ def build_pages(k_q, k_s, v_q, v_s, seed_perm: int, n_poison: int = 64, max_page
     if max_pages is None:
         max_pages = max(n_live)
     perm = fisher_yates(seed_perm, n_pages)
-    k_pages = np.full((n_pages, PAGE, hkv, d), -128, dtype=np.int8)
-    v_pages = np.full((n_pages, PAGE, hkv, d), -128, dtype=np.int8)
+    k_pages = np.full((n_pages, hkv, PAGE, d), -128, dtype=np.int8)
+    v_pages = np.full((n_pages, hkv, PAGE, d), -128, dtype=np.int8)
     k_scales = np.full((n_pages, hkv, PAGE), np.nan, dtype=np.float32)
     v_scales = np.full((n_pages, hkv, PAGE), np.nan, dtype=np.float32)
     table = np.full((B, max_pages), -1, dtype=np.int32)
@@ -203,15 +203,15 @@ def build_pages(k_q, k_s, v_q, v_s, seed_perm: int, n_poison: int = 64, max_page
         full = L // PAGE
         if full:
             pf = phys[:full]
-            k_pages[pf] = k_q[b][: full * PAGE].reshape(full, PAGE, hkv, d)
-            v_pages[pf] = v_q[b][: full * PAGE].reshape(full, PAGE, hkv, d)
+            k_pages[pf] = k_q[b][: full * PAGE].reshape(full, PAGE, hkv, d).transpose(0, 2, 1, 3)
+            v_pages[pf] = v_q[b][: full * PAGE].reshape(full, PAGE, hkv, d).transpose(0, 2, 1, 3)
             k_scales[pf] = k_s[b][: full * PAGE].reshape(full, PAGE, hkv).transpose(0, 2, 1)
             v_scales[pf] = v_s[b][: full * PAGE].reshape(full, PAGE, hkv).transpose(0, 2, 1)
         rem = L - full * PAGE
         if rem:
             pl = phys[full]
-            k_pages[pl, :rem] = k_q[b][full * PAGE:]
-            v_pages[pl, :rem] = v_q[b][full * PAGE:]
+            k_pages[pl, :, :rem] = k_q[b][full * PAGE:].transpose(1, 0, 2)
+            v_pages[pl, :, :rem] = v_q[b][full * PAGE:].transpose(1, 0, 2)
             k_scales[pl, :, :rem] = k_s[b][full * PAGE:].T
             v_scales[pl, :, :rem] = v_s[b][full * PAGE:].T
         g += n_live[b]
@@ -293,8 +293,8 @@ def tiered_inputs(seed_c, h, hkv, d, cold_len, hot_len, hot_window, hot_start, n
         cold = dict(q=normal_f32(stream_seed(seed_c, TID_Q), (1, h, d)),
                     k_q=[np.zeros((0, hkv, d), np.int8)], k_s=[np.zeros((0, hkv), np.float32)],
                     v_q=[np.zeros((0, hkv, d), np.int8)], v_s=[np.zeros((0, hkv), np.float32)],
-                    k_pages=np.full((1, PAGE, hkv, d), -128, np.int8),
-                    v_pages=np.full((1, PAGE, hkv, d), -128, np.int8),
+                    k_pages=np.full((1, hkv, PAGE, d), -128, np.int8),
+                    v_pages=np.full((1, hkv, PAGE, d), -128, np.int8),
                     k_scales=np.full((1, hkv, PAGE), np.nan, np.float32),
                     v_scales=np.full((1, hkv, PAGE), np.nan, np.float32),
                     page_table=np.zeros((1, 1), np.int32), kv_lens=np.zeros(1, np.int32))

@@ -234,7 +234,7 @@ def run_paged(dev, d, W=0, cap=0.0, kv_lens=None, table=None):
     if table is not None:
         t["page_table"] = to_dev(table, dev)
     B, H, D = d["q"].shape
-    Hkv = d["k_pages"].shape[2]
+    Hkv = d["k_pages"].shape[1]
     mp = d["page_table"].shape[1]
     o = torch.empty((B, H, D), dtype=torch.float32, device=dev)
     ws = ta.decode_workspace(B, H, Hkv, D, mp * 16, dev)

@@ -68,8 +68,8 @@ def test_paged_layout_round_trips_and_is_poisoned():
         for t in range(int(L)):
             ph = tab[b, t >> 4]
             sl = t & 15
-            assert np.array_equal(kp[ph, sl], d["k_q"][b][t])
-            assert np.array_equal(vp[ph, sl], d["v_q"][b][t])
+            assert np.array_equal(kp[ph, :, sl], d["k_q"][b][t])
+            assert np.array_equal(vp[ph, :, sl], d["v_q"][b][t])
             assert np.array_equal(ks[ph, :, sl], d["k_s"][b][t])
             assert np.array_equal(vs[ph, :, sl], d["v_s"][b][t])
         for lp in range(n_live[b]):
@@ -78,7 +78,7 @@ def test_paged_layout_round_trips_and_is_poisoned():
         rem = int(L) % 16
         if rem:
             last = tab[b, n_live[b] - 1]
-            assert np.all(kp[last, rem:] == -128) and np.all(np.isnan(ks[last, :, rem:]))
+            assert np.all(kp[last, :, rem:] == -128) and np.all(np.isnan(ks[last, :, rem:]))
     assert len(used) == sum(n_live)
     poison = sorted(set(range(kp.shape[0])) - used)
     assert len(poison) == 5
@@ -117,6 +117,6 @@ def test_tiered_inputs_place_the_hot_tier_in_the_ring():
     assert c["k_q"][0].shape == (40, 2, 16) and c["page_table"].shape == (1, 3)
     assert c["k_scales"].shape == (c["k_pages"].shape[0], 2, 16)
     e = synth.tiered_inputs(20261297, 4, 2, 16, 0, 5, 8, 0)
-    assert e["cold"]["k_pages"].shape == (1, 16, 2, 16) and np.all(np.isnan(e["cold"]["k_scales"]))
+    assert e["cold"]["k_pages"].shape == (1, 2, 16, 16) and np.all(np.isnan(e["cold"]["k_scales"]))
     # the query is the same stream whether or not there is a cold tier
     assert np.array_equal(e["q"], t["q"])

@@ -189,12 +189,12 @@ def attn_decode_ring(q, k, v, o, workspace, *, total_len: int, scale: float,
 def attn_decode_paged_q8(q, k_pages, v_pages, k_scales, v_scales, page_table, kv_lens, o,
                          workspace, *, scale: float, sliding_window: int = 0,
                          attn_softcap: float = 0.0, stream=None):
-    """q, o: float32 [batch, num_heads, head_dim]; pages int8 [num_pages, 16, num_kv_heads,
+    """q, o: float32 [batch, num_heads, head_dim]; pages int8 [num_pages, num_kv_heads, 16,
     head_dim]; scales float32 [num_pages, num_kv_heads, 16]; page_table int32
     [batch, max_pages]; kv_lens int32 [batch] (device)."""
     _need_contig(q, k_pages, v_pages, k_scales, v_scales, page_table, kv_lens, o)
     B, H, D = q.shape
-    P, ps, Hkv, Dk = k_pages.shape
+    P, Hkv, ps, Dk = k_pages.shape
     if Dk != D or v_pages.shape != k_pages.shape or o.shape != q.shape:
         raise ValueError("shape mismatch")
     if k_scales.shape != (P, Hkv, ps) or v_scales.shape != (P, Hkv, ps):
@@ -214,18 +214,18 @@ def attn_decode_tiered_q8(q, hot_k, hot_v, cold_k_pages, cold_v_pages, cold_k_sc
                           attn_softcap: float = 0.0, stream=None):
     """q, o: float32 [num_heads, head_dim]; hot_k, hot_v: float16 ring [num_kv_heads,
     hot_window, head_dim] holding position p >= cold_len at row (hot_start + p - cold_len) %
-    hot_window; cold pages int8 [num_pages, 16, num_kv_heads, head_dim], scales float32
+    hot_window; cold pages int8 [num_pages, num_kv_heads, 16, head_dim], scales float32
     [num_pages, num_kv_heads, 16], page table int32 [max_pages] for positions < cold_len."""
     _need_contig(q, hot_k, hot_v, cold_k_pages, cold_v_pages, cold_k_scales, cold_v_scales,
                  cold_page_table, o)
     H, D = q.shape
     Hkv, R, Dk = hot_k.shape
-    P, ps, Hkv2, Dc = cold_k_pages.shape
+    P, Hkv2, ps, Dc = cold_k_pages.shape
     if Dk != D or Dc != D or Hkv2 != Hkv or hot_v.shape != hot_k.shape or o.shape != q.shape:
         raise ValueError("shape mismatch")
     if cold_v_pages.shape != cold_k_pages.shape or cold_k_scales.shape != (P, Hkv, ps) or \
             cold_v_scales.shape != (P, Hkv, ps) or cold_page_table.dim() != 1:
-        raise ValueError("cold tier: pages [P, 16, Hkv, D], scales [P, Hkv, 16], table [max_pages]")
+        raise ValueError("cold tier: pages [P, Hkv, 16, D], scales [P, Hkv, 16], table [max_pages]")
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check(lib().attn_decode_tiered_q8(
         _ptr(q), _ptr(hot_k), _ptr(hot_v), _ptr(cold_k_pages), _ptr(cold_v_pages),

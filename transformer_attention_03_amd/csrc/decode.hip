@@ -33,7 +33,9 @@
 // travel through device-scope stores and loads, so no cache-wide fence is needed.
 //
 // Paged addressing is integer-exact: physical page = page_table[b][t >> 4], slot t & 15,
-// row ((page * 16 + slot) * Hkv + kvh) * D.  Rows at or past kv_len are never read: the
+// row ((page * Hkv + kvh) * 16 + slot) * D (pages are head-major, [page][kv head][16][D],
+// and so are the scales, [page][kv head][16]: one KV head's block of 16 tokens is one
+// contiguous run of rows and of scales).  Rows at or past kv_len are never read: the
 // DMA of a block's tail fetches the split's last valid row instead, and those tokens are
 // masked, so poisoned slots of a partial last page cannot reach the result.
 
@@ -174,21 +176,12 @@ template <bool PAGED, bool RING>
 __device__ __forceinline__ size_t row_index(const RowCtx& c, int t) {
     if constexpr (PAGED) {
         const int pg = c.pages[(t >> 4) - c.page0];
-        return ((size_t)pg * 16 + (t & 15)) * c.Hkv + c.kvh;
+        return ((size_t)pg * c.Hkv + c.kvh) * 16 + (t & 15);
     } else if constexpr (RING) {
         return (size_t)c.kvh * c.ring + ring_slot(c, t);
     } else {
         return (size_t)c.kvh * c.kv_len + t;
     }
-}
-
-// Index of token t's scale for this KV head (paged).  Scales are stored head-major within a
-// page, [page][kv head][16], so the 16 scales a block needs are one contiguous 64-byte run
-// (a token-major [page][16][kv head] layout would make every KV head pull the whole page's
-// scale lines, all heads' scales, for its own 16).
-__device__ __forceinline__ size_t scale_index(const RowCtx& c, int t) {
-    const int pg = c.pages[(t >> 4) - c.page0];
-    return ((size_t)pg * c.Hkv + c.kvh) * 16 + (t & 15);
 }
 
 // The same DMAs with a uniform 64-bit base in SGPRs and a 32-bit per-lane offset.
@@ -215,7 +208,7 @@ __device__ __forceinline__ void dma4s(const void* sbase, uint32_t voff, const vo
 
 // Per-lane byte offsets, relative to a block's first row, of the 16-byte chunks this lane
 // moves when the block's 16 rows are RS bytes apart in memory (a full block; paged, one
-// page).  Slot layout: K tile, V tile, 256 bytes of K scales, 256 bytes of V scales.
+// page; rows are adjacent in every layout).  Slot layout: K tile, V tile, 256 bytes of K scales, 256 bytes of V scales.
 template <int D, bool PAGED>
 struct DmaLane {
     uint32_t k[DecShape<D, PAGED>::TD];
@@ -224,7 +217,7 @@ struct DmaLane {
 };
 
 template <int D, bool PAGED>
-__device__ __forceinline__ DmaLane<D, PAGED> dma_lane(int lane, uint32_t rs, int Hkv) {
+__device__ __forceinline__ DmaLane<D, PAGED> dma_lane(int lane, uint32_t rs) {
     using S = DecShape<D, PAGED>;
     DmaLane<D, PAGED> L;
 #pragma unroll
@@ -251,11 +244,9 @@ __device__ __forceinline__ void dma_block(char* slot, const RowCtx& c, const Dma
     const bool full = tb + kTB <= t_end && (!PAGED || (tb & 15) == 0) && (!RING || slot0 + kTB <= c.ring);
     if (full) {
         size_t row0;
-        size_t srow0 = 0;      // paged: first scale of the block ([page][kv head][16] layout)
         if constexpr (PAGED) {
             const int pg = __builtin_amdgcn_readfirstlane(c.pages[(tb >> 4) - c.page0]);
-            row0 = (size_t)pg * 16 * c.Hkv + c.kvh;
-            srow0 = ((size_t)pg * c.Hkv + c.kvh) * 16;
+            row0 = ((size_t)pg * c.Hkv + c.kvh) * 16;
         } else if constexpr (RING) {
             row0 = (size_t)c.kvh * c.ring + slot0;
         } else {
@@ -271,8 +262,8 @@ __device__ __forceinline__ void dma_block(char* slot, const RowCtx& c, const Dma
         if constexpr (PAGED) {
             // 16 lanes carry the block's 16 scales (the instruction still counts once per wave)
             if (lane < 16) {
-                dma4s(c.kscales + srow0, L.sc, slot + 2 * S::TILE);
-                dma4s(c.vscales + srow0, L.sc, slot + 2 * S::TILE + 256);
+                dma4s(c.kscales + row0, L.sc, slot + 2 * S::TILE);
+                dma4s(c.vscales + row0, L.sc, slot + 2 * S::TILE + 256);
             }
         }
     } else {
@@ -286,7 +277,8 @@ __device__ __forceinline__ void dma_block(char* slot, const RowCtx& c, const Dma
         }
         if constexpr (PAGED) {
             if (lane < 16) {
-                const size_t si = scale_index(c, min(tb + lane, t_end - 1));
+                // a token's scale has the index of its row
+                const size_t si = row_index<PAGED, RING>(c, min(tb + lane, t_end - 1));
                 dma4(c.kscales + si, slot + 2 * S::TILE);
                 dma4(c.vscales + si, slot + 2 * S::TILE + 256);
             }
@@ -515,7 +507,7 @@ __device__ __forceinline__ void split_partial(const DecodeParams& a, const TierS
     char* ring = rings + w * S::WAVE_LDS;
     const int first = t_begin + w * kTB;
     const int nb = first < t_end ? (t_end - first + STRIDE - 1) / STRIDE : 0;
-    const DmaLane<D, PAGED> dl = dma_lane<D, PAGED>(lane, (uint32_t)((PAGED ? a.Hkv : 1) * S::RB), a.Hkv);
+    const DmaLane<D, PAGED> dl = dma_lane<D, PAGED>(lane, (uint32_t)S::RB);
 #pragma unroll
     for (int k = 0; k < S::RING; ++k)
         if (k < nb) dma_block<D, PAGED, RING>(ring + k * S::SLOT, c, dl, first + k * STRIDE, t_end, lane);
