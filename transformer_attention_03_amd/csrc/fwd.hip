@@ -355,123 +355,123 @@ __global__ void __launch_bounds__(64 * NW) fwd_f16_kernel(FwdParams a) {
         }
         const int kt = tr.kt0 + it * KS + kg;
         if (KS == 1 || kt < tr.kt1) {
-        const char* kl = k_lds[stage][kg];
-        const char* vl = v_lds[stage][kg];
-        const int ks = tile_key(kt);
-        const bool masked = tile_needs_mask(a, tr, ks, S::BN);
+            const char* kl = k_lds[stage][kg];
+            const char* vl = v_lds[stage][kg];
+            const int ks = tile_key(kt);
+            const bool masked = tile_needs_mask(a, tr, ks, S::BN);
 
-        // ---- S^T = K Q^T -----------------------------------------------------------------
-        float4_t st[S::NKB][S::QB];
-#pragma unroll
-        for (int kb = 0; kb < S::NKB; ++kb)
-#pragma unroll
-            for (int qb = 0; qb < S::QB; ++qb) st[kb][qb] = float4_t{0.f, 0.f, 0.f, 0.f};
-        // K fragments are fetched a 32-wide d chunk ahead of their products
-        half8_t kf[2][S::NKB];
-#pragma unroll
-        for (int kb = 0; kb < S::NKB; ++kb)
-            kf[0][kb] = *reinterpret_cast<const half8_t*>(kl + koff[0] + 16 * kb * 2 * D);
-#pragma unroll
-        for (int c = 0; c < S::DC; ++c) {
-            if (c + 1 < S::DC) {
-#pragma unroll
-                for (int kb = 0; kb < S::NKB; ++kb)
-                    kf[(c + 1) & 1][kb] = *reinterpret_cast<const half8_t*>(kl + koff[c + 1] + 16 * kb * 2 * D);
-            }
+            // ---- S^T = K Q^T -----------------------------------------------------------------
+            float4_t st[S::NKB][S::QB];
 #pragma unroll
             for (int kb = 0; kb < S::NKB; ++kb)
 #pragma unroll
-                for (int qb = 0; qb < S::QB; ++qb)
-                    st[kb][qb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf[c & 1][kb], qf[qb][c], st[kb][qb], 0, 0, 0);
-        }
-
-        // V^T fragments of the tile's first 32 keys, read ahead of the softmax so that their
-        // LDS latency overlaps it
-        constexpr int NPF = D >= 256 ? S::NDB / 2 : S::NDB;   // register budget
-        half8_t vf0[NPF];
-#pragma unroll
-        for (int db = 0; db < NPF; ++db) {
-            const half4_t lo = lds_read_tr16(vl + voff[db]);
-            const half4_t hi = lds_read_tr16(vl + voff[db] + 16 * 2 * D);
-            vf0[db] = half8_t{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        }
-
-        // ---- online softmax in the S^T layout: lane = query (ln), keys 16kb + 4lg + i ----
-        // Uncapped scores stay raw (scale > 0 preserves the max); the scale is folded into
-        // the exponent: p = 2^(s * scale * log2 e - m).  Capped scores are turned into log2
-        // units first.  Masked keys get -inf added.
-        half8_t pf[S::QB][S::BN / 32];
-#pragma unroll
-        for (int qb = 0; qb < S::QB; ++qb) {
-            if constexpr (CAP) {
-#pragma unroll
-                for (int kb = 0; kb < S::NKB; ++kb)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const float e2 = fast_exp2(st[kb][qb][i] * K1);
-                        st[kb][qb][i] = __builtin_fmaf(-C2, fast_rcp(e2 + 1.f), C1);
-                    }
-            }
-            if (masked) {
-                // visible keys of this row form [vlo, vhi]; key - vlo <= vhi - vlo (unsigned)
-                const int off = ks + 4 * lg - vlo[qb];
-#pragma unroll
-                for (int kb = 0; kb < S::NKB; ++kb)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i)
-                        st[kb][qb][i] = ((unsigned)(off + 16 * kb + i) <= vspan[qb]) ? st[kb][qb][i] : -INFINITY;
-            }
-            float mx = st[0][qb][0];
+                for (int qb = 0; qb < S::QB; ++qb) st[kb][qb] = float4_t{0.f, 0.f, 0.f, 0.f};
+            // K fragments are fetched a 32-wide d chunk ahead of their products
+            half8_t kf[2][S::NKB];
 #pragma unroll
             for (int kb = 0; kb < S::NKB; ++kb)
+                kf[0][kb] = *reinterpret_cast<const half8_t*>(kl + koff[0] + 16 * kb * 2 * D);
 #pragma unroll
-                for (int i = (kb == 0 ? 1 : 0); i < 4; ++i) mx = fmaxf(mx, st[kb][qb][i]);
-            mx = rows_max(mx);
-            const float mxl = mx * sc2;        // in log2 units
-            if (__builtin_amdgcn_ballot_w64(mxl > m_run[qb] + kSlack) != 0) {
-                const float mnew = fmaxf(m_run[qb], mxl);
-                const float alpha = fast_exp2(m_run[qb] - mnew);
-                m_run[qb] = mnew;
-                acc_l[qb] *= alpha;
+            for (int c = 0; c < S::DC; ++c) {
+                if (c + 1 < S::DC) {
 #pragma unroll
-                for (int db = 0; db < S::NDB; ++db) acc_o[db][qb] *= alpha;
-            }
-            const float mq = m_run[qb];
-#pragma unroll
-            for (int kb = 0; kb < S::NKB; ++kb)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) st[kb][qb][i] = fast_exp2(__builtin_fmaf(st[kb][qb][i], sc2, -mq));
-#pragma unroll
-            for (int c = 0; c < S::BN / 32; ++c) {
-                const half2_t h0 = __builtin_convertvector(float2_t{st[2 * c][qb][0], st[2 * c][qb][1]}, half2_t);
-                const half2_t h1 = __builtin_convertvector(float2_t{st[2 * c][qb][2], st[2 * c][qb][3]}, half2_t);
-                const half2_t h2 = __builtin_convertvector(float2_t{st[2 * c + 1][qb][0], st[2 * c + 1][qb][1]}, half2_t);
-                const half2_t h3 = __builtin_convertvector(float2_t{st[2 * c + 1][qb][2], st[2 * c + 1][qb][3]}, half2_t);
-                pf[qb][c] = half8_t{h0[0], h0[1], h1[0], h1[1], h2[0], h2[1], h3[0], h3[1]};
-                // row sums of P on the matrix core: a block of ones times P^T
-                acc_l[qb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, pf[qb][c], acc_l[qb], 0, 0, 0);
-            }
-        }
-
-        // ---- O^T += V^T P^T ---------------------------------------------------------------
-#pragma unroll
-        for (int c = 0; c < S::BN / 32; ++c) {
-#pragma unroll
-            for (int db = 0; db < S::NDB; ++db) {
-                half8_t vf;
-                if (c == 0 && db < NPF) {
-                    vf = vf0[db];
-                } else {
-                    const half4_t lo = lds_read_tr16(vl + voff[db] + (32 * c) * 2 * D);
-                    const half4_t hi = lds_read_tr16(vl + voff[db] + (32 * c + 16) * 2 * D);
-                    vf = half8_t{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+                    for (int kb = 0; kb < S::NKB; ++kb)
+                        kf[(c + 1) & 1][kb] = *reinterpret_cast<const half8_t*>(kl + koff[c + 1] + 16 * kb * 2 * D);
                 }
 #pragma unroll
-                for (int qb = 0; qb < S::QB; ++qb)
-                    acc_o[db][qb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf, pf[qb][c], acc_o[db][qb], 0, 0, 0);
+                for (int kb = 0; kb < S::NKB; ++kb)
+#pragma unroll
+                    for (int qb = 0; qb < S::QB; ++qb)
+                        st[kb][qb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf[c & 1][kb], qf[qb][c], st[kb][qb], 0, 0, 0);
+            }
+
+            // V^T fragments of the tile's first 32 keys, read ahead of the softmax so that their
+            // LDS latency overlaps it
+            constexpr int NPF = D >= 256 ? S::NDB / 2 : S::NDB;   // register budget
+            half8_t vf0[NPF];
+#pragma unroll
+            for (int db = 0; db < NPF; ++db) {
+                const half4_t lo = lds_read_tr16(vl + voff[db]);
+                const half4_t hi = lds_read_tr16(vl + voff[db] + 16 * 2 * D);
+                vf0[db] = half8_t{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+            }
+
+            // ---- online softmax in the S^T layout: lane = query (ln), keys 16kb + 4lg + i ----
+            // Uncapped scores stay raw (scale > 0 preserves the max); the scale is folded into
+            // the exponent: p = 2^(s * scale * log2 e - m).  Capped scores are turned into log2
+            // units first.  Masked keys get -inf added.
+            half8_t pf[S::QB][S::BN / 32];
+#pragma unroll
+            for (int qb = 0; qb < S::QB; ++qb) {
+                if constexpr (CAP) {
+#pragma unroll
+                    for (int kb = 0; kb < S::NKB; ++kb)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            const float e2 = fast_exp2(st[kb][qb][i] * K1);
+                            st[kb][qb][i] = __builtin_fmaf(-C2, fast_rcp(e2 + 1.f), C1);
+                        }
+                }
+                if (masked) {
+                    // visible keys of this row form [vlo, vhi]; key - vlo <= vhi - vlo (unsigned)
+                    const int off = ks + 4 * lg - vlo[qb];
+#pragma unroll
+                    for (int kb = 0; kb < S::NKB; ++kb)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i)
+                            st[kb][qb][i] = ((unsigned)(off + 16 * kb + i) <= vspan[qb]) ? st[kb][qb][i] : -INFINITY;
+                }
+                float mx = st[0][qb][0];
+#pragma unroll
+                for (int kb = 0; kb < S::NKB; ++kb)
+#pragma unroll
+                    for (int i = (kb == 0 ? 1 : 0); i < 4; ++i) mx = fmaxf(mx, st[kb][qb][i]);
+                mx = rows_max(mx);
+                const float mxl = mx * sc2;        // in log2 units
+                if (__builtin_amdgcn_ballot_w64(mxl > m_run[qb] + kSlack) != 0) {
+                    const float mnew = fmaxf(m_run[qb], mxl);
+                    const float alpha = fast_exp2(m_run[qb] - mnew);
+                    m_run[qb] = mnew;
+                    acc_l[qb] *= alpha;
+#pragma unroll
+                    for (int db = 0; db < S::NDB; ++db) acc_o[db][qb] *= alpha;
+                }
+                const float mq = m_run[qb];
+#pragma unroll
+                for (int kb = 0; kb < S::NKB; ++kb)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) st[kb][qb][i] = fast_exp2(__builtin_fmaf(st[kb][qb][i], sc2, -mq));
+#pragma unroll
+                for (int c = 0; c < S::BN / 32; ++c) {
+                    const half2_t h0 = __builtin_convertvector(float2_t{st[2 * c][qb][0], st[2 * c][qb][1]}, half2_t);
+                    const half2_t h1 = __builtin_convertvector(float2_t{st[2 * c][qb][2], st[2 * c][qb][3]}, half2_t);
+                    const half2_t h2 = __builtin_convertvector(float2_t{st[2 * c + 1][qb][0], st[2 * c + 1][qb][1]}, half2_t);
+                    const half2_t h3 = __builtin_convertvector(float2_t{st[2 * c + 1][qb][2], st[2 * c + 1][qb][3]}, half2_t);
+                    pf[qb][c] = half8_t{h0[0], h0[1], h1[0], h1[1], h2[0], h2[1], h3[0], h3[1]};
+                    // row sums of P on the matrix core: a block of ones times P^T
+                    acc_l[qb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, pf[qb][c], acc_l[qb], 0, 0, 0);
+                }
+            }
+
+            // ---- O^T += V^T P^T ---------------------------------------------------------------
+#pragma unroll
+            for (int c = 0; c < S::BN / 32; ++c) {
+#pragma unroll
+                for (int db = 0; db < S::NDB; ++db) {
+                    half8_t vf;
+                    if (c == 0 && db < NPF) {
+                        vf = vf0[db];
+                    } else {
+                        const half4_t lo = lds_read_tr16(vl + voff[db] + (32 * c) * 2 * D);
+                        const half4_t hi = lds_read_tr16(vl + voff[db] + (32 * c + 16) * 2 * D);
+                        vf = half8_t{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+                    }
+#pragma unroll
+                    for (int qb = 0; qb < S::QB; ++qb)
+                        acc_o[db][qb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf, pf[qb][c], acc_o[db][qb], 0, 0, 0);
+                }
             }
         }
-        }  // kt < kt1
         stage = (stage + 1 == NS) ? 0 : stage + 1;
     }
 
