@@ -637,6 +637,8 @@ def test_prefill_full_workload_sampled_rows(dev, c3_inputs):
     (1024, 1024, 16, 8, 128, 0),     # 256 workgroups of 64 rows: the unsplit configuration
     (64, 4096, 4, 2, 128, 0),        # a short chunk after a long cache: four key groups
     (100, 3000, 2, 1, 64, 700),      # key groups with a window and a ragged chunk
+    (1, 1, 4, 2, 128, 0),            # one query, one key: three of the four key groups idle
+    (1, 5000, 8, 8, 64, 0),          # one query against a long cache
 ])
 def test_prefill_both_configurations(dev, S, L, H, Hkv, D, W):
     """Grids that fill the device run 64-row workgroups; smaller ones run 32-row workgroups
@@ -646,7 +648,7 @@ def test_prefill_both_configurations(dev, S, L, H, Hkv, D, W):
     q, k, v = synth.prefill_inputs(synth.seed_of(3) + S + L, S, L, H, Hkv, D, "f16")
     got = run_prefill(dev, q, k, v, True, W, 0.0)
     assert np.all(np.isfinite(got))
-    rows = sorted(set([0, 1, 31, 32, S // 2, S - 2, S - 1]))
+    rows = sorted(set(r for r in (0, 1, 31, 32, S // 2, S - 2, S - 1) if 0 <= r < S))
     want = prefill_oracle_rows(q, k, v, rows, True, W, 0.0)
     assert maxabs(got[rows], want) < TOL_F16
 
