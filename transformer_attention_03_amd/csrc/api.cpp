@@ -493,22 +493,32 @@ int attn_decode_tiered_q8(const float* q, const void* hot_k, const void* hot_v, 
     DecodePlan plan = plan_decode(1, num_heads, num_kv_heads, head_dim, cold_vis + hot_vis, false);
     const int stride = workspace_row_splits(1, num_heads, num_kv_heads, head_dim, total);
     const int max_split = ta03::decode_max_split_tokens_paged();
-    int ts = g_split_override;
-    if (ts <= 0) {
+    // Split lengths in tokens, cold (tc) and hot (th): equal bytes per split, since a cold
+    // token carries 2D + 8 bytes (int8 K and V rows and their scales) and a hot one 4D (f16
+    // rows); the thread's split override sets both.
+    int tc = g_split_override, th = g_split_override;
+    if (tc <= 0) {
         int per_cu = ta03::decode_workgroups_per_cu(head_dim, false);
         const int per_cu_paged = ta03::decode_workgroups_per_cu(head_dim, true);
         if (per_cu_paged < per_cu) per_cu = per_cu_paged;
         const long chunks = (long)num_kv_heads * plan.nch;
         const long n_target = (256L * per_cu + chunks - 1) / chunks;
         const int unit = ta03::decode_waves(head_dim, true) * ta03::decode_tokens_per_block();
-        const long per = ((long)cold_vis + hot_vis + n_target - 1) / n_target;
-        ts = (int)(((per + unit - 1) / unit) * unit);
+        const long cold_b = (long)cold_vis * (2 * head_dim + 8), hot_b = (long)hot_vis * 4 * head_dim;
+        const long per_b = (cold_b + hot_b + n_target - 1) / n_target;
+        auto whole_rounds = [&](long t) { return (int)((((t < 1 ? 1 : t) + unit - 1) / unit) * unit); };
+        tc = whole_rounds(per_b / (2 * head_dim + 8));
+        th = whole_rounds(per_b / (4 * head_dim));
     }
-    if (ts > max_split) ts = max_split;
-    auto splits = [&](int t) { return (cold_vis + t - 1) / t + (hot_vis + t - 1) / t; };
-    while (splits(ts) > stride && ts < max_split) ts += 16;
-    if (splits(ts) > stride)
-        return fail(ATTN_ERR_UNSUPPORTED, "%s: %d splits needed but the workspace row holds %d", what, splits(ts),
+    if (tc > max_split) tc = max_split;
+    if (th > max_split) th = max_split;
+    auto splits = [&]() { return (cold_vis + tc - 1) / tc + (hot_vis + th - 1) / th; };
+    while (splits() > stride && (tc < max_split || th < max_split)) {
+        if (tc < max_split) tc += 16;
+        if (th < max_split) th += 16;
+    }
+    if (splits() > stride)
+        return fail(ATTN_ERR_UNSUPPORTED, "%s: %d splits needed but the workspace row holds %d", what, splits(),
                     stride);
     plan.n_split = stride;
     const WorkspaceLayout wl = workspace_layout(1, num_heads, num_kv_heads, head_dim, plan);
@@ -533,17 +543,17 @@ int attn_decode_tiered_q8(const float* q, const void* hot_k, const void* hot_v, 
     d.ring = hot_len > 0 ? hot_window : 1;
     d.num_pages = num_pages; d.max_pages = max_pages;
     fill_scalars(d, sliding_window, attn_softcap, scale);
-    d.split_tokens = ts;
+    d.split_tokens = th;
     d.n_split_max = stride;
     d.batch = 1;
     d.hot_k = hot_k; d.hot_v = hot_v;
     // position p of the hot tier lives at row (hot_start + p - cold_len) mod hot_window
     d.ring_off = hot_len > 0 ? (int)((((long)hot_start - cold_len) % hot_window + hot_window) % hot_window) : 0;
     d.tier_cold_len = cold_len;
-    d.tier_cold_splits = (cold_vis + ts - 1) / ts;
+    d.tier_cold_splits = (cold_vis + tc - 1) / tc;
     d.tier_k_lo = k_lo;
-    d.tier_cold_tokens = ts;
-    return launch_status(ta03::launch_decode_tiered(d, head_dim, plan.gc, splits(ts),
+    d.tier_cold_tokens = tc;
+    return launch_status(ta03::launch_decode_tiered(d, head_dim, plan.gc, splits(),
                                                     reinterpret_cast<hipStream_t>(stream)),
                          what);
 }
