@@ -549,7 +549,7 @@ def cpu_baseline(wl, budget_s=10.0):
 def main():
     a = parse()
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path (the hot path "
+        print("bench.py measures one GPU: the library has no multi-GPU path (the hot path "
               "shards by head, query block or sequence with no exchange; see the design notes). "
               "Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
