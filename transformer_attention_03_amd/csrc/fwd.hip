@@ -92,8 +92,11 @@ __device__ __forceinline__ void work_item(const FwdParams& a, int& head, int& qb
     qblock = a.causal ? a.n_qblocks - 1 - qb : qb;
 }
 
+// Scaled score in log2 units, capped when CAP (a compile-time choice, so the per-element
+// code has no branch).
+template <bool CAP>
 __device__ __forceinline__ float score_transform(const FwdParams& a, float s) {
-    if (a.softcap > 0.f) return a.softcap * tanh_via_exp(s * a.scale * a.inv_softcap) * kLog2e;
+    if constexpr (CAP) return a.softcap * tanh_via_exp(s * a.scale * a.inv_softcap) * kLog2e;
     return s * a.scale_log2;
 }
 
@@ -547,7 +550,7 @@ struct F32Shape {
     static constexpr int DC = D / 4;
 };
 
-template <int D>
+template <int D, bool CAP>
 __global__ void __launch_bounds__(256) fwd_f32_kernel(FwdParams a) {
     using S = F32Shape<D>;
     __shared__ float k_lds[S::BN * S::LD];
@@ -628,16 +631,22 @@ __global__ void __launch_bounds__(256) fwd_f32_kernel(FwdParams a) {
                 const float kf = k_lds[(16 * kb + ln) * S::LD + 4 * c + lg];
                 st[kb] = __builtin_amdgcn_mfma_f32_16x16x4f32(kf, qf[c], st[kb], 0, 0, 0);
             }
+#pragma unroll
+        for (int kb = 0; kb < S::NKB; ++kb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) st[kb][i] = score_transform<CAP>(a, st[kb][i]);
+        if (masked) {
+#pragma unroll
+            for (int kb = 0; kb < S::NKB; ++kb)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    st[kb][i] = visible(a, ks + 16 * kb + 4 * lg + i, qpos) ? st[kb][i] : -INFINITY;
+        }
         float mx = -INFINITY;
 #pragma unroll
         for (int kb = 0; kb < S::NKB; ++kb)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                float t = score_transform(a, st[kb][i]);
-                if (masked) t += visible(a, ks + 16 * kb + 4 * lg + i, qpos) ? 0.f : -INFINITY;
-                st[kb][i] = t;
-                mx = fmaxf(mx, t);
-            }
+            for (int i = 0; i < 4; ++i) mx = fmaxf(mx, st[kb][i]);
         mx = fmaxf(mx, shfl_xor_f(mx, 16));
         mx = fmaxf(mx, shfl_xor_f(mx, 32));
         if (__builtin_amdgcn_ballot_w64(mx > m_run + kSlack) != 0) {
@@ -730,7 +739,10 @@ hipError_t launch_d(const FwdParams& p, int dtype, hipStream_t st) {
         }
         return launch_f16<D, F16Cfg<D>>(p, grid, st);
     } else {
-        hipLaunchKernelGGL(fwd_f32_kernel<D>, grid, dim3(256), 0, st, p);
+        if (p.softcap > 0.f)
+            hipLaunchKernelGGL((fwd_f32_kernel<D, true>), grid, dim3(256), 0, st, p);
+        else
+            hipLaunchKernelGGL((fwd_f32_kernel<D, false>), grid, dim3(256), 0, st, p);
     }
     return hipGetLastError();
 }
