@@ -752,6 +752,9 @@ __global__ void __launch_bounds__((DecShape<D, PAGED>::NT)) decode_split_kernel(
         // of sequence b, where sequence i gets lb_i = ceil(len_i / kMaxSplitTokens) splits
         // plus its share, by length, of the remaining workgroups (at most one block round per
         // wave less than a split).  Every workgroup derives the same assignment from kv_lens.
+        // The lengths are read 64 sequences per load, one per lane (each load is a round trip
+        // to memory that is busy with the cache stream, so a per-sequence loop would cost
+        // microseconds); sums, the prefix of split counts and the owner search are wave-wide.
         const int max_len = a.max_pages * 16;
         auto eff_of = [&](int li) {
             const bool valid = li >= 1 && li <= max_len;
@@ -759,31 +762,45 @@ __global__ void __launch_bounds__((DecShape<D, PAGED>::NT)) decode_split_kernel(
         };
         long tot = 0;
         int lb_sum = 0;
-        for (int i = 0; i < a.batch; ++i) {
-            const int e = eff_of(a.kv_lens[i]);
-            tot += e;
-            lb_sum += e > 0 ? (e + kMaxSplitTokens - 1) / kMaxSplitTokens : 1;
+        int len0 = 0;                             // lane's length in the first 64 sequences
+        for (int i0 = 0; i0 < a.batch; i0 += 64) {
+            const int i = i0 + lane;
+            const int li = i < a.batch ? a.kv_lens[i] : 0;
+            if (i0 == 0) len0 = li;
+            const int e = eff_of(li);             // <= 2^20 (host-checked), so 64 fit an int
+            const int lb = i < a.batch ? (e > 0 ? (e + kMaxSplitTokens - 1) / kMaxSplitTokens : 1) : 0;
+            tot += wave_sum_i(e);
+            lb_sum += wave_sum_i(lb);
         }
         const int extra = max(0, (int)gridDim.x - lb_sum);
         const int p = blockIdx.x;
         int cum = 0, nb_b = 0;
         b = -1;
-        for (int i = 0; i < a.batch; ++i) {
-            const int e = eff_of(a.kv_lens[i]);
+        L = 0;
+        for (int i0 = 0; i0 < a.batch && b < 0; i0 += 64) {
+            const int i = i0 + lane;
+            const int li = i < a.batch ? (i0 == 0 ? len0 : a.kv_lens[i]) : 0;
+            const int e = eff_of(li);
             const int lb = e > 0 ? (e + kMaxSplitTokens - 1) / kMaxSplitTokens : 1;
             int n = lb + (tot > 0 ? (int)((long)extra * e / tot) : 0);
             n = min(n, max(lb, (e + NW * kTB - 1) / (NW * kTB)));
             n = min(n, a.n_split_max);
-            if (p < cum + n) {
-                b = i;
-                nb_b = n;
-                break;
+            if (i >= a.batch) n = 0;
+            const int incl = wave_incl_scan_i(n);  // splits of sequences i0 .. i
+            // the owner is the first sequence whose splits reach past workgroup p
+            const uint64_t hit = __builtin_amdgcn_ballot_w64(i < a.batch && p < cum + incl);
+            if (hit) {
+                const int j = __builtin_ctzll(hit);
+                b = i0 + j;
+                nb_b = __builtin_amdgcn_readlane(n, j);
+                cum += __builtin_amdgcn_readlane(incl, j) - nb_b;
+                L = __builtin_amdgcn_readlane(li, j);
+            } else {
+                cum += __builtin_amdgcn_readlane(incl, 63);
             }
-            cum += n;
         }
         if (b < 0) return;                        // more workgroups than splits
         split = p - cum;
-        L = a.kv_lens[b];
         if (L < 1 || L > max_len) {
             // out of contract: the row becomes NaN; nothing else is read
             if (split == 0)

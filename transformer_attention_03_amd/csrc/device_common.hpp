@@ -59,6 +59,22 @@ __device__ __forceinline__ float group_sum(float x) {
     return x;
 }
 
+// Integer sum over the wave (every lane gets it) and inclusive prefix sum by lane.
+__device__ __forceinline__ int wave_sum_i(int x) {
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1) x += __shfl_xor(x, m, 64);
+    return x;
+}
+__device__ __forceinline__ int wave_incl_scan_i(int x) {
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int y = __shfl_up(x, o, 64);
+        if (lane >= o) x += y;
+    }
+    return x;
+}
+
 // Max over lanes that are congruent modulo N (N = 1..64, power of two): reduces across
 // the 64/N groups of N lanes.  Every lane gets the max of its residue class.
 template <int N>
