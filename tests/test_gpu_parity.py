@@ -298,6 +298,10 @@ def test_paged_q8_relative_accuracy(dev, lens, H, Hkv, D, vf):
     ([33, 4000, 1, 700, 16], 32, 2, 64),               # sixteen query heads per KV head
     ([1, 32768], 8, 2, 128),                            # one token next to a 32K sequence
     ([(7 * i) % 200 + 1 for i in range(40)], 8, 4, 128),  # forty short sequences
+    # more than 64 sequences: the lengths are read 64 per load, so the owner of a workgroup
+    # may sit in the second or third load
+    ([(13 * i) % 300 + 1 for i in range(150)], 8, 4, 128),
+    ([2000 if i % 9 == 0 else (5 * i) % 90 + 1 for i in range(70)], 8, 2, 64),
 ])
 def test_paged_q8_batch_balance(dev, lens, H, Hkv, D):
     """The paged kernel shares its workgroups out over the batch by length: skewed and wide
