@@ -145,8 +145,9 @@ __device__ __forceinline__ float pow2i(int e) {
 // int8 -> f16 for the MFMA operands without any arithmetic: with u = b + 128 (sign bit
 // flipped) the f16 bit pattern 0x3C00 | u is exactly 1 + u / 1024.  For such values x a
 // product sum obeys  sum y b = 1024 sum y x - 1152 sum y,  so the kernel subtracts the
-// second term once per score (K) or once at the end (V).  A dword gives the f16 pairs
-// (u0, u2) and (u1, u3): the other operand of the product uses the same element order.
+// second term once per score (K) or once per block and O^T tile (V).  A dword gives the
+// f16 pairs (u0, u2) and (u1, u3): the other operand of the product uses the same element
+// order.
 __device__ __forceinline__ void i8x4_biased(uint32_t w, uint32_t& even, uint32_t& odd) {
     w ^= 0x80808080u;
     even = __builtin_amdgcn_perm(0x3C3C3C3Cu, w, 0x04020400u);
@@ -292,7 +293,6 @@ struct WaveAcc {
     float4_t o[D / 16];   // O^T tiles: column lane % 16, d = 16 dt + 4 (lane / 16) + v
     float m;              // running max of the column's head (log2 units)
     float l;              // this lane's share of the running sum of p
-    float xs;             // paged: this lane's share of the sum of the PV operand values
     int e;                // paged: running exponent of the largest V scale (wave-uniform)
 };
 
@@ -415,7 +415,6 @@ __device__ __forceinline__ void process_block(const char* slot, int tb, int t_en
         const float al = fast_exp2(A.m - mn);          // 0 on the first block (m = -inf)
         const float ao = al * pow2i(A.e - en);
         A.l *= al;
-        A.xs *= ao;
 #pragma unroll
         for (int dt = 0; dt < S::DT; ++dt) A.o[dt] *= ao;
         A.m = mn;
@@ -430,7 +429,6 @@ __device__ __forceinline__ void process_block(const char* slot, int tb, int t_en
         const float p = fast_exp2(s[v] - A.m);
         A.l += p;
         xv[v] = PAGED ? p * vs[v] * pe : p;
-        if constexpr (PAGED) A.xs += xv[v];
     }
     // paged: token order (0, 2, 1, 3), the order of the biased int8 V operand
     const half4_t pb = PAGED ? half4_t{split_part(xv[0], odd), split_part(xv[2], odd),
@@ -439,6 +437,16 @@ __device__ __forceinline__ void process_block(const char* slot, int tb, int t_en
                                        split_part(xv[2], odd), split_part(xv[3], odd)};
 
     // ---- O^T += V^T P^T --------------------------------------------------------------------
+    // int8 V enters as (1152 + v) / 1024.  The bias part, 1.125 * sum_t p_t for every row d, is
+    // taken out of each O^T tile block by block (one product with a constant -1.125 operand),
+    // so the accumulators keep the size of the output and their f32 rounding does not grow
+    // with the number of blocks a wave accumulates.
+    if constexpr (PAGED) {
+        const half4_t nbias = {(_Float16)-1.125f, (_Float16)-1.125f, (_Float16)-1.125f, (_Float16)-1.125f};
+        const float4_t nb = __builtin_amdgcn_mfma_f32_16x16x16f16(nbias, pb, float4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+#pragma unroll
+        for (int dt = 0; dt < S::DT; ++dt) A.o[dt] += nb;
+    }
 #pragma unroll
     for (int i = 0; i < NVR; ++i) {
         if constexpr (PAGED) {
@@ -559,7 +567,6 @@ __device__ __forceinline__ void split_partial(const DecodeParams& a, const TierS
     for (int dt = 0; dt < S::DT; ++dt) A.o[dt] = float4_t{0.f, 0.f, 0.f, 0.f};
     A.m = -INFINITY;
     A.l = 0.f;
-    A.xs = 0.f;
     A.e = PAGED ? -126 : 0;
 
     for (int k = 0; k < nb; ++k) {
@@ -583,7 +590,6 @@ __device__ __forceinline__ void split_partial(const DecodeParams& a, const TierS
     // ---- finish the wave: pair sums (hi + lo columns), row sums over the 16-lane rows ------
     const float lw = rows_sum(A.l);
     const float oscale = PAGED ? pow2i(A.e) : 1.f;
-    const float vbias = PAGED ? 1152.f * rows_sum(A.xs) : 0.f;   // int8 V: 1152 * sum of operands
     __syncthreads();                      // every wave is done with its ring
     {
         const bool writer = (col & 1) == 0 && hq < GC;
@@ -592,7 +598,7 @@ __device__ __forceinline__ void split_partial(const DecodeParams& a, const TierS
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
                 float o = A.o[dt][v] + dpp_f<kDppXor1>(A.o[dt][v]);
-                if constexpr (PAGED) o = __builtin_fmaf(o, 1024.f, -vbias);
+                if constexpr (PAGED) o *= 1024.f;
                 o *= oscale;
                 if (writer) lds_o[w][hq][16 * dt + 4 * (lane >> 4) + v] = o;
             }
