@@ -294,6 +294,25 @@ def test_paged_q8_relative_accuracy(dev, lens, H, Hkv, D, vf):
     assert maxabs(got, want) < 5e-5 * np.abs(want).max()
 
 
+def test_paged_q8_error_does_not_grow_with_split_length(dev):
+    """int8 V enters the products with a bias of 1.125 per weight, which leaves the
+    accumulators block by block: a 4096-token split (32 blocks per wave) keeps the accuracy
+    of a 256-token one."""
+    say("paged error against split length")
+    d = synth.paged_inputs(synth.seed_of(5) + 991, 1, 8, 2, 128, [32768], n_poison=3)
+    want = paged_oracle(d)
+    errs = []
+    try:
+        for ts in (256, 4096):
+            ta.attn_set_decode_split(ts)
+            got = run_paged(dev, d)
+            errs.append(maxabs(got, want) / np.abs(want).max())
+    finally:
+        ta.attn_set_decode_split(0)
+    say("relative errors %s" % errs)
+    assert max(errs) < 1e-5
+
+
 @pytest.mark.parametrize("lens,H,Hkv,D", [
     ([33, 4000, 1, 700, 16], 32, 2, 64),               # sixteen query heads per KV head
     ([1, 32768], 8, 2, 128),                            # one token next to a 32K sequence
