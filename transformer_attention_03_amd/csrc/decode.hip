@@ -592,19 +592,26 @@ __device__ __forceinline__ void split_partial(const DecodeParams& a, const TierS
     const float oscale = PAGED ? pow2i(A.e) : 1.f;
     __syncthreads();                      // every wave is done with its ring
     {
+        // all pair sums first, then one 16-byte write per O^T tile under a single mask (a
+        // masked write per element costs an exec save/restore each)
         const bool writer = (col & 1) == 0 && hq < GC;
+        float4_t ov[S::DT];
 #pragma unroll
         for (int dt = 0; dt < S::DT; ++dt)
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
                 float o = A.o[dt][v] + dpp_f<kDppXor1>(A.o[dt][v]);
                 if constexpr (PAGED) o *= 1024.f;
-                o *= oscale;
-                if (writer) lds_o[w][hq][16 * dt + 4 * (lane >> 4) + v] = o;
+                ov[dt][v] = o * oscale;
             }
-        if (writer && lane < 16) {
-            lds_m[w][hq] = A.m;
-            lds_l[w][hq] = lw;
+        if (writer) {
+#pragma unroll
+            for (int dt = 0; dt < S::DT; ++dt)
+                *reinterpret_cast<float4_t*>(&lds_o[w][hq][16 * dt + 4 * (lane >> 4)]) = ov[dt];
+            if (lane < 16) {
+                lds_m[w][hq] = A.m;
+                lds_l[w][hq] = lw;
+            }
         }
     }
     __syncthreads();
