@@ -473,6 +473,11 @@ struct TierSrc {
     int ring, ring_off;
 };
 
+// 16-byte entries per query chunk in the caller's qx buffer: the f16 bodies stage the f32
+// query there first (two float4 per lane); the int8 body loads it straight to registers.
+template <bool PAGED>
+constexpr int qx_entries() { return PAGED ? 64 : 128; }
+
 // One split: stream tokens [t_begin, t_end) of KV head kvh through the waves, merge the
 // waves, and either write the output (a single split) or publish the split's partial
 // (m, l, o) for the last-arriving workgroup.  LDS is the caller's, so that one kernel can
@@ -480,12 +485,13 @@ struct TierSrc {
 template <int D, int GC, bool PAGED, bool CAP, bool RING>
 __device__ __forceinline__ void split_partial(const DecodeParams& a, const TierSrc& src, char* rings,
                                               float (*lds_m)[GC], float (*lds_l)[GC], int* lds_pages,
-                                              half8_t (*lds_qx)[64], float (*lds_qs)[64], int b,
+                                              half8_t* lds_qx, float (*lds_qs)[64], int b,
                                               int split, int n_live, int t_begin, int t_end, int kvh,
                                               int h0) {
     using S = DecShape<D, PAGED>;
     constexpr int NW = S::NW;
     constexpr int NT = S::NT;
+    constexpr int QXN = qx_entries<PAGED>();
     const int lane = threadIdx.x & 63;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     float(*lds_o)[GC][D] = reinterpret_cast<float(*)[GC][D]>(rings);                    // [NW][GC][D]
@@ -516,6 +522,18 @@ __device__ __forceinline__ void split_partial(const DecodeParams& a, const TierS
     const int first = t_begin + w * kTB;
     const int nb = first < t_end ? (t_end - first + STRIDE - 1) / STRIDE : 0;
     const DmaLane<D, PAGED> dl = dma_lane<D, PAGED>(lane, (uint32_t)S::RB);
+    const int col = lane & 15;
+    const int hq = col >> 1;
+    const float* qh = a.q + ((size_t)b * a.H + h0 + min(hq, GC - 1)) * D + 8 * (lane >> 4);
+    // f16 bodies: the query chunks this wave converts come in by DMA ahead of the ring, so a
+    // counted wait covers them alone and block 0 can be processed while later blocks are in
+    // flight (a plain load would be waited for together with every DMA before it).  The two
+    // float4 of a lane land in the 2 KB of qx chunk kc, whose first half becomes qx.
+    if constexpr (!PAGED)
+        for (int kc = w; kc < S::KC; kc += NW) {
+            dma16(qh + 32 * kc, lds_qx + kc * QXN);
+            dma16(qh + 32 * kc + 4, lds_qx + kc * QXN + 64);
+        }
 #pragma unroll
     for (int k = 0; k < S::RING; ++k)
         if (k < nb) dma_block<D, PAGED, RING>(ring + k * S::SLOT, c, dl, first + k * STRIDE, t_end, lane);
@@ -526,18 +544,32 @@ __device__ __forceinline__ void split_partial(const DecodeParams& a, const TierS
     // out in log2 units (or as the tanh argument when a cap is set).
     const float qmul = CAP ? a.scale * a.inv_softcap : a.scale_log2;
     const float cap_log2 = a.softcap * kLog2e;
-    const int col = lane & 15;
-    const int hq = col >> 1;
     // Computed once per workgroup: wave w converts the d chunks kc = w, w + NW, ... and
     // every wave reads all of them back from LDS.
     half8_t qx[S::KC];
     float qbias;
     {
         constexpr int kOrder[8] = {0, 2, 1, 3, 4, 6, 5, 7};
-        const float* qh = a.q + ((size_t)b * a.H + h0 + min(hq, GC - 1)) * D + 8 * (lane >> 4);
+        if constexpr (!PAGED) {
+            if (w < S::KC) {
+                // the query DMAs were issued before the ring's min(nb, RING) blocks
+                const int issued = min(nb, S::RING);
+                if constexpr (S::RING >= 4) { if (issued == 4) wait_vmem_at_most<4 * S::NDMA>(); }
+                if constexpr (S::RING >= 3) { if (issued == 3) wait_vmem_at_most<3 * S::NDMA>(); }
+                if (issued == 2) wait_vmem_at_most<2 * S::NDMA>();
+                else if (issued == 1) wait_vmem_at_most<S::NDMA>();
+                else if (issued == 0) wait_vmem_at_most<0>();
+            }
+        }
         for (int kc = w; kc < S::KC; kc += NW) {
-            const float4_t x0 = *reinterpret_cast<const float4_t*>(qh + 32 * kc);
-            const float4_t x1 = *reinterpret_cast<const float4_t*>(qh + 32 * kc + 4);
+            float4_t x0, x1;
+            if constexpr (PAGED) {
+                x0 = *reinterpret_cast<const float4_t*>(qh + 32 * kc);
+                x1 = *reinterpret_cast<const float4_t*>(qh + 32 * kc + 4);
+            } else {
+                x0 = reinterpret_cast<const float4_t*>(lds_qx + kc * QXN)[lane];
+                x1 = reinterpret_cast<const float4_t*>(lds_qx + kc * QXN + 64)[lane];
+            }
             const float qf[8] = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
             half8_t h;
             float qs = 0.f;
@@ -547,14 +579,14 @@ __device__ __forceinline__ void split_partial(const DecodeParams& a, const TierS
                 h[e] = split_part(x, col & 1);
                 qs += (float)h[e];
             }
-            lds_qx[kc][lane] = h;
+            lds_qx[kc * QXN + lane] = h;
             lds_qs[kc][lane] = qs;
         }
         __syncthreads();
         float qsum = 0.f;
 #pragma unroll
         for (int kc = 0; kc < S::KC; ++kc) {
-            qx[kc] = lds_qx[kc][lane];
+            qx[kc] = lds_qx[kc * QXN + lane];
             qsum += lds_qs[kc][lane];
         }
         // int8 K: the bias term 1152 * sum_d q[d] of the head (hi + lo columns, all rows)
@@ -747,7 +779,7 @@ __global__ void __launch_bounds__((DecShape<D, PAGED>::NT)) decode_split_kernel(
     __shared__ float lds_l[NW][GC];
     __shared__ int lds_pages[PAGED ? kMaxSplitTokens / 16 + 1 : 1];
     __shared__ int lds_last;
-    __shared__ half8_t lds_qx[S::KC][64];
+    __shared__ __attribute__((aligned(1024))) half8_t lds_qx[S::KC][qx_entries<PAGED>()];
     __shared__ float lds_qs[S::KC][64];
     static_assert(sizeof(float) * NW * GC * D <= NW * S::WAVE_LDS, "merge buffer fits in the rings");
 
@@ -840,7 +872,7 @@ __global__ void __launch_bounds__((DecShape<D, PAGED>::NT)) decode_split_kernel(
     }
 
     const TierSrc src{a.k, a.v, a.k_scales, a.v_scales, RING ? a.ring : 0, 0};
-    split_partial<D, GC, PAGED, CAP, RING>(a, src, rings, lds_m, lds_l, lds_pages, lds_qx, lds_qs, b, split,
+    split_partial<D, GC, PAGED, CAP, RING>(a, src, rings, lds_m, lds_l, lds_pages, &lds_qx[0][0], lds_qs, b, split,
                                            n_live, t_begin, t_end, kvh, h0);
     if (n_live == 1) return;
     merge_splits<D, GC, NT, merge_chunk<D, GC, PAGED>()>(a, rings, &lds_last, b, h0, n_live);
@@ -870,7 +902,7 @@ __global__ void __launch_bounds__((DecShape<D, true>::NT)) decode_tiered_kernel(
     __shared__ float lds_l[SP::NW][GC];
     __shared__ int lds_pages[kMaxSplitTokens / 16 + 1];
     __shared__ int lds_last;
-    __shared__ half8_t lds_qx[SP::KC][64];
+    __shared__ __attribute__((aligned(1024))) half8_t lds_qx[SP::KC][qx_entries<false>()];   // both bodies
     __shared__ float lds_qs[SP::KC][64];
     static_assert(sizeof(float) * SP::NW * GC * D <= RB, "merge buffer fits in the rings");
     constexpr int CS = (RB / 4) / (GC * (D + 2)) > kMaxSplits ? kMaxSplits : (RB / 4) / (GC * (D + 2));
@@ -885,13 +917,13 @@ __global__ void __launch_bounds__((DecShape<D, true>::NT)) decode_tiered_kernel(
         const int t_begin = a.tier_k_lo + split * a.tier_cold_tokens;
         const int t_end = min(a.tier_cold_len, t_begin + a.tier_cold_tokens);
         const TierSrc src{a.k, a.v, a.k_scales, a.v_scales, 0, 0};
-        split_partial<D, GC, true, CAP, false>(a, src, rings, lds_m, lds_l, lds_pages, lds_qx, lds_qs, 0,
+        split_partial<D, GC, true, CAP, false>(a, src, rings, lds_m, lds_l, lds_pages, &lds_qx[0][0], lds_qs, 0,
                                                split, n_live, t_begin, t_end, kvh, h0);
     } else {
         const int t_begin = max(a.tier_k_lo, a.tier_cold_len) + (split - a.tier_cold_splits) * a.split_tokens;
         const int t_end = min(a.kv_len, t_begin + a.split_tokens);
         const TierSrc src{a.hot_k, a.hot_v, nullptr, nullptr, a.ring, a.ring_off};
-        split_partial<D, GC, false, CAP, true>(a, src, rings, lds_m, lds_l, lds_pages, lds_qx, lds_qs, 0,
+        split_partial<D, GC, false, CAP, true>(a, src, rings, lds_m, lds_l, lds_pages, &lds_qx[0][0], lds_qs, 0,
                                                split, n_live, t_begin, t_end, kvh, h0);
     }
     if (n_live == 1) return;
