@@ -320,7 +320,7 @@ class Forward(Workload):
             self.S, self.H, self.Hkv, self.D, self.causal, self.W, self.cap = 128, 1, 1, 64, True, 0, 0.0
             q, k, v = synth.prefill_inputs(synth.seed_of(1), 128, 128, 1, 1, 64, "f32")
             self.kind = "f32"
-            self.kernel = "fwd_f32_kernel<64, false>"
+            self.kernel = "fwd_f32_kernel<64, false, true>"
             self.desc = {"workload": "causal prefill, f32, 1 sequence, 1 head, seq_len 128, "
                                      "head_dim 64, scale 1/8"}
         elif name == "prefill_f16":

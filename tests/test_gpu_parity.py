@@ -623,6 +623,8 @@ def test_prefill_f16(dev, D, S, L, causal, W, cap):
     (64, 100, 250, 2, 1, True, 0, 0.0),
     (128, 70, 70, 4, 2, True, 16, 0.0),
     (256, 65, 65, 2, 2, False, 0, 10.0),
+    (128, 40, 90, 3, 1, True, 0, 5.0),         # key groups with a cap and three heads per KV head
+    (64, 520, 520, 8, 2, True, 0, 0.0),        # 72 workgroups of 64 rows: no key groups
 ])
 def test_prefill_f32(dev, D, S, L, H, Hkv, causal, W, cap):
     say("prefill f32 D=%d S=%d L=%d" % (D, S, L))

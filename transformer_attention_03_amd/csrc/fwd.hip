@@ -550,9 +550,15 @@ struct F32Shape {
     static constexpr int DC = D / 4;
 };
 
-template <int D, bool CAP>
+// KG (key groups, for grids too small to fill the device): the four waves share one 16-row
+// query block and wave w takes key block w (16 keys) of every tile, so each wave does a
+// quarter of the products; the four partial softmaxes are folded by log-sum-exp at the end.
+template <int D, bool CAP, bool KG>
 __global__ void __launch_bounds__(256) fwd_f32_kernel(FwdParams a) {
     using S = F32Shape<D>;
+    constexpr int BM = KG ? 16 : S::BM;
+    constexpr int NKBW = KG ? 1 : S::NKB;          // key blocks of a tile per wave
+    static_assert(!KG || S::NKB == 4, "key groups take one of the four 16-key blocks of a tile");
     __shared__ float k_lds[S::BN * S::LD];
     __shared__ float v_lds[S::BN * S::LD];
 
@@ -565,15 +571,15 @@ __global__ void __launch_bounds__(256) fwd_f32_kernel(FwdParams a) {
     int head, qblock;
     work_item(a, head, qblock);
     const int kvh = head / (a.H / a.Hkv);
-    const int q0 = qblock * S::BM;
-    if (!resolve_kv_len<float, D>(a, head, q0, S::BM)) return;
-    const TileRange tr = tile_range(a, q0, S::BM, S::BN);
+    const int q0 = qblock * BM;
+    if (!resolve_kv_len<float, D>(a, head, q0, BM)) return;
+    const TileRange tr = tile_range(a, q0, BM, S::BN);
 
     const float* qg = reinterpret_cast<const float*>(a.q) + (long)head * a.q_head;
     const float* kg = reinterpret_cast<const float*>(a.k) + (long)kvh * a.k_head;
     const float* vg = reinterpret_cast<const float*>(a.v) + (long)kvh * a.k_head;
 
-    const int row = q0 + w * 16 + ln;
+    const int row = q0 + (KG ? 0 : w * 16) + ln;
     const int qpos = a.kv_len - a.seq_len + row;
     float qf[S::DC];
     {
@@ -620,31 +626,32 @@ __global__ void __launch_bounds__(256) fwd_f32_kernel(FwdParams a) {
         const int ks = kt * S::BN;
         const bool masked = tile_needs_mask(a, tr, ks, S::BN);
 
-        // NKB independent accumulation chains, interleaved
-        float4_t st[S::NKB];
+        // NKBW independent accumulation chains, interleaved; key block kbi(kb) of the tile
+        auto kbi = [&](int kb) { return KG ? w : kb; };
+        float4_t st[NKBW];
 #pragma unroll
-        for (int kb = 0; kb < S::NKB; ++kb) st[kb] = float4_t{0.f, 0.f, 0.f, 0.f};
+        for (int kb = 0; kb < NKBW; ++kb) st[kb] = float4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int c = 0; c < S::DC; ++c)
 #pragma unroll
-            for (int kb = 0; kb < S::NKB; ++kb) {
-                const float kf = k_lds[(16 * kb + ln) * S::LD + 4 * c + lg];
+            for (int kb = 0; kb < NKBW; ++kb) {
+                const float kf = k_lds[(16 * kbi(kb) + ln) * S::LD + 4 * c + lg];
                 st[kb] = __builtin_amdgcn_mfma_f32_16x16x4f32(kf, qf[c], st[kb], 0, 0, 0);
             }
 #pragma unroll
-        for (int kb = 0; kb < S::NKB; ++kb)
+        for (int kb = 0; kb < NKBW; ++kb)
 #pragma unroll
             for (int i = 0; i < 4; ++i) st[kb][i] = score_transform<CAP>(a, st[kb][i]);
         if (masked) {
 #pragma unroll
-            for (int kb = 0; kb < S::NKB; ++kb)
+            for (int kb = 0; kb < NKBW; ++kb)
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
-                    st[kb][i] = visible(a, ks + 16 * kb + 4 * lg + i, qpos) ? st[kb][i] : -INFINITY;
+                    st[kb][i] = visible(a, ks + 16 * kbi(kb) + 4 * lg + i, qpos) ? st[kb][i] : -INFINITY;
         }
         float mx = -INFINITY;
 #pragma unroll
-        for (int kb = 0; kb < S::NKB; ++kb)
+        for (int kb = 0; kb < NKBW; ++kb)
 #pragma unroll
             for (int i = 0; i < 4; ++i) mx = fmaxf(mx, st[kb][i]);
         mx = fmaxf(mx, shfl_xor_f(mx, 16));
@@ -658,7 +665,7 @@ __global__ void __launch_bounds__(256) fwd_f32_kernel(FwdParams a) {
             for (int db = 0; db < S::NDB; ++db) acc_o[db] *= alpha;
         }
 #pragma unroll
-        for (int kb = 0; kb < S::NKB; ++kb)
+        for (int kb = 0; kb < NKBW; ++kb)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const float p = fast_exp2(st[kb][i] - m_run);
@@ -668,12 +675,12 @@ __global__ void __launch_bounds__(256) fwd_f32_kernel(FwdParams a) {
         // O^T += V^T P^T, four keys {16kb + 4g + i : g} per product; the NDB output blocks
         // are independent chains, interleaved
 #pragma unroll
-        for (int kb = 0; kb < S::NKB; ++kb)
+        for (int kb = 0; kb < NKBW; ++kb)
 #pragma unroll
             for (int i = 0; i < 4; ++i)
 #pragma unroll
                 for (int db = 0; db < S::NDB; ++db) {
-                    const float vf = v_lds[(16 * kb + 4 * lg + i) * S::LD + 16 * db + ln];
+                    const float vf = v_lds[(16 * kbi(kb) + 4 * lg + i) * S::LD + 16 * db + ln];
                     acc_o[db] = __builtin_amdgcn_mfma_f32_16x16x4f32(vf, st[kb][i], acc_o[db], 0, 0, 0);
                 }
     }
@@ -681,8 +688,52 @@ __global__ void __launch_bounds__(256) fwd_f32_kernel(FwdParams a) {
     float l = l_part;
     l += shfl_xor_f(l, 16);
     l += shfl_xor_f(l, 32);
-    const float inv = l != 0.f ? 1.0f / l : 0.f;
     float* og = reinterpret_cast<float*>(a.o) + (long)head * a.o_head;
+    if constexpr (KG) {
+        // Fold the four key groups.  The tile buffers are free after the barrier: O^T
+        // partials [wave][d][column] go to k_lds for d < D/2 and to v_lds for the rest
+        // (4 * D/2 * 16 floats each, within BN * LD), maxima and sums to kg_ml.
+        __shared__ float kg_ml[2][4][16];
+        auto po = [&](int ww, int d) -> float& {
+            return d < D / 2 ? k_lds[(ww * (D / 2) + d) * 16 + ln] : v_lds[(ww * (D / 2) + d - D / 2) * 16 + ln];
+        };
+        __syncthreads();
+#pragma unroll
+        for (int db = 0; db < S::NDB; ++db)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) po(w, 16 * db + 4 * lg + i) = acc_o[db][i];
+        if (lg == 0) {
+            kg_ml[0][w][ln] = m_run;
+            kg_ml[1][w][ln] = l;
+        }
+        __syncthreads();
+        float M = kg_ml[0][0][ln];
+#pragma unroll
+        for (int ww = 1; ww < 4; ++ww) M = fmaxf(M, kg_ml[0][ww][ln]);
+        float f[4], L = 0.f;
+#pragma unroll
+        for (int ww = 0; ww < 4; ++ww) {
+            f[ww] = fast_exp2(kg_ml[0][ww][ln] - M);
+            L += f[ww] * kg_ml[1][ww][ln];
+        }
+        const float inv = L != 0.f ? 1.0f / L : 0.f;
+        if (row < a.seq_len) {
+            // wave w writes the output tiles db = w, w + 4, ...
+            for (int db = w; db < S::NDB; db += 4) {
+                float r[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    float o = 0.f;
+#pragma unroll
+                    for (int ww = 0; ww < 4; ++ww) o += f[ww] * po(ww, 16 * db + 4 * lg + i);
+                    r[i] = o * inv;
+                }
+                *reinterpret_cast<float4*>(og + (long)row * a.o_row + 16 * db + 4 * lg) = float4{r[0], r[1], r[2], r[3]};
+            }
+        }
+        return;
+    }
+    const float inv = l != 0.f ? 1.0f / l : 0.f;
     if (row < a.seq_len) {
 #pragma unroll
         for (int db = 0; db < S::NDB; ++db) {
@@ -730,6 +781,21 @@ hipError_t launch_f16(const FwdParams& p, dim3 grid, hipStream_t st) {
     return hipGetLastError();
 }
 
+// f32 grids of fewer than 64 workgroups of 64 rows run key groups (16-row workgroups), where
+// a tile holds four 16-key blocks (head_dim 64 and 128: 64-key tiles).
+bool use_f32_key_groups(int head_dim, int seq_len, int H) {
+    return head_dim <= 128 && (long)((seq_len + 63) / 64) * H < 64;
+}
+
+template <int D, bool KG>
+hipError_t launch_f32(const FwdParams& p, dim3 grid, hipStream_t st) {
+    if (p.softcap > 0.f)
+        hipLaunchKernelGGL((fwd_f32_kernel<D, true, KG>), grid, dim3(256), 0, st, p);
+    else
+        hipLaunchKernelGGL((fwd_f32_kernel<D, false, KG>), grid, dim3(256), 0, st, p);
+    return hipGetLastError();
+}
+
 template <int D>
 hipError_t launch_d(const FwdParams& p, int dtype, hipStream_t st) {
     const dim3 grid(p.n_qblocks * p.H);
@@ -738,19 +804,17 @@ hipError_t launch_d(const FwdParams& p, int dtype, hipStream_t st) {
             if (use_small(D, dtype, p.seq_len, p.H)) return launch_f16<D, F16Small<D>>(p, grid, st);
         }
         return launch_f16<D, F16Cfg<D>>(p, grid, st);
-    } else {
-        if (p.softcap > 0.f)
-            hipLaunchKernelGGL((fwd_f32_kernel<D, true>), grid, dim3(256), 0, st, p);
-        else
-            hipLaunchKernelGGL((fwd_f32_kernel<D, false>), grid, dim3(256), 0, st, p);
     }
-    return hipGetLastError();
+    if constexpr (F32Shape<D>::NKB == 4) {
+        if (use_f32_key_groups(D, p.seq_len, p.H)) return launch_f32<D, true>(p, grid, st);
+    }
+    return launch_f32<D, false>(p, grid, st);
 }
 
 }  // namespace
 
 int fwd_block_rows(int head_dim, int dtype, int seq_len, int H) {
-    if (dtype != 1) return F32Shape<64>::BM;
+    if (dtype != 1) return use_f32_key_groups(head_dim, seq_len, H) ? 16 : F32Shape<64>::BM;
     if (use_small(head_dim, dtype, seq_len, H))
         return head_dim == 64 ? F16Small<64>::QB * (F16Small<64>::NW / F16Small<64>::KS) * 16
                               : F16Small<128>::QB * (F16Small<128>::NW / F16Small<128>::KS) * 16;
