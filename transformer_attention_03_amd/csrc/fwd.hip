@@ -336,6 +336,19 @@ __global__ void __launch_bounds__(64 * NW) fwd_f16_kernel(FwdParams a) {
         }
     }
 
+    // Keys any row of this wave can see: one interval, since the rows are consecutive.  A tile
+    // outside it adds exact zeros to this wave's softmax, so the wave skips its products
+    // (it still takes part in the DMA, waits and barriers).
+    int wave_lo, wave_hi;
+    {
+        const int r0 = q0 + qw * S::QB * 16;
+        const int r1 = min(r0 + S::QB * 16, a.seq_len) - 1;
+        const int p0 = a.kv_len - a.seq_len + r0, p1 = a.kv_len - a.seq_len + r1;
+        wave_lo = a.window > 0 ? max(0, p0 - a.window + 1) : 0;
+        wave_hi = r1 < r0 ? -1 : (a.causal ? min(p1, a.kv_len - 1) : a.kv_len - 1);
+    }
+    auto wave_sees = [&](int ks) { return ks <= wave_hi && ks + S::BN - 1 >= wave_lo; };
+
     int stage = 0;
     for (int it = 0; it * KS < tr.kt1 - tr.kt0; ++it) {
         // this iteration's DMA (issued NS - 1 iterations ago) has landed for every wave, and
@@ -357,7 +370,7 @@ __global__ void __launch_bounds__(64 * NW) fwd_f16_kernel(FwdParams a) {
                                                     k_lds[sn][j], v_lds[sn][j]);
         }
         const int kt = tr.kt0 + it * KS + kg;
-        if (KS == 1 || kt < tr.kt1) {
+        if ((KS == 1 || kt < tr.kt1) && wave_sees(tile_key(kt))) {
             const char* kl = k_lds[stage][kg];
             const char* vl = v_lds[stage][kg];
             const int ks = tile_key(kt);
