@@ -745,10 +745,11 @@ def test_prefill_device_kv_len_graph_replays(dev):
     assert maxabs(got[rows], want) < TOL_F16
 
 
-def test_prefill_device_kv_len_out_of_contract_gives_nan(dev):
-    say("prefill device kv_len out of contract")
+@pytest.mark.parametrize("dtype", ["f16", "f32"])
+def test_prefill_device_kv_len_out_of_contract_gives_nan(dev, dtype):
+    say("prefill device kv_len out of contract %s" % dtype)
     S, Lmax, H, Hkv, D = 40, 100, 2, 1, 64
-    q, k, v = synth.prefill_inputs(synth.seed_of(3) + 51, S, Lmax, H, Hkv, D, "f16")
+    q, k, v = synth.prefill_inputs(synth.seed_of(3) + 51, S, Lmax, H, Hkv, D, dtype)
     for L in (39, 0, 101):
         got = run_prefill_dev_len(dev, q, k, v, L, True)
         assert np.all(np.isnan(got)), L
