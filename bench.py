@@ -13,7 +13,9 @@ f16 ring hot tier) are measured on the same JSON line under
 "workloads".
 
 Timing: W untimed steps, then K steps between HIP events recorded on the stream the
-kernels run on, after a device synchronisation on both sides.  Every workload rotates
+kernels run on, after a device synchronisation on both sides.  The K launches are captured
+into a HIP graph; untimed replays of it (at least 20 ms of device work, so that the clocks
+have settled) come before the one timed replay.  Every workload rotates
 over enough independent input copies (>= 1 GiB in total) that each step reads its
 operands from HBM, not from the 256 MB Infinity Cache.
 
@@ -37,6 +39,7 @@ METRIC = "attention TFLOP/s (prefill/vision) and KV GB/s (decode), % of MI355X r
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 MFMA_F16_PEAK_TFS = 2500.0     # dense f16 MFMA, TFLOP/s
 F32_PEAK_TFS = 157.3           # f32 (vector and matrix), TFLOP/s
+SETTLE_MS = 20.0               # untimed graph replays before the timed one, ms of device work
 ROTATE_BYTES = 1 << 30
 
 
@@ -459,9 +462,20 @@ def time_steps(wl, steps, warmup, graph=True):
             for i in range(steps):
                 wl.step(warmup + i)
         torch.cuda.synchronize()
-        g.replay()                      # untimed replay
-        torch.cuda.synchronize()
+        # untimed replays until the device has run >= 20 ms of this work (clocks settle;
+        # a single short replay left the first timed one 5-10% slow), at most 50
         st = torch.cuda.current_stream()
+        w0 = torch.cuda.Event(enable_timing=True)
+        w1 = torch.cuda.Event(enable_timing=True)
+        spent = 0.0
+        for _ in range(50):
+            w0.record(st)
+            g.replay()
+            w1.record(st)
+            torch.cuda.synchronize()
+            spent += w0.elapsed_time(w1)
+            if spent >= SETTLE_MS:
+                break
         e0.record(st)
         g.replay()
         e1.record(st)
@@ -606,8 +620,9 @@ def main():
            "dtype": "f32" if head.kind != "mfma" else "f16",
            "data": "synthetic (seeded SplitMix64 + Box-Muller, N(0,1))",
            "config": dict(head.desc), "roofline": roof, "max_abs_err_vs_oracle": err,
-           "timing": ("HIP events around one replay of a HIP graph holding the %d launches"
-                      % a.steps) if not a.no_graph else "HIP events around %d host launches" % a.steps}
+           "timing": ("HIP events around one replay of a HIP graph holding the %d launches, "
+                      "after untimed replays of >= %g ms of device work" % (a.steps, SETTLE_MS))
+           if not a.no_graph else "HIP events around %d host launches" % a.steps}
     if not a.no_cpu_baseline:
         log("cpu baseline (oracle)")
         out["cpu_baseline"] = cpu_baseline(head)
