@@ -569,6 +569,21 @@ def test_paged_out_of_contract_kv_len_gives_nan_row(dev):
     assert np.all(np.isnan(got[1])) and np.all(np.isnan(got[2]))
 
 
+def test_paged_out_of_contract_kv_len_past_the_first_64_sequences(dev):
+    """Seventy sequences, two of them (in the second load of 64 lengths) out of contract:
+    their rows are NaN and every other row matches the oracle."""
+    say("paged out-of-contract kv_len, 70 sequences")
+    lens = [(11 * i) % 150 + 1 for i in range(70)]
+    d = synth.paged_inputs(synth.seed_of(5) + 8, 70, 8, 2, 64, lens, n_poison=2)
+    mp = d["page_table"].shape[1]
+    bad = {66: 0, 69: mp * 16 + 1}
+    got = run_paged(dev, d, kv_lens=[bad.get(b, L) for b, L in enumerate(lens)])
+    want = paged_oracle(d)
+    good = [b for b in range(70) if b not in bad]
+    assert maxabs(got[good], want[good]) < TOL_F16
+    assert all(np.all(np.isnan(got[b])) for b in bad)
+
+
 # =============================================================================================
 # prefill (token-major) and vision (head-major)
 # =============================================================================================
