@@ -13,11 +13,12 @@ f16 ring hot tier) are measured on the same JSON line under
 "workloads".
 
 Timing: W untimed steps, then K steps between HIP events recorded on the stream the
-kernels run on, after a device synchronisation on both sides.  The K launches are captured
-into a HIP graph; untimed replays of it (at least 20 ms of device work, so that the clocks
-have settled) come before the one timed replay.  Every workload rotates
-over enough independent input copies (>= 1 GiB in total) that each step reads its
-operands from HBM, not from the 256 MB Infinity Cache.
+kernels run on, after a device synchronisation on both sides; the median of 5 such timed
+replays is reported.  The K launches are captured into HIP graphs; untimed replays (at
+least 20 ms of device work, so that the clocks have settled) come before the timed ones.
+Every workload rotates over enough independent input copies (>= 1 GiB in total), in order
+across replays, that each step reads its operands from HBM, not from the 256 MB Infinity
+Cache.
 
 The cpu_baseline leg times the float64 oracle (test infrastructure) on the host cores,
 on the same workload, repeated for about ten seconds.
@@ -52,6 +53,8 @@ def parse():
                     choices=["decode_f16", "prefill_f32", "prefill_f16", "vision_f16",
                              "decode_paged_q8", "prefill_chunk_f16", "decode_ring_f16",
                              "decode_tiered_q8", "all"])
+    ap.add_argument("--repeats", type=int, default=5,
+                    help="timed replays; the median is reported")
     ap.add_argument("--only-headline", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true",
@@ -79,7 +82,12 @@ class Workload:
 
 
 def n_copies(bytes_per_copy):
-    return max(2, min(512, int(math.ceil(ROTATE_BYTES / max(1, bytes_per_copy)))))
+    """Input copies that together hold >= 1 GiB, rounded up to a multiple of 16 (a power of
+    two below 16), so that few graphs of K launches cover a whole number of rounds through
+    the copies for the usual K; at most 512."""
+    n = max(2, int(math.ceil(ROTATE_BYTES / max(1, bytes_per_copy))))
+    n = 1 << (n - 1).bit_length() if n < 16 else (n + 15) // 16 * 16
+    return min(512, n)
 
 
 def log(msg):
@@ -444,51 +452,76 @@ def make(name, dev):
 # measurement
 # ---------------------------------------------------------------------------------------------
 
-def time_steps(wl, steps, warmup, graph=True):
-    """ms per step: K steps between HIP events on the launch stream.  With graph=True the K
-    launches (each on its own input copy) are captured once into a HIP graph and replayed,
-    so host-side launch cost does not pace the GPU."""
+def time_steps(wl, steps, warmup, graph=True, repeats=5):
+    """ms per step and the per-replay times: K steps between HIP events on the launch stream,
+    median over `repeats` timed replays.  With graph=True the steps are captured into HIP
+    graphs and replayed, so host-side launch cost does not pace the GPU.
+
+    Input copies: step s of the run uses copy s mod nc.  The steps are captured as G graphs
+    of K launches, graph g holding steps gK .. gK + K - 1, with G = nc / gcd(nc, K), and the
+    graphs are replayed in turn; so the launch sequence runs through the copies in order
+    whatever K is, and a copy is read again only after every other copy (>= 1 GiB of inputs
+    in total) has been streamed: no replay finds its operands in the 256 MB Infinity Cache.
+    (G is capped at 64; only workloads whose copies all fit the cache anyway, the 128-token
+    f32 prefill, reach the cap.)"""
     import torch
     for i in range(warmup):
         wl.step(i)
     torch.cuda.synchronize()
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
+    st = torch.cuda.current_stream()
+    times = []
     if graph:
-        g = torch.cuda.CUDAGraph()
+        nc = max(1, getattr(wl, "nc", 1))
+        n_graphs = min(64, nc // math.gcd(nc, steps))
         side = torch.cuda.Stream()
-        side.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.graph(g, stream=side):
-            for i in range(steps):
-                wl.step(warmup + i)
+        side.wait_stream(st)
+        graphs = []
+        for g in range(n_graphs):
+            gr = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(gr, stream=side):
+                for i in range(steps):
+                    wl.step(g * steps + i)
+            graphs.append(gr)
         torch.cuda.synchronize()
         # untimed replays until the device has run >= 20 ms of this work (clocks settle;
-        # a single short replay left the first timed one 5-10% slow), at most 50
-        st = torch.cuda.current_stream()
+        # a single short replay left the first timed one 5-10% slow), at least one round of
+        # every graph, at most 200 replays
         w0 = torch.cuda.Event(enable_timing=True)
         w1 = torch.cuda.Event(enable_timing=True)
-        spent = 0.0
-        for _ in range(50):
+        spent, r = 0.0, 0
+        while r < 200 and (spent < SETTLE_MS or r < n_graphs):
             w0.record(st)
-            g.replay()
+            graphs[r % n_graphs].replay()
             w1.record(st)
             torch.cuda.synchronize()
             spent += w0.elapsed_time(w1)
-            if spent >= SETTLE_MS:
-                break
-        e0.record(st)
-        g.replay()
-        e1.record(st)
-        torch.cuda.synchronize()
-        del g
+            r += 1
+        for _ in range(repeats):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            e0.record(st)
+            graphs[r % n_graphs].replay()
+            e1.record(st)
+            torch.cuda.synchronize()
+            times.append(e0.elapsed_time(e1))
+            r += 1
+        del graphs
     else:
-        st = torch.cuda.current_stream()
-        e0.record(st)
-        for i in range(steps):
-            wl.step(warmup + i)
-        e1.record(st)
-        torch.cuda.synchronize()
-    return e0.elapsed_time(e1) / steps      # ms per step
+        base = warmup
+        for _ in range(repeats):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            e0.record(st)
+            for i in range(steps):
+                wl.step(base + i)
+            e1.record(st)
+            torch.cuda.synchronize()
+            times.append(e0.elapsed_time(e1))
+            base += steps
+    med = sorted(times)[len(times) // 2]
+    return med / steps, [t / steps for t in times]      # ms per step
 
 
 def summarize(wl, ms):
@@ -537,6 +570,7 @@ def cpu_baseline(wl, budget_s=10.0):
             break
         if len(times) >= 5000:            # the time budget normally ends the loop first
             break
+    used = oracle.threads_used()          # threads that computed rows in the last call
     times.sort()
     med = times[len(times) // 2]
     amount, unit = wl.units()
@@ -556,7 +590,8 @@ def cpu_baseline(wl, budget_s=10.0):
     else:
         sample = "the full workload, %d repeats" % len(times)
     val = amount / med / (1e9 if unit == "bytes" else 1e12)
-    return {"value": val, "unit": "GB/s" if unit == "bytes" else "TFLOP/s", "cores": threads,
+    return {"value": val, "unit": "GB/s" if unit == "bytes" else "TFLOP/s", "cores": used,
+            "threads_started": threads,
             "kind": "oracle", "sample": sample + " (median %.3f s per repeat)" % med}
 
 
@@ -607,7 +642,7 @@ def main():
     head = make(a.workload, dev)
     err = head.check()
     log("%s max-abs error vs oracle %.3g; timing %d steps" % (head.name, err, a.steps))
-    ms = time_steps(head, a.steps, a.warmup, graph=not a.no_graph)
+    ms, per_replay = time_steps(head, a.steps, a.warmup, graph=not a.no_graph, repeats=a.repeats)
     s = summarize(head, ms)
     src = os.path.join(ROOT, "transformer_attention_03_amd", "csrc",
                        "decode.hip" if head.kind == "hbm" else "fwd.hip")
@@ -620,9 +655,12 @@ def main():
            "dtype": "f32" if head.kind != "mfma" else "f16",
            "data": "synthetic (seeded SplitMix64 + Box-Muller, N(0,1))",
            "config": dict(head.desc), "roofline": roof, "max_abs_err_vs_oracle": err,
-           "timing": ("HIP events around one replay of a HIP graph holding the %d launches, "
-                      "after untimed replays of >= %g ms of device work" % (a.steps, SETTLE_MS))
-           if not a.no_graph else "HIP events around %d host launches" % a.steps}
+           "timing": ("median of %d timed replays, HIP events around each replay of a HIP graph "
+                      "holding the %d launches (graphs rotate over the input copies), after "
+                      "untimed replays of >= %g ms of device work" % (a.repeats, a.steps, SETTLE_MS))
+           if not a.no_graph else "median of %d runs of %d host launches" % (a.repeats, a.steps),
+           "timed_replays": a.repeats,
+           "us_per_step_each_replay": [round(x * 1e3, 3) for x in per_replay]}
     if not a.no_cpu_baseline:
         log("cpu baseline (oracle)")
         out["cpu_baseline"] = cpu_baseline(head)
@@ -635,7 +673,8 @@ def main():
             wl = make(name, dev)
             e = wl.check()
             log("%s max-abs error vs oracle %.3g" % (name, e))
-            ms_w = time_steps(wl, max(20, a.steps // 4), a.warmup, graph=not a.no_graph)
+            ms_w, _ = time_steps(wl, max(20, a.steps // 4), a.warmup, graph=not a.no_graph,
+                                 repeats=a.repeats)
             sw = summarize(wl, ms_w)
             others[name] = {"config": wl.desc, "us_per_call": round(sw["us_per_call"], 3),
                             "value": round(sw["value"], 3), "unit": sw["unit"],

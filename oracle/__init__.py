@@ -53,6 +53,8 @@ def _load():
         lib.oracle_dequant_i8.argtypes = [
             ctypes.c_void_p, ctypes.c_void_p, ctypes.c_long, ctypes.c_int, dp]
         lib.oracle_dequant_i8.restype = None
+        lib.oracle_threads_used.argtypes = []
+        lib.oracle_threads_used.restype = ctypes.c_int
         _lib = lib
     return _lib
 
@@ -94,6 +96,11 @@ def attention(q, k, v, *, kv_len=None, causal=False, window=0, softcap=0.0, scal
     if rc != 0:
         raise ValueError("oracle_attention_f64 rejected its arguments")
     return o
+
+
+def threads_used() -> int:
+    """Threads that computed at least one row in the last attention() call."""
+    return int(_load().oracle_threads_used())
 
 
 def dequant_i8(q8, scales):

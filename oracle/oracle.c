@@ -44,9 +44,15 @@ typedef struct {
     int causal, window;
     double softcap, scale;
     long n_rows;          /* B * S * H */
+    long grab;            /* rows taken per visit of the work counter */
     long next;            /* shared work counter, guarded by mu */
+    int workers;          /* threads that computed at least one row, guarded by mu */
     pthread_mutex_t mu;
 } job_t;
+
+/* Threads that computed at least one row in the last oracle_attention_f64 call of the
+ * process (a figure for reports; not synchronised between concurrent calls). */
+static int g_threads_used = 0;
 
 /* One output row: batch b, query row i, query head h. */
 static void one_row(const job_t *J, int b, int i, int h, double *score)
@@ -95,14 +101,19 @@ static void *worker(void *arg)
     job_t *J = (job_t *)arg;
     double *score = (double *)malloc(sizeof(double) * (size_t)(J->Lmax > 0 ? J->Lmax : 1));
     if (!score) return NULL;
+    int counted = 0;
     for (;;) {
         long r0;
         pthread_mutex_lock(&J->mu);
         r0 = J->next;
-        J->next += 16;
+        J->next += J->grab;
+        if (r0 < J->n_rows && !counted) {
+            counted = 1;
+            J->workers += 1;
+        }
         pthread_mutex_unlock(&J->mu);
         if (r0 >= J->n_rows) break;
-        long r1 = r0 + 16 < J->n_rows ? r0 + 16 : J->n_rows;
+        long r1 = r0 + J->grab < J->n_rows ? r0 + J->grab : J->n_rows;
         for (long r = r0; r < r1; ++r) {
             const int h = (int)(r % J->H);
             const int i = (int)((r / J->H) % J->S);
@@ -137,9 +148,15 @@ int oracle_attention_f64(const double *q, const double *k, const double *v, doub
     J.softcap = softcap; J.scale = scale;
     J.n_rows = (long)B * S * H;
     J.next = 0;
+    J.workers = 0;
     pthread_mutex_init(&J.mu, NULL);
     if (nthreads < 1) nthreads = 1;
     if (nthreads > 256) nthreads = 256;
+    /* about four grabs per thread, at most 16 rows each, so that a call with few (long)
+     * rows, such as one decode token over 32 heads, still spreads over every thread */
+    J.grab = J.n_rows / (4L * nthreads);
+    if (J.grab < 1) J.grab = 1;
+    if (J.grab > 16) J.grab = 16;
     pthread_t th[256];
     int started = 0;
     for (int t = 1; t < nthreads; ++t)
@@ -147,8 +164,11 @@ int oracle_attention_f64(const double *q, const double *k, const double *v, doub
     worker(&J);
     for (int t = 0; t < started; ++t) pthread_join(th[t], NULL);
     pthread_mutex_destroy(&J.mu);
+    g_threads_used = J.workers;
     return 0;
 }
+
+int oracle_threads_used(void) { return g_threads_used; }
 
 /*
  * Dequantisation of a symmetric int8 cache row: x = q8 * scale, one f32 scale

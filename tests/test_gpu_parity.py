@@ -2,9 +2,10 @@
 seeded inputs, element by element.
 
 Tolerances (max-abs, on outputs of O(1)): 1e-4 for the float32 path, 3e-3 for the
-float16 and int8 paths.  Full-size workloads compare every output (decode) or sampled
-query rows computed one by one by the oracle (prefill / vision).  Page-table indexing is
-checked bit-exactly: two placements of the same logical cache give identical bits.
+float16 and int8 paths.  Every test compares every output element, full-size workloads
+included.
+Page-table indexing is checked bit-exactly: two placements of the same logical cache give
+identical bits.
 """
 import math
 
@@ -656,17 +657,16 @@ def c3_inputs():
     return synth.prefill_inputs(synth.seed_of(3), 2048, 2048, 16, 8, 256, "f16")
 
 
-C3_ROWS = [0, 1, 2, 15, 16, 63, 64, 127, 128, 255, 256, 511, 512, 513, 777, 1023, 1024, 1500,
-           1919, 2046, 2047]
-
-
-def test_prefill_full_workload_sampled_rows(dev, c3_inputs):
-    say("prefill full workload")
+def test_prefill_full_workload_every_element(dev, c3_inputs):
+    """The 2048-token windowed softcapped GQA prefill at head_dim 256, every output element
+    against the oracle (the oracle runs all 32768 rows)."""
+    say("prefill full workload, every element")
     q, k, v = c3_inputs
     got = run_prefill(dev, q, k, v, True, 512, 50.0)
     assert np.all(np.isfinite(got))
-    want = prefill_oracle_rows(q, k, v, C3_ROWS, True, 512, 50.0)
-    assert maxabs(got[C3_ROWS], want) < TOL_F16
+    want = oracle.attention(q[None], k[None], v[None], causal=True, window=512, softcap=50.0,
+                            scale=1 / 16)[0]
+    assert maxabs(got, want) < TOL_F16
     # row 0 sees only key 0: its output is v0 exactly, for every head
     G = 2
     for h in range(16):
@@ -682,15 +682,71 @@ def test_prefill_full_workload_sampled_rows(dev, c3_inputs):
 ])
 def test_prefill_both_configurations(dev, S, L, H, Hkv, D, W):
     """Grids that fill the device run 64-row workgroups; smaller ones run 32-row workgroups
-    whose waves split the keys four ways and merge in LDS.  Both against the oracle on
-    sampled rows (first, last, a tile edge, the middle)."""
+    whose waves split the keys four ways and merge in LDS.  Both against the oracle, every
+    element."""
     say("prefill configuration S=%d L=%d H=%d Hkv=%d D=%d W=%d" % (S, L, H, Hkv, D, W))
     q, k, v = synth.prefill_inputs(synth.seed_of(3) + S + L, S, L, H, Hkv, D, "f16")
     got = run_prefill(dev, q, k, v, True, W, 0.0)
     assert np.all(np.isfinite(got))
-    rows = sorted(set(r for r in (0, 1, 31, 32, S // 2, S - 2, S - 1) if 0 <= r < S))
-    want = prefill_oracle_rows(q, k, v, rows, True, W, 0.0)
-    assert maxabs(got[rows], want) < TOL_F16
+    want = oracle.attention(q[None], k[None], v[None], causal=True, window=W,
+                            scale=1 / math.sqrt(D))[0]
+    assert maxabs(got, want) < TOL_F16
+
+
+# Grids that fill the device (>= 256 workgroups of the standard block: 16 heads and >= 1100
+# query rows, or head_dim 256), so that the configuration the full-size calls run is the one
+# tested, with ragged last key tiles (1100 and 1700 keys are no multiple of 64 or 96), windows,
+# softcaps (the capped instantiations) and chunks shorter than the cache.  Every element.
+@pytest.mark.parametrize("S,L,H,Hkv,D,causal,W,cap", [
+    (1100, 1100, 16, 8, 64, True, 0, 0.0),
+    (1100, 1100, 16, 8, 64, True, 300, 50.0),
+    (1100, 1700, 16, 8, 64, True, 0, 0.0),
+    (1100, 1100, 16, 16, 64, False, 0, 20.0),
+    (1100, 1100, 16, 8, 128, True, 0, 0.0),
+    (1100, 1100, 16, 8, 128, True, 257, 50.0),
+    (1100, 1700, 16, 4, 128, True, 0, 0.0),
+    (1100, 1700, 16, 8, 128, True, 500, 30.0),
+    (1100, 1100, 16, 16, 128, False, 0, 0.0),
+    (700, 900, 24, 8, 256, True, 100, 30.0),
+    (700, 700, 16, 16, 256, False, 0, 0.0),
+])
+def test_prefill_at_size_every_element(dev, S, L, H, Hkv, D, causal, W, cap):
+    say("prefill at size S=%d L=%d H=%d Hkv=%d D=%d causal=%d W=%d cap=%g" % (S, L, H, Hkv, D, causal, W, cap))
+    q, k, v = synth.prefill_inputs(synth.seed_of(3) + 3 * S + L + D + W, S, L, H, Hkv, D, "f16")
+    got = run_prefill(dev, q, k, v, causal, W, cap)
+    assert np.all(np.isfinite(got))
+    want = oracle.attention(q[None], k[None], v[None], causal=causal, window=W, softcap=cap,
+                            scale=1 / math.sqrt(D))[0]
+    assert maxabs(got, want) < TOL_F16
+
+
+@pytest.mark.parametrize("dtype,S,L,H,Hkv,D", [
+    ("f16", 1100, 1100, 16, 8, 64),      # the standard configurations
+    ("f16", 1100, 1300, 16, 8, 128),
+    ("f16", 300, 300, 8, 4, 256),
+    ("f16", 100, 400, 2, 1, 64),         # small grids (key groups)
+    ("f16", 64, 64, 4, 2, 128),
+    ("f32", 128, 128, 1, 1, 64),
+    ("f32", 520, 600, 8, 2, 128),
+])
+def test_prefill_window_one_returns_own_value(dev, dtype, S, L, H, Hkv, D):
+    """With a causal window of one key every query row sees only its own position, so its
+    weight is exp(0) = 1 and the output is that key's V row, bit for bit."""
+    say("prefill W=1 %s S=%d L=%d D=%d" % (dtype, S, L, D))
+    q, k, v = synth.prefill_inputs(synth.seed_of(3) + 13 * S + D, S, L, H, Hkv, D, dtype)
+    got = run_prefill(dev, q, k, v, True, 1, 0.0)
+    G = H // Hkv
+    for h in range(H):
+        assert np.array_equal(got[:, h], v[L - S:, h // G]), h
+
+
+def test_decode_window_one_returns_last_value(dev):
+    """Decode with a window of one key: the output is the newest V row exactly (in f32)."""
+    say("decode W=1")
+    q, k, v = synth.decode_inputs(synth.seed_of(2) + 77, 32, 8, 128, 1000)
+    got, _ = run_decode(dev, q, k, v, W=1)
+    for h in range(32):
+        assert np.array_equal(got[h], v[h // 4, -1].astype(np.float32)), h
 
 
 # ---- chunked prefill against a cache whose length is read on the device -----------------
@@ -818,15 +874,29 @@ def test_vision_small(dev, H, P, D):
     assert maxabs(np.transpose(got, (1, 0, 2)), want) < TOL_F16
 
 
-def test_vision_full_workload_sampled_rows(dev):
-    say("vision full workload")
+def test_vision_full_workload_every_element(dev):
+    """The 2304-patch, 16-head, head_dim 64 vision call, every output element against the
+    oracle."""
+    say("vision full workload, every element")
     q, k, v = synth.vision_inputs(synth.seed_of(4), 2304, 16, 64)
     got = run_vision(dev, q, k, v, 0.125)
     assert np.all(np.isfinite(got))
-    rows = [0, 1, 127, 128, 1000, 2047, 2303]
     qt, kt, vt = (np.transpose(x, (1, 0, 2)) for x in (q, k, v))
-    want = prefill_oracle_rows(qt, kt, vt, rows, False, scale=0.125)
-    assert maxabs(np.transpose(got, (1, 0, 2))[rows], want) < TOL_F16
+    want = oracle.attention(qt[None], kt[None], vt[None], causal=False, scale=0.125)[0]
+    assert maxabs(np.transpose(got, (1, 0, 2)), want) < TOL_F16
+
+
+@pytest.mark.parametrize("H,P,D", [(16, 1000, 64), (16, 1100, 128), (8, 777, 256)])
+def test_vision_at_size_every_element(dev, H, P, D):
+    """Vision grids of >= 256 workgroups with a ragged last key tile (1000 patches: ten
+    96-key tiles and 40 keys; 1100: seventeen 64-key tiles and 12), every element."""
+    say("vision at size H=%d P=%d D=%d" % (H, P, D))
+    q, k, v = synth.vision_inputs(synth.seed_of(4) + 7 * P + D, P, H, D)
+    got = run_vision(dev, q, k, v, 1 / math.sqrt(D))
+    assert np.all(np.isfinite(got))
+    qt, kt, vt = (np.transpose(x, (1, 0, 2)) for x in (q, k, v))
+    want = oracle.attention(qt[None], kt[None], vt[None], causal=False, scale=1 / math.sqrt(D))[0]
+    assert maxabs(np.transpose(got, (1, 0, 2)), want) < TOL_F16
 
 
 def test_vision_equals_bidirectional_prefill(dev):

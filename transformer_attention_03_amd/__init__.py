@@ -83,6 +83,11 @@ def _ptr(t):
     return None if t is None else t.data_ptr()
 
 
+def _dname(t):
+    """The dtype name of a tensor ("float32", "float16", ...), for _need."""
+    return str(getattr(t, "dtype", "?")).replace("torch.", "")
+
+
 def _dtype_code(t):
     import torch
     if t.dtype == torch.float32:
@@ -98,14 +103,44 @@ def _need_contig(*ts):
             raise ValueError("tensors must be contiguous")
 
 
+def _need(what, **named):
+    """Dtype and device checks before anything reaches the library: every tensor named
+    here must have the dtype given with it and live on the same GPU as the first one.
+    named: name -> (tensor, dtype name or tuple of dtype names).  A tensor of the wrong
+    dtype would be read with the wrong element size, and a host tensor would hand the
+    kernels a host pointer, so both are refused."""
+    import torch
+    dev = None
+    for name, (t, want) in named.items():
+        if t is None:
+            continue
+        if not isinstance(t, torch.Tensor):
+            raise TypeError("%s: %s must be a torch.Tensor" % (what, name))
+        wants = want if isinstance(want, tuple) else (want,)
+        if not any(t.dtype == getattr(torch, w) for w in wants):
+            raise ValueError("%s: %s must be %s, got %s" % (what, name, " or ".join(wants),
+                                                            str(t.dtype).replace("torch.", "")))
+    for name, (t, _) in named.items():
+        if t is None:
+            continue
+        if t.device.type != "cuda":
+            raise ValueError("%s: %s must be on a GPU, got %s" % (what, name, t.device))
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise ValueError("%s: %s is on %s, the other tensors on %s" % (what, name, t.device, dev))
+
+
 def attn_prefill(q, k, v, o, *, causal: bool, scale: float, sliding_window: int = 0,
                  attn_softcap: float = 0.0, stream=None):
     """q, o: [seq_len, num_heads, head_dim]; k, v: [kv_len, num_kv_heads, head_dim]."""
+    _need("attn_prefill", q=(q, ("float32", "float16")), k=(k, _dname(q)), v=(v, _dname(q)),
+          o=(o, _dname(q)))
     _need_contig(q, k, v, o)
     S, H, D = q.shape
     L, Hkv, Dk = k.shape
-    if Dk != D or v.shape != k.shape or o.shape != q.shape or o.dtype != q.dtype:
-        raise ValueError("shape/dtype mismatch")
+    if Dk != D or v.shape != k.shape or o.shape != q.shape:
+        raise ValueError("shape mismatch")
     _check(lib().attn_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _dtype_code(q), S, L, H, Hkv,
                               D, 1 if causal else 0, int(sliding_window), float(attn_softcap),
                               float(scale), _stream(q, stream)))
@@ -115,13 +150,14 @@ def attn_prefill_device_kv_len(q, k, v, o, kv_len, *, causal: bool, scale: float
                                sliding_window: int = 0, attn_softcap: float = 0.0, stream=None):
     """q, o: [seq_len, num_heads, head_dim]; k, v: [max_kv_len, num_kv_heads, head_dim];
     kv_len: int32 device tensor of one element, read when the kernel runs."""
+    _need("attn_prefill_device_kv_len", q=(q, ("float32", "float16")), k=(k, _dname(q)),
+          v=(v, _dname(q)), o=(o, _dname(q)), kv_len=(kv_len, "int32"))
     _need_contig(q, k, v, o)
     S, H, D = q.shape
     Lmax, Hkv, Dk = k.shape
-    if Dk != D or v.shape != k.shape or o.shape != q.shape or o.dtype != q.dtype:
-        raise ValueError("shape/dtype mismatch")
-    import torch
-    if kv_len.dtype != torch.int32 or kv_len.numel() != 1 or kv_len.device != q.device:
+    if Dk != D or v.shape != k.shape or o.shape != q.shape:
+        raise ValueError("shape mismatch")
+    if kv_len.numel() != 1:
         raise ValueError("kv_len must be one int32 element on the device of q")
     _check(lib().attn_prefill_device_kv_len(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _dtype_code(q), S,
                                             Lmax, _ptr(kv_len), H, Hkv, D, 1 if causal else 0,
@@ -131,6 +167,7 @@ def attn_prefill_device_kv_len(q, k, v, o, kv_len, *, causal: bool, scale: float
 
 def attn_vision(q, k, v, o, *, scale: float, stream=None):
     """q, k, v, o: float16 [num_heads, num_patches, head_dim]."""
+    _need("attn_vision", q=(q, "float16"), k=(k, "float16"), v=(v, "float16"), o=(o, "float16"))
     _need_contig(q, k, v, o)
     H, P, D = q.shape
     if k.shape != q.shape or v.shape != q.shape or o.shape != q.shape:
@@ -160,6 +197,8 @@ def decode_workspace(batch, num_heads, num_kv_heads, head_dim, max_kv_len, devic
 def attn_decode(q, k, v, o, workspace, *, scale: float, sliding_window: int = 0,
                 attn_softcap: float = 0.0, stream=None):
     """q, o: float32 [num_heads, head_dim]; k, v: float16 [num_kv_heads, kv_len, head_dim]."""
+    _need("attn_decode", q=(q, "float32"), k=(k, "float16"), v=(v, "float16"), o=(o, "float32"),
+          workspace=(workspace, "uint8"))
     _need_contig(q, k, v, o)
     H, D = q.shape
     Hkv, L, Dk = k.shape
@@ -175,6 +214,8 @@ def attn_decode_ring(q, k, v, o, workspace, *, total_len: int, scale: float,
                      sliding_window: int = 0, attn_softcap: float = 0.0, stream=None):
     """q, o: float32 [num_heads, head_dim]; k, v: float16 ring [num_kv_heads, ring_len,
     head_dim] holding position t at row t % ring_len; total_len tokens seen so far."""
+    _need("attn_decode_ring", q=(q, "float32"), k=(k, "float16"), v=(v, "float16"),
+          o=(o, "float32"), workspace=(workspace, "uint8"))
     _need_contig(q, k, v, o)
     H, D = q.shape
     Hkv, R, Dk = k.shape
@@ -192,6 +233,10 @@ def attn_decode_paged_q8(q, k_pages, v_pages, k_scales, v_scales, page_table, kv
     """q, o: float32 [batch, num_heads, head_dim]; pages int8 [num_pages, num_kv_heads, 16,
     head_dim]; scales float32 [num_pages, num_kv_heads, 16]; page_table int32
     [batch, max_pages]; kv_lens int32 [batch] (device)."""
+    _need("attn_decode_paged_q8", q=(q, "float32"), k_pages=(k_pages, "int8"),
+          v_pages=(v_pages, "int8"), k_scales=(k_scales, "float32"), v_scales=(v_scales, "float32"),
+          page_table=(page_table, "int32"), kv_lens=(kv_lens, "int32"), o=(o, "float32"),
+          workspace=(workspace, "uint8"))
     _need_contig(q, k_pages, v_pages, k_scales, v_scales, page_table, kv_lens, o)
     B, H, D = q.shape
     P, Hkv, ps, Dk = k_pages.shape
@@ -216,6 +261,11 @@ def attn_decode_tiered_q8(q, hot_k, hot_v, cold_k_pages, cold_v_pages, cold_k_sc
     hot_window, head_dim] holding position p >= cold_len at row (hot_start + p - cold_len) %
     hot_window; cold pages int8 [num_pages, num_kv_heads, 16, head_dim], scales float32
     [num_pages, num_kv_heads, 16], page table int32 [max_pages] for positions < cold_len."""
+    _need("attn_decode_tiered_q8", q=(q, "float32"), hot_k=(hot_k, "float16"),
+          hot_v=(hot_v, "float16"), cold_k_pages=(cold_k_pages, "int8"),
+          cold_v_pages=(cold_v_pages, "int8"), cold_k_scales=(cold_k_scales, "float32"),
+          cold_v_scales=(cold_v_scales, "float32"), cold_page_table=(cold_page_table, "int32"),
+          o=(o, "float32"), workspace=(workspace, "uint8"))
     _need_contig(q, hot_k, hot_v, cold_k_pages, cold_v_pages, cold_k_scales, cold_v_scales,
                  cold_page_table, o)
     H, D = q.shape
