@@ -24,7 +24,9 @@
  *
  * Ownership.  All buffers are owned by the caller.  The library allocates nothing, frees
  * nothing, never synchronises and keeps no pointer after returning.  The caller keeps
- * every buffer alive until the queued work has completed on `stream`.
+ * every buffer alive until the queued work has completed on `stream`.  (The one piece of
+ * device memory the library owns is the fixed scratch array of attn_decode_noalloc, part
+ * of its loaded code object.)
  *
  * Errors.  Each entry point returns ATTN_OK (0) or a negative attn_status.  Argument
  * errors are detected on the host BEFORE any HIP call, so nothing is queued and no output
@@ -32,9 +34,10 @@
  * message for the last failure of the calling thread is returned by attn_last_error().
  * Faults during kernel execution surface at the caller's next synchronisation.
  *
- * Threading.  Re-entrant: the only mutable library state is thread-local (the error
- * string and the decode split override).  Concurrent calls on different streams must
- * use different workspaces.
+ * Threading.  Re-entrant: the only mutable host state is thread-local (the error string
+ * and the decode split override), apart from the per-device address of the scratch array,
+ * looked up once under a lock.  Concurrent calls on different streams must use different
+ * workspaces; concurrent attn_decode_noalloc calls on one GPU share its scratch and race.
  */
 #ifndef TA03_ATTN_H
 #define TA03_ATTN_H
@@ -132,6 +135,27 @@ int attn_decode(const float *q, const void *k, const void *v, float *o,
                 int num_heads, int num_kv_heads, int head_dim, int kv_len,
                 int sliding_window, float attn_softcap, float scale,
                 void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * attn_decode for callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc): the same computation, kernels and
+ * result as attn_decode, with the split partials and arrival counters in a library-owned
+ * device array of ATTN_DECODE_SCRATCH_BYTES (4 MiB) per GPU instead of a caller workspace.
+ * The array is part of the loaded code object, so each GPU the library runs on holds one
+ * until the process ends; this entry point allocates and frees nothing.
+ *
+ *   Arguments, layouts and host-side checks as attn_decode, minus the workspace.  A shape
+ *   whose split partials need more than ATTN_DECODE_SCRATCH_BYTES (attn_decode_workspace_bytes
+ *   (1, num_heads, num_kv_heads, head_dim, kv_len) > 4 MiB, e.g. more than about 240 splits
+ *   of 32 heads at head_dim 128) is refused with ATTN_ERR_UNSUPPORTED before any HIP call.
+ *   The arrival counters are cleared on `stream` by a small kernel before every launch.
+ *   All calls on one GPU share its array: calls whose execution overlaps on one GPU (two
+ *   streams, or two threads) race and give wrong results; serialise them.
+ */
+#define ATTN_DECODE_SCRATCH_BYTES ((size_t)4 << 20)
+int attn_decode_noalloc(const float *q, const void *k, const void *v, float *o,
+                        int num_heads, int num_kv_heads, int head_dim, int kv_len,
+                        int sliding_window, float attn_softcap, float scale, void *stream);
 
 /*
  * Single-token decode over a ring-buffer f16 cache that keeps the newest tokens of a

@@ -255,3 +255,14 @@ def test_error_string_is_thread_local_and_cleared_on_success():
     assert "head_dim" in ta.attn_last_error()
     ta.attn_set_decode_split(0)   # a successful call clears it
     assert ta.attn_last_error() == ""
+
+
+def test_noalloc_refuses_shapes_beyond_its_scratch():
+    """A decode whose split partials would not fit the library's scratch array is refused on
+    the host, before any HIP call, with the limit in the message."""
+    L = ta.lib()
+    rc = L.attn_decode_noalloc(P, P, P, P, 64, 8, 256, 1000000, 0, 0.0, 0.0625, None)
+    assert rc == ta.ATTN_ERR_UNSUPPORTED
+    assert "scratch" in ta.attn_last_error() and "4194304" in ta.attn_last_error()
+    rc = L.attn_decode_noalloc(None, P, P, P, 32, 8, 128, 4096, 0, 0.0, 0.088, None)
+    assert rc == ta.ATTN_ERR_INVALID_ARG and "q must not be null" in ta.attn_last_error()

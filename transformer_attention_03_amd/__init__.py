@@ -13,7 +13,8 @@ import math
 import os
 
 __all__ = [
-    "AttnError", "lib", "attn_prefill", "attn_vision", "attn_decode", "attn_decode_paged_q8", "attn_decode_tiered_q8",
+    "AttnError", "lib", "attn_prefill", "attn_prefill_device_kv_len", "attn_vision", "attn_decode",
+    "attn_decode_noalloc", "attn_decode_ring", "attn_decode_paged_q8", "attn_decode_tiered_q8",
     "attn_decode_workspace_bytes", "attn_set_decode_split", "attn_last_error", "decode_workspace",
     "ATTN_OK", "ATTN_ERR_INVALID_ARG", "ATTN_ERR_UNSUPPORTED", "ATTN_ERR_WORKSPACE",
     "ATTN_ERR_LAUNCH", "ATTN_F32", "ATTN_F16", "LIB_PATH",
@@ -45,6 +46,7 @@ def lib() -> ctypes.CDLL:
         L.attn_prefill_device_kv_len.argtypes = [vp, vp, vp, vp, i, i, i, vp, i, i, i, i, i, f, f, vp]
         L.attn_vision.argtypes = [vp, vp, vp, vp, i, i, i, f, vp]
         L.attn_decode.argtypes = [vp, vp, vp, vp, i, i, i, i, i, f, f, vp, sz, vp]
+        L.attn_decode_noalloc.argtypes = [vp, vp, vp, vp, i, i, i, i, i, f, f, vp]
         L.attn_decode_ring.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, f, f, vp, sz, vp]
         L.attn_decode_paged_q8.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i,
                                            f, f, vp, sz, vp]
@@ -56,7 +58,7 @@ def lib() -> ctypes.CDLL:
         L.attn_last_error.argtypes = []
         L.attn_last_error.restype = ctypes.c_char_p
         for name in ("attn_prefill", "attn_prefill_device_kv_len", "attn_vision", "attn_decode",
-                     "attn_decode_ring", "attn_decode_paged_q8", "attn_decode_tiered_q8",
+                     "attn_decode_noalloc", "attn_decode_ring", "attn_decode_paged_q8", "attn_decode_tiered_q8",
                      "attn_set_decode_split"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
@@ -208,6 +210,22 @@ def attn_decode(q, k, v, o, workspace, *, scale: float, sliding_window: int = 0,
     _check(lib().attn_decode(_ptr(q), _ptr(k), _ptr(v), _ptr(o), H, Hkv, D, L,
                              int(sliding_window), float(attn_softcap), float(scale),
                              _ptr(workspace), ws_bytes, _stream(q, stream)))
+
+
+def attn_decode_noalloc(q, k, v, o, *, scale: float, sliding_window: int = 0,
+                        attn_softcap: float = 0.0, stream=None):
+    """attn_decode without a workspace: the library's own per-GPU scratch holds the split
+    partials.  Calls that overlap on one GPU race; see include/attn.h."""
+    _need("attn_decode_noalloc", q=(q, "float32"), k=(k, "float16"), v=(v, "float16"),
+          o=(o, "float32"))
+    _need_contig(q, k, v, o)
+    H, D = q.shape
+    Hkv, L, Dk = k.shape
+    if Dk != D or v.shape != k.shape or o.shape != q.shape:
+        raise ValueError("shape mismatch")
+    _check(lib().attn_decode_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(o), H, Hkv, D, L,
+                                     int(sliding_window), float(attn_softcap), float(scale),
+                                     _stream(q, stream)))
 
 
 def attn_decode_ring(q, k, v, o, workspace, *, total_len: int, scale: float,

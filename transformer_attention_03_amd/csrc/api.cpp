@@ -207,10 +207,12 @@ int run_fwd(const void* q, const void* k, const void* v, void* o, int dtype, int
 
 // Contiguous or ring f16 decode: kv_len logical tokens (ring: at rows t mod ring), eff of
 // them visible (the newest), window as the kernel applies it.
+// scratch_owned: the workspace is the library's scratch, whose previous contents are unknown:
+// its arrival counters are cleared on the stream before the launch.
 int run_decode_contiguous(const float* q, const void* k, const void* v, float* o, int num_heads,
                           int num_kv_heads, int head_dim, int kv_len, int ring, int eff, int window,
                           float attn_softcap, float scale, void* workspace, size_t workspace_bytes,
-                          void* stream, const char* what) {
+                          void* stream, const char* what, bool scratch_owned = false) {
     const DecodePlan plan = plan_decode(1, num_heads, num_kv_heads, head_dim, eff, false);
     const WorkspaceLayout wl = workspace_layout(1, num_heads, num_kv_heads, head_dim, plan);
     if (plan.n_split > 1) {
@@ -233,6 +235,11 @@ int run_decode_contiguous(const float* q, const void* k, const void* v, float* o
     fill_scalars(d, window, attn_softcap, scale);
     d.split_tokens = plan.split_tokens;
     d.n_split_max = plan.n_split;
+    if (scratch_owned && plan.n_split > 1) {
+        const int n_tickets = (int)((wl.total - wl.t_off) / sizeof(uint32_t));
+        const hipError_t e = ta03::zero_words(d.tickets, n_tickets, reinterpret_cast<hipStream_t>(stream));
+        if (e != hipSuccess) return launch_status(e, what);
+    }
     return launch_status(ta03::launch_decode(d, head_dim, plan.gc, false, 1,
                                              reinterpret_cast<hipStream_t>(stream)),
                          what);
@@ -342,6 +349,34 @@ int attn_decode(const float* q, const void* k, const void* v, float* o, int num_
     return run_decode_contiguous(q, k, v, o, num_heads, num_kv_heads, head_dim, kv_len, 0, eff,
                                  sliding_window, attn_softcap, scale, workspace, workspace_bytes,
                                  stream, "attn_decode");
+}
+
+int attn_decode_noalloc(const float* q, const void* k, const void* v, float* o, int num_heads,
+                        int num_kv_heads, int head_dim, int kv_len, int sliding_window, float attn_softcap,
+                        float scale, void* stream) {
+    const char* what = "attn_decode_noalloc";
+    TRY(check_ptr(q, "q"));
+    TRY(check_ptr(k, "k"));
+    TRY(check_ptr(v, "v"));
+    TRY(check_ptr(o, "o"));
+    TRY(check_heads(num_heads, num_kv_heads, head_dim));
+    if (kv_len < 1) return fail(ATTN_ERR_INVALID_ARG, "%s: invalid kv_len %d (must be >= 1)", what, kv_len);
+    TRY(check_scalars(sliding_window, attn_softcap, scale));
+    if ((long)kv_len * num_kv_heads * head_dim > kMaxElems) return fail(ATTN_ERR_INVALID_ARG, "%s: tensor too large", what);
+    const int eff = (sliding_window > 0 && sliding_window < kv_len) ? sliding_window : kv_len;
+    // the scratch needed by this call's plan (host arithmetic only, before any HIP call)
+    const DecodePlan plan = plan_decode(1, num_heads, num_kv_heads, head_dim, eff, false);
+    const size_t need = workspace_layout(1, num_heads, num_kv_heads, head_dim, plan).total;
+    if (need > ta03::decode_scratch_bytes())
+        return fail(ATTN_ERR_UNSUPPORTED,
+                    "%s: this shape needs %zu bytes of split partials, more than the %zu bytes of the "
+                    "library's scratch; use attn_decode with a workspace",
+                    what, need, ta03::decode_scratch_bytes());
+    void* ws = nullptr;
+    const hipError_t e = ta03::decode_scratch(&ws, reinterpret_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(ATTN_ERR_LAUNCH, "%s: scratch lookup failed: %s", what, hipGetErrorString(e));
+    return run_decode_contiguous(q, k, v, o, num_heads, num_kv_heads, head_dim, kv_len, 0, eff, sliding_window,
+                                 attn_softcap, scale, ws, ta03::decode_scratch_bytes(), stream, what, true);
 }
 
 int attn_decode_ring(const float* q, const void* k, const void* v, float* o, int num_heads,

@@ -39,6 +39,8 @@
 // DMA of a block's tail fetches the split's last valid row instead, and those tokens are
 // masked, so poisoned slots of a partial last page cannot reach the result.
 
+#include <mutex>
+
 #include "device_common.hpp"
 #include "launch.hpp"
 
@@ -1009,6 +1011,65 @@ hipError_t launch_decode_tiered(const DecodeParams& p, int head_dim, int gc, int
         case 256: return launch_tiered_d<256>(p, gc, grid, st);
     }
     return hipErrorInvalidValue;
+}
+
+// ---- library-owned scratch, for callers that cannot allocate ---------------------------------
+//
+// attn_decode_noalloc keeps the split partials and arrival counters in this array instead of
+// a caller workspace.  Each GPU the library runs on holds its own copy (loaded with the code
+// object) until the process ends.  In host code the name `scratch` is only a host-side
+// stand-in: its device address, different on every GPU, comes from hipGetSymbolAddress with
+// that GPU current, once per device, and only that address is ever handed to a kernel.
+
+namespace {
+
+constexpr size_t kScratchBytes = size_t(4) << 20;
+constexpr int kMaxDevices = 64;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+__global__ void __launch_bounds__(256) zero_u32_kernel(uint32_t* p, int n) {
+    for (int i = blockIdx.x * 256 + threadIdx.x; i < n; i += gridDim.x * 256) p[i] = 0u;
+}
+
+}  // namespace
+
+size_t decode_scratch_bytes() { return kScratchBytes; }
+
+hipError_t decode_scratch(void** ptr, hipStream_t st) {
+    int dev = 0;
+    hipError_t e = st ? hipStreamGetDevice(st, &dev) : hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        int cur = 0;
+        e = hipGetDevice(&cur);
+        if (e != hipSuccess) return e;
+        if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return e;
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (cur != dev) {
+            const hipError_t e2 = hipSetDevice(cur);
+            if (e == hipSuccess) e = e2;
+        }
+        if (e != hipSuccess) return e;
+        if (!p) return hipErrorInvalidSymbol;
+        g_scratch_ptr[dev] = p;
+    }
+    *ptr = g_scratch_ptr[dev];
+    return hipSuccess;
+}
+
+// Clears n uint32 words on the stream with a kernel (no memset node, so the call can also be
+// captured into a graph).
+hipError_t zero_words(uint32_t* p, int n, hipStream_t st) {
+    if (n <= 0) return hipSuccess;
+    const int blocks = (n + 255) / 256 < 64 ? (n + 255) / 256 : 64;
+    hipLaunchKernelGGL(zero_u32_kernel, dim3(blocks), dim3(256), 0, st, p, n);
+    return hipGetLastError();
 }
 
 int decode_tokens_per_block() { return kTB; }

@@ -74,6 +74,13 @@ int decode_max_split_tokens_paged();
 // tiered decode: grid (n_splits, Hkv * head chunks)
 hipError_t launch_decode_tiered(const DecodeParams& p, int head_dim, int gc, int n_splits, hipStream_t st);
 
+// Library-owned decode scratch of this GPU (the device of `st`, or the current device for
+// the null stream): its device address, looked up once per device.
+hipError_t decode_scratch(void** ptr, hipStream_t st);
+size_t decode_scratch_bytes();
+// n uint32 words set to zero by a kernel on `st`
+hipError_t zero_words(uint32_t* p, int n, hipStream_t st);
+
 // dtype: 0 f32, 1 f16
 hipError_t launch_fwd(const FwdParams& p, int head_dim, int dtype, hipStream_t st);
 // query rows per workgroup for this call shape (the launcher picks the same configuration)
