@@ -9,8 +9,11 @@ The arithmetic lives in ``oracle.c`` (plain C, double, two passes over a fully
 materialised score row).  This module only marshals numpy arrays into the
 canonical layouts that file documents and calls it.
 
-Every function here has a pin in ``tests/test_oracle_pins.py``; there is no
-"parity unpinned" function.
+Every function here has pins in ``tests/test_oracle_pins.py`` and
+``tests/test_oracle_block_local_pins.py``.  One part of ``block_local`` is a reading with no
+anchor on the pages: which row of the positional projection belongs to which key (the pages
+name the projection, not its indexing); the pins fix the oracle to that stated reading, not
+to the pages, so that term is "parity unpinned" against the pages.
 """
 from __future__ import annotations
 
@@ -53,6 +56,9 @@ def _load():
         lib.oracle_dequant_i8.argtypes = [
             ctypes.c_void_p, ctypes.c_void_p, ctypes.c_long, ctypes.c_int, dp]
         lib.oracle_dequant_i8.restype = None
+        lib.oracle_block_local_f64.argtypes = [
+            dp, dp, dp, dp, dp] + [ctypes.c_int] * 11 + [ctypes.c_double, ctypes.c_int]
+        lib.oracle_block_local_f64.restype = ctypes.c_int
         lib.oracle_threads_used.argtypes = []
         lib.oracle_threads_used.restype = ctypes.c_int
         _lib = lib
@@ -95,6 +101,46 @@ def attention(q, k, v, *, kv_len=None, causal=False, window=0, softcap=0.0, scal
         int(threads if threads else default_threads()))
     if rc != 0:
         raise ValueError("oracle_attention_f64 rejected its arguments")
+    return o
+
+
+def block_local(q, k, v, pos, *, seq, chunk_size, max_past, max_future, logit_cap=0.0,
+                context_size=None, max_span=None, pad_left=None, threads=None):
+    """Conformer block-local attention with a relative-position term, in float64.
+
+    q : [padded_len, H, D]; k, v : [kv_rows, H, D] with row r holding position r - pad_left;
+    pos : [max_span, H, D], row j the relative offset j - max_past.  context_size, max_span
+    and pad_left default to the consistent geometry (chunk + past + future, past + future +
+    1, past); other values are passed through so that the oracle's checks see them.
+    Returns o : [padded_len, H, D] float64 (rows past seq included).
+    """
+    q = np.ascontiguousarray(q, dtype=np.float64)
+    k = np.ascontiguousarray(k, dtype=np.float64)
+    v = np.ascontiguousarray(v, dtype=np.float64)
+    pos = np.ascontiguousarray(pos, dtype=np.float64)
+    if q.ndim != 3 or k.ndim != 3 or v.shape != k.shape or pos.ndim != 3:
+        raise ValueError("q [P,H,D], k/v [R,H,D], pos [span,H,D]")
+    P, H, D = q.shape
+    R = k.shape[0]
+    if k.shape[1:] != (H, D) or pos.shape[1:] != (H, D):
+        raise ValueError("head / head_dim mismatch")
+    if context_size is None:
+        context_size = chunk_size + max_past + max_future
+    if max_span is None:
+        max_span = max_past + max_future + 1
+    if pad_left is None:
+        pad_left = max_past
+    if pos.shape[0] != max_span:
+        raise ValueError("pos must have max_span rows")
+    o = np.zeros((P, H, D), dtype=np.float64)
+    dp = ctypes.POINTER(ctypes.c_double)
+    rc = _load().oracle_block_local_f64(
+        q.ctypes.data_as(dp), k.ctypes.data_as(dp), v.ctypes.data_as(dp), pos.ctypes.data_as(dp),
+        o.ctypes.data_as(dp), int(seq), P, R, H, D, int(chunk_size), int(context_size),
+        int(max_span), int(max_past), int(max_future), int(pad_left), float(logit_cap),
+        int(threads if threads else default_threads()))
+    if rc != 0:
+        raise ValueError("oracle_block_local_f64 rejected its arguments")
     return o
 
 

@@ -183,3 +183,148 @@ void oracle_dequant_i8(const int8_t *q8, const float *scale, long rows, int D, d
         for (int d = 0; d < D; ++d)
             out[r * D + d] = (double)q8[r * D + d] * (double)scale[r];
 }
+
+/*
+ * Conformer block-local attention with a relative-position term, in double precision.
+ *
+ * The pages (rullama 0.5.0, src/backend/dispatch/attention.rs,
+ * block_local_attention_chained and its doc comment) give the call, not the kernel:
+ * q_pad [padded_len, hidden] (Q projected and already per-dimension scaled),
+ * k_padded / v_padded [(pad_left + padded_len + pad_right), hidden] (K with its scale
+ * applied, zero padded), pos_proj [max_span, hidden] (sinusoidal relative positions
+ * through a linear projection), chunk_size, context_size, max_span, max_past,
+ * max_future, pad_left, logit_cap, head_dim 128, output [padded_len, hidden] of which
+ * the caller keeps the first seq rows.  Readings of what they leave open:
+ *   - hidden = H * D; head h owns columns [h D, (h + 1) D) of every row;
+ *   - query row i sits at position i; row r of k_padded / v_padded holds position
+ *     r - pad_left;
+ *   - query i sees key position t iff i - max_past <= t <= i + max_future and
+ *     0 <= t < seq (the zero padding outside [0, seq) is masked, not attended);
+ *   - row j of pos_proj is the relative offset j - max_past (key minus query): row 0
+ *     belongs to the key max_past positions before the query, row max_past to the
+ *     query's own position, row max_span - 1 to the key max_future after it;
+ *   - score s = q_i . k_t + q_i . pos_proj[t - i + max_past]; no further scale (the
+ *     scale is folded into q_pad); if logit_cap > 0, s = cap * tanh(s / cap); 0 = off;
+ *   - softmax over the visible keys, o_i = sum w v_t / sum w; a row with no visible key
+ *     (a padding row far past seq) is written as zeros;
+ *   - the geometry is consistent: max_span = max_past + max_future + 1,
+ *     context_size = chunk_size + max_past + max_future, pad_left = max_past,
+ *     padded_len a multiple of chunk_size, so the keys of every query of chunk c lie in
+ *     the context rows [c chunk_size, c chunk_size + context_size) of k_padded.  Under
+ *     this geometry the chunking changes which rows a kernel stages, never the result,
+ *     so the definition below needs no chunk loop.
+ *   q, o : [padded_len][H][D];  k, v : [kv_rows][H][D];  pos : [max_span][H][D]
+ * Returns 0, or -1 on an argument error (an inconsistent geometry included).
+ */
+typedef struct {
+    const double *q, *k, *v, *pos;
+    double *o;
+    int seq, padded_len, H, D, max_past, max_future, pad_left;
+    double cap;
+    long n_rows;
+    long grab;
+    long next;
+    int workers;
+    pthread_mutex_t mu;
+} bl_job_t;
+
+static void bl_row(const bl_job_t *J, int i, int h, double *score)
+{
+    const int D = J->D, H = J->H;
+    const double *qrow = J->q + ((long)i * H + h) * D;
+    double *orow = J->o + ((long)i * H + h) * D;
+    const int span = J->max_past + J->max_future + 1;
+
+    /* pass 1: scores of the visible keys t = i - max_past + j, j in [0, span) */
+    double m = -INFINITY;
+    int any = 0;
+    for (int j = 0; j < span; ++j) {
+        const long t = (long)i - J->max_past + j;
+        if (t < 0 || t >= J->seq) { score[j] = NAN; continue; }
+        const double *krow = J->k + ((t + J->pad_left) * H + h) * D;
+        const double *prow = J->pos + ((long)j * H + h) * D;
+        double content = 0.0, position = 0.0;
+        for (int d = 0; d < D; ++d) {
+            content += qrow[d] * krow[d];
+            position += qrow[d] * prow[d];
+        }
+        double s = content + position;
+        if (J->cap > 0.0) s = J->cap * tanh(s / J->cap);
+        score[j] = s;
+        if (s > m) m = s;
+        any = 1;
+    }
+    for (int d = 0; d < D; ++d) orow[d] = 0.0;
+    if (!any) return;
+
+    /* pass 2: weights, their sum and the weighted sum of V rows */
+    double l = 0.0;
+    for (int j = 0; j < span; ++j) {
+        if (isnan(score[j])) continue;
+        const long t = (long)i - J->max_past + j;
+        const double w = exp(score[j] - m);
+        l += w;
+        const double *vrow = J->v + ((t + J->pad_left) * H + h) * D;
+        for (int d = 0; d < D; ++d) orow[d] += w * vrow[d];
+    }
+    for (int d = 0; d < D; ++d) orow[d] /= l;
+}
+
+static void *bl_worker(void *arg)
+{
+    bl_job_t *J = (bl_job_t *)arg;
+    double *score = (double *)malloc(sizeof(double) * (size_t)(J->max_past + J->max_future + 1));
+    if (!score) return NULL;
+    int counted = 0;
+    for (;;) {
+        long r0;
+        pthread_mutex_lock(&J->mu);
+        r0 = J->next;
+        J->next += J->grab;
+        if (r0 < J->n_rows && !counted) {
+            counted = 1;
+            J->workers += 1;
+        }
+        pthread_mutex_unlock(&J->mu);
+        if (r0 >= J->n_rows) break;
+        long r1 = r0 + J->grab < J->n_rows ? r0 + J->grab : J->n_rows;
+        for (long r = r0; r < r1; ++r) bl_row(J, (int)(r / J->H), (int)(r % J->H), score);
+    }
+    free(score);
+    return NULL;
+}
+
+int oracle_block_local_f64(const double *q, const double *k, const double *v, const double *pos,
+                           double *o, int seq, int padded_len, int kv_rows, int H, int D,
+                           int chunk_size, int context_size, int max_span, int max_past,
+                           int max_future, int pad_left, double logit_cap, int nthreads)
+{
+    if (H < 1 || D < 1 || chunk_size < 1 || seq < 1 || padded_len < seq) return -1;
+    if (padded_len % chunk_size != 0 || max_past < 0 || max_future < 0) return -1;
+    if (max_span != max_past + max_future + 1) return -1;
+    if (context_size != chunk_size + max_past + max_future) return -1;
+    if (pad_left != max_past || kv_rows < pad_left + seq) return -1;
+    if (!(logit_cap >= 0.0)) return -1;
+    bl_job_t J;
+    memset(&J, 0, sizeof J);
+    J.q = q; J.k = k; J.v = v; J.pos = pos; J.o = o;
+    J.seq = seq; J.padded_len = padded_len; J.H = H; J.D = D;
+    J.max_past = max_past; J.max_future = max_future; J.pad_left = pad_left;
+    J.cap = logit_cap;
+    J.n_rows = (long)padded_len * H;
+    pthread_mutex_init(&J.mu, NULL);
+    if (nthreads < 1) nthreads = 1;
+    if (nthreads > 256) nthreads = 256;
+    J.grab = J.n_rows / (4L * nthreads);
+    if (J.grab < 1) J.grab = 1;
+    if (J.grab > 64) J.grab = 64;
+    pthread_t th[256];
+    int started = 0;
+    for (int t = 1; t < nthreads; ++t)
+        if (pthread_create(&th[started], NULL, bl_worker, &J) == 0) ++started;
+    bl_worker(&J);
+    for (int t = 0; t < started; ++t) pthread_join(th[t], NULL);
+    pthread_mutex_destroy(&J.mu);
+    g_threads_used = J.workers;
+    return 0;
+}
