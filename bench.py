@@ -52,7 +52,7 @@ def parse():
     ap.add_argument("--workload", default="decode_f16",
                     choices=["decode_f16", "prefill_f32", "prefill_f16", "vision_f16",
                              "decode_paged_q8", "prefill_chunk_f16", "decode_ring_f16",
-                             "decode_tiered_q8", "all"])
+                             "decode_tiered_q8", "block_local_f32", "all"])
     ap.add_argument("--repeats", type=int, default=5,
                     help="timed replays; the median is reported")
     ap.add_argument("--only-headline", action="store_true")
@@ -317,6 +317,64 @@ class Tiered(Workload):
         return self._oracle(threads)
 
 
+class BlockLocal(Workload):
+    """Conformer block-local attention (audio encoder): 3000 frames, 8 heads of 128, chunks
+    of 12 frames attending over 12 frames of past and none of future, logit cap 50, f32."""
+    name = "block_local_f32"
+    kind = "hbm"
+    kernel = "block_local_kernel<true>"
+
+    def __init__(self, dev, seq=3000, H=8, chunk=12, past=12, future=0, cap=50.0):
+        import numpy as np
+        import torch
+
+        import synth
+        import transformer_attention_03_amd as ta
+        self.ta, self.torch = ta, torch
+        self.seq, self.H, self.chunk, self.past, self.future, self.cap = seq, H, chunk, past, future, cap
+        d = synth.block_local_inputs(synth.seed_of(7), seq, chunk, past, future, H)
+        self.d = d
+        dv = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to(dev)
+        first = tuple(dv(d[x]) for x in ("q", "k", "v", "pos"))
+        per = sum(x.nbytes for x in first)
+        self.nc = n_copies(per)
+        self.copies = [first] + [tuple(x.clone() for x in first) for _ in range(self.nc - 1)]
+        self.o = torch.empty_like(first[0])
+        self.desc = {"workload": "Conformer block-local attention, f32, 3000 frames, 8 heads x "
+                                 "head_dim 128, chunk 12, max_past 12, max_future 0, logit cap 50, "
+                                 "relative-position projection [13, 1024]",
+                     "seq": seq, "num_heads": H, "head_dim": 128, "chunk_size": chunk,
+                     "max_past": past, "max_future": future, "logit_cap": cap,
+                     "input_copies": self.nc}
+
+    def step(self, i):
+        q, k, v, pos = self.copies[i % self.nc]
+        self.ta.attn_block_local(q, k, v, pos, self.o, seq=self.seq, chunk_size=self.chunk,
+                                 max_past=self.past, max_future=self.future, logit_cap=self.cap)
+
+    def units(self):
+        D, span = 128, self.past + self.future + 1
+        P = self.d["padded_len"]
+        b = 4 * self.H * D * (2 * P + 2 * self.seq + span)     # q, o, k and v rows of [0, seq), pos
+        return b, "bytes"
+
+    def _oracle(self, threads):
+        import oracle
+        d = self.d
+        return oracle.block_local(d["q"], d["k"], d["v"], d["pos"], seq=self.seq,
+                                  chunk_size=self.chunk, max_past=self.past,
+                                  max_future=self.future, logit_cap=self.cap, threads=threads)
+
+    def check(self):
+        import numpy as np
+        self.step(0)
+        self.torch.cuda.synchronize()
+        return float(np.abs(self.o.cpu().numpy() - self._oracle(None)).max())
+
+    def cpu_run(self, threads):
+        return self._oracle(threads)
+
+
 class Forward(Workload):
     """Prefill (token-major) or vision (head-major) forward."""
 
@@ -433,7 +491,7 @@ class Forward(Workload):
 
 
 ALL = ["decode_f16", "prefill_f32", "prefill_f16", "vision_f16", "decode_paged_q8", "prefill_chunk_f16",
-       "decode_ring_f16", "decode_tiered_q8"]
+       "decode_ring_f16", "decode_tiered_q8", "block_local_f32"]
 
 
 def make(name, dev):
@@ -445,6 +503,8 @@ def make(name, dev):
         return DecodeRing(dev)
     if name == "decode_tiered_q8":
         return Tiered(dev)
+    if name == "block_local_f32":
+        return BlockLocal(dev)
     return Forward(dev, name)
 
 
@@ -537,6 +597,13 @@ def summarize(wl, ms):
     return {"value": tfs, "unit": "TFLOP/s", "bound": "mfma", "achieved": tfs, "peak": peak,
             "peak_unit": "TFLOP/s", "frac": tfs / peak, "algorithmic_flops": amount,
             "us_per_call": ms * 1e3}
+
+
+def kernel_source(wl):
+    """The source file of a workload's kernel."""
+    if wl.kernel.startswith("block_local"):
+        return "block_local.hip"
+    return "decode.hip" if wl.kind == "hbm" else "fwd.hip"
 
 
 def traffic_for(kernel_src, kernel):
@@ -644,8 +711,7 @@ def main():
     log("%s max-abs error vs oracle %.3g; timing %d steps" % (head.name, err, a.steps))
     ms, per_replay = time_steps(head, a.steps, a.warmup, graph=not a.no_graph, repeats=a.repeats)
     s = summarize(head, ms)
-    src = os.path.join(ROOT, "transformer_attention_03_amd", "csrc",
-                       "decode.hip" if head.kind == "hbm" else "fwd.hip")
+    src = os.path.join(ROOT, "transformer_attention_03_amd", "csrc", kernel_source(head))
     roof = {"bound": s["bound"], "achieved": round(s["achieved"], 3), "peak": s["peak"],
             "unit": s["peak_unit"], "frac": round(s["frac"], 4),
             "traffic": traffic_for(src, head.kernel), "kernel": head.kernel}
@@ -683,8 +749,7 @@ def main():
                                          "frac": round(sw["frac"], 4), "kernel": wl.kernel,
                                          "traffic": traffic_for(os.path.join(
                                              ROOT, "transformer_attention_03_amd", "csrc",
-                                             "decode.hip" if wl.kind == "hbm" else "fwd.hip"),
-                                             wl.kernel)},
+                                             kernel_source(wl)), wl.kernel)},
                             "max_abs_err_vs_oracle": e}
             del wl
             torch.cuda.empty_cache()

@@ -252,6 +252,39 @@ int attn_decode_tiered_q8(const float *q, const void *hot_k, const void *hot_v,
                           void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * Conformer block-local self-attention with a relative-position term (rullama 0.5.0,
+ * src/backend/dispatch/attention.rs, block_local_attention_chained: the audio conformer's
+ * attention over chunks of chunk_size queries, each attending over a context of
+ * context_size keys, max_past before and max_future after, with a sinusoidal position
+ * table through a linear projection, an optional logit cap, head_dim 128).  float32.
+ *
+ *   q_pad    : [padded_len, num_heads * 128]  queries, already projected and scaled per
+ *              dimension (the kernel applies no further scale); row i is position i
+ *   k_padded,
+ *   v_padded : [kv_rows, num_heads * 128]  row r holds position r - pad_left; the rows of
+ *              positions outside [0, seq) are padding and never read
+ *   pos_proj : [max_span, num_heads * 128]  row j belongs to the key j - max_past positions
+ *              from the query (row max_past: the query's own position).  The pages name this
+ *              projection but not its indexing; this is the reading adopted.
+ *   attn_out : [padded_len, num_heads * 128]; rows >= seq are computed like the others (the
+ *              caller trims them); a row with no visible key is written as zeros
+ *   Query i sees key t iff i - max_past <= t <= i + max_future and 0 <= t < seq;
+ *   s = q_i . k_t + q_i . pos_proj[t - i + max_past]; if logit_cap > 0, s = c tanh(s / c);
+ *   o_i = softmax-weighted sum of the visible v_t.
+ *   Requires head_dim == 128 (else ATTN_ERR_UNSUPPORTED), 1 <= seq <= padded_len,
+ *   padded_len a multiple of chunk_size, max_span == max_past + max_future + 1,
+ *   context_size == chunk_size + max_past + max_future, pad_left == max_past,
+ *   kv_rows >= pad_left + seq, logit_cap finite >= 0 (else ATTN_ERR_INVALID_ARG), and
+ *   max_past + max_future <= 28 (else ATTN_ERR_UNSUPPORTED: the key window of 16 queries
+ *   and the position rows are staged in 64 KB of LDS).
+ */
+int attn_block_local(const float *q_pad, const float *k_padded, const float *v_padded,
+                     const float *pos_proj, float *attn_out,
+                     int seq, int padded_len, int kv_rows, int num_heads, int head_dim,
+                     int chunk_size, int context_size, int max_span, int max_past,
+                     int max_future, int pad_left, float logit_cap, void *stream);
+
+/*
  * Workspace bytes needed by attn_decode (batch = 1) and attn_decode_paged_q8 for the
  * given shape (split partials and arrival counters).  Returns 0 for invalid sizes.
  * Honours the calling thread's split override (attn_set_decode_split).

@@ -15,7 +15,8 @@ Generator (counter based, so any slice can be drawn independently):
   * values are drawn in float64, rounded to float32, then to float16 with
     round-to-nearest-even where a tensor is stored in f16.
   * stream seed = seed_c * 256 + tensor_id, with tensor ids Q=1, K=2, V=3,
-    kv lengths=4, page permutation=5, alternative permutation=6, hot-tier K=7, hot-tier V=8.
+    kv lengths=4, page permutation=5, alternative permutation=6, hot-tier K=7, hot-tier V=8,
+    positional projection=9.
 """
 from __future__ import annotations
 
@@ -308,3 +309,31 @@ def tiered_inputs(seed_c, h, hkv, d, cold_len, hot_len, hot_window, hot_start, n
     return dict(q=cold["q"][0], cold=cold, hot_k=hot_k, hot_v=hot_v, ring_k=ring_k, ring_v=ring_v,
                 cold_len=int(cold_len), hot_len=int(hot_len), hot_start=int(hot_start))
 
+
+
+TID_POS = 9
+
+
+def block_local_inputs(seed_c, seq, chunk_size, max_past, max_future, h, d=128,
+                       q_scale=None):
+    """Conformer block-local inputs, float32.
+
+    q_pad [padded_len, h, d] with padded_len = seq rounded up to a multiple of chunk_size;
+    k_padded, v_padded [max_past + padded_len + max_future, h, d] (row r is position
+    r - max_past; the rows of positions outside [0, seq) are zeros, as in the pages'
+    zero-padded buffers); pos_proj [max_past + max_future + 1, h, d].  Values N(0, 1),
+    except q, drawn N(0, 1) and multiplied by q_scale (default 1/sqrt(d): the pages' q_pad
+    arrives already scaled per dimension), so that the scores have unit order.  Stream ids:
+    Q 1, K 2, V 3, pos 9.
+    """
+    P = -(-seq // chunk_size) * chunk_size
+    R = max_past + P + max_future
+    span = max_past + max_future + 1
+    qs = np.float32(1.0 / math.sqrt(d) if q_scale is None else q_scale)
+    q = normal_f32(stream_seed(seed_c, TID_Q), (P, h, d)) * qs
+    k = np.zeros((R, h, d), dtype=np.float32)
+    v = np.zeros((R, h, d), dtype=np.float32)
+    k[max_past:max_past + seq] = normal_f32(stream_seed(seed_c, TID_K), (seq, h, d))
+    v[max_past:max_past + seq] = normal_f32(stream_seed(seed_c, TID_V), (seq, h, d))
+    pos = normal_f32(stream_seed(seed_c, TID_POS), (span, h, d))
+    return {"q": q, "k": k, "v": v, "pos": pos, "padded_len": P, "kv_rows": R}

@@ -266,3 +266,30 @@ def test_noalloc_refuses_shapes_beyond_its_scratch():
     assert "scratch" in ta.attn_last_error() and "4194304" in ta.attn_last_error()
     rc = L.attn_decode_noalloc(None, P, P, P, 32, 8, 128, 4096, 0, 0.0, 0.088, None)
     assert rc == ta.ATTN_ERR_INVALID_ARG and "q must not be null" in ta.attn_last_error()
+
+
+def block_local(**kw):
+    a = dict(q=P, k=P, v=P, pos=P, o=P, seq=30, padded=36, rows=48, H=2, D=128, chunk=12,
+             context=24, span=13, past=12, future=0, pad=12, cap=50.0)
+    a.update(kw)
+    return ta.lib().attn_block_local(a["q"], a["k"], a["v"], a["pos"], a["o"], a["seq"], a["padded"],
+                                     a["rows"], a["H"], a["D"], a["chunk"], a["context"], a["span"],
+                                     a["past"], a["future"], a["pad"], a["cap"], None)
+
+
+@pytest.mark.parametrize("kw,code,msg", [
+    (dict(pos=None), ta.ATTN_ERR_INVALID_ARG, "pos_proj must not be null"),
+    (dict(D=64), ta.ATTN_ERR_UNSUPPORTED, "requires head_dim == 128"),
+    (dict(seq=40), ta.ATTN_ERR_INVALID_ARG, "seq"),
+    (dict(padded=30), ta.ATTN_ERR_INVALID_ARG, "multiple of chunk_size"),
+    (dict(span=12), ta.ATTN_ERR_INVALID_ARG, "max_span"),
+    (dict(context=25), ta.ATTN_ERR_INVALID_ARG, "context_size"),
+    (dict(pad=0), ta.ATTN_ERR_INVALID_ARG, "pad_left"),
+    (dict(rows=41), ta.ATTN_ERR_INVALID_ARG, "kv_rows"),
+    (dict(past=20, future=9, span=30, context=41, pad=20, rows=56), ta.ATTN_ERR_UNSUPPORTED, "max_span <= 29"),
+    (dict(cap=-1.0), ta.ATTN_ERR_INVALID_ARG, "logit_cap"),
+    (dict(H=0), ta.ATTN_ERR_INVALID_ARG, "num_heads"),
+])
+def test_block_local_validation(kw, code, msg):
+    assert block_local(**kw) == code
+    assert msg in ta.attn_last_error()

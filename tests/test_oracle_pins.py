@@ -346,10 +346,11 @@ MUTATIONS = {
     "interleaved_kv_heads": ("const int kvh = h / G;", "const int kvh = h % J->Hkv;"),
     "window_off_by_one": ("p - j >= J->window", "p - j > J->window"),
     "no_softcap": ("if (J->softcap > 0.0) s =", "if (J->softcap < 0.0) s ="),
-    "v_is_k": ("const double *vrow = J->v +", "const double *vrow = J->k +"),
+    "v_is_k": ("const double *vrow = J->v + (((long)b", "const double *vrow = J->k + (((long)b"),
     "causal_strict": ("if (J->causal && j > p)", "if (J->causal && j >= p)"),
     "query_at_start": ("const long p = (long)L - J->S + i;", "const long p = i;"),
-    "no_normalise": ("orow[d] /= l;", "orow[d] /= 1.0;"),
+    "no_normalise": ("for (int d = 0; d < J->D; ++d) orow[d] /= l;",
+                     "for (int d = 0; d < J->D; ++d) orow[d] /= 1.0;"),
 }
 
 

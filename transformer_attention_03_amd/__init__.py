@@ -15,6 +15,7 @@ import os
 __all__ = [
     "AttnError", "lib", "attn_prefill", "attn_prefill_device_kv_len", "attn_vision", "attn_decode",
     "attn_decode_noalloc", "attn_decode_ring", "attn_decode_paged_q8", "attn_decode_tiered_q8",
+    "attn_block_local",
     "attn_decode_workspace_bytes", "attn_set_decode_split", "attn_last_error", "decode_workspace",
     "ATTN_OK", "ATTN_ERR_INVALID_ARG", "ATTN_ERR_UNSUPPORTED", "ATTN_ERR_WORKSPACE",
     "ATTN_ERR_LAUNCH", "ATTN_F32", "ATTN_F16", "LIB_PATH",
@@ -52,13 +53,14 @@ def lib() -> ctypes.CDLL:
                                            f, f, vp, sz, vp]
         L.attn_decode_tiered_q8.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i,
                                             i, i, i, f, f, vp, sz, vp]
+        L.attn_block_local.argtypes = [vp, vp, vp, vp, vp] + [i] * 11 + [f, vp]
         L.attn_decode_workspace_bytes.argtypes = [i, i, i, i, i]
         L.attn_decode_workspace_bytes.restype = sz
         L.attn_set_decode_split.argtypes = [i]
         L.attn_last_error.argtypes = []
         L.attn_last_error.restype = ctypes.c_char_p
         for name in ("attn_prefill", "attn_prefill_device_kv_len", "attn_vision", "attn_decode",
-                     "attn_decode_noalloc", "attn_decode_ring", "attn_decode_paged_q8", "attn_decode_tiered_q8",
+                     "attn_decode_noalloc", "attn_decode_ring", "attn_block_local", "attn_decode_paged_q8", "attn_decode_tiered_q8",
                      "attn_set_decode_split"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
@@ -302,3 +304,34 @@ def attn_decode_tiered_q8(q, hot_k, hot_v, cold_k_pages, cold_v_pages, cold_k_sc
         int(sliding_window), float(attn_softcap), float(scale), _ptr(workspace), ws_bytes,
         _stream(q, stream)))
 
+
+
+def attn_block_local(q_pad, k_padded, v_padded, pos_proj, attn_out, *, seq: int, chunk_size: int,
+                     max_past: int, max_future: int, logit_cap: float = 0.0, context_size=None,
+                     max_span=None, pad_left=None, stream=None):
+    """Conformer block-local attention, float32.  q_pad, attn_out: [padded_len, H, 128];
+    k_padded, v_padded: [kv_rows, H, 128] with row r at position r - pad_left; pos_proj:
+    [max_span, H, 128].  context_size, max_span and pad_left default to chunk + past +
+    future, past + future + 1 and past."""
+    _need("attn_block_local", q_pad=(q_pad, "float32"), k_padded=(k_padded, "float32"),
+          v_padded=(v_padded, "float32"), pos_proj=(pos_proj, "float32"),
+          attn_out=(attn_out, "float32"))
+    _need_contig(q_pad, k_padded, v_padded, pos_proj, attn_out)
+    P, H, D = q_pad.shape
+    R = k_padded.shape[0]
+    if k_padded.shape[1:] != (H, D) or v_padded.shape != k_padded.shape or \
+            pos_proj.shape[1:] != (H, D) or attn_out.shape != q_pad.shape:
+        raise ValueError("shape mismatch")
+    if context_size is None:
+        context_size = chunk_size + max_past + max_future
+    if max_span is None:
+        max_span = max_past + max_future + 1
+    if pad_left is None:
+        pad_left = max_past
+    if pos_proj.shape[0] != max_span:
+        raise ValueError("pos_proj must have max_span rows")
+    _check(lib().attn_block_local(_ptr(q_pad), _ptr(k_padded), _ptr(v_padded), _ptr(pos_proj),
+                                  _ptr(attn_out), int(seq), P, R, H, D, int(chunk_size),
+                                  int(context_size), int(max_span), int(max_past),
+                                  int(max_future), int(pad_left), float(logit_cap),
+                                  _stream(q_pad, stream)))

@@ -21,7 +21,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libattn.so")
 BUILD_DIR = os.path.join(PKG, "_build")
 
-SOURCES = ["api.cpp", "decode.hip", "fwd.hip"]
+SOURCES = ["api.cpp", "decode.hip", "fwd.hip", "block_local.hip"]
 # per-source extra hipcc flags (none at present)
 KERNEL_FLAGS = {}
 ARCH = os.environ.get("TA03_OFFLOAD_ARCH", "gfx950")

@@ -593,6 +593,54 @@ int attn_decode_tiered_q8(const float* q, const void* hot_k, const void* hot_v, 
                          what);
 }
 
+int attn_block_local(const float* q_pad, const float* k_padded, const float* v_padded, const float* pos_proj,
+                     float* attn_out, int seq, int padded_len, int kv_rows, int num_heads, int head_dim,
+                     int chunk_size, int context_size, int max_span, int max_past, int max_future, int pad_left,
+                     float logit_cap, void* stream) {
+    const char* what = "attn_block_local";
+    TRY(check_ptr(q_pad, "q_pad"));
+    TRY(check_ptr(k_padded, "k_padded"));
+    TRY(check_ptr(v_padded, "v_padded"));
+    TRY(check_ptr(pos_proj, "pos_proj"));
+    TRY(check_ptr(attn_out, "attn_out"));
+    if (num_heads < 1) return fail(ATTN_ERR_INVALID_ARG, "%s: num_heads %d must be >= 1", what, num_heads);
+    if (head_dim != ta03::block_local_head_dim())
+        return fail(ATTN_ERR_UNSUPPORTED, "%s: requires head_dim == %d (got %d)", what,
+                    ta03::block_local_head_dim(), head_dim);
+    if (seq < 1 || padded_len < seq)
+        return fail(ATTN_ERR_INVALID_ARG, "%s: requires 1 <= seq (%d) <= padded_len (%d)", what, seq, padded_len);
+    if (chunk_size < 1 || padded_len % chunk_size != 0)
+        return fail(ATTN_ERR_INVALID_ARG, "%s: padded_len %d must be a positive multiple of chunk_size %d", what,
+                    padded_len, chunk_size);
+    if (max_past < 0 || max_future < 0)
+        return fail(ATTN_ERR_INVALID_ARG, "%s: max_past (%d) and max_future (%d) must be >= 0", what, max_past,
+                    max_future);
+    if ((long)max_span != (long)max_past + max_future + 1)
+        return fail(ATTN_ERR_INVALID_ARG, "%s: requires max_span (%d) == max_past + max_future + 1", what, max_span);
+    if ((long)context_size != (long)chunk_size + max_past + max_future)
+        return fail(ATTN_ERR_INVALID_ARG, "%s: requires context_size (%d) == chunk_size + max_past + max_future",
+                    what, context_size);
+    if (pad_left != max_past)
+        return fail(ATTN_ERR_INVALID_ARG, "%s: requires pad_left (%d) == max_past (%d)", what, pad_left, max_past);
+    if ((long)kv_rows < (long)pad_left + seq)
+        return fail(ATTN_ERR_INVALID_ARG, "%s: kv_rows %d must be >= pad_left + seq = %ld", what, kv_rows,
+                    (long)pad_left + seq);
+    if (max_span > ta03::block_local_max_span())
+        return fail(ATTN_ERR_UNSUPPORTED, "%s: requires max_span <= %d (max_past + max_future <= %d)", what,
+                    ta03::block_local_max_span(), ta03::block_local_max_span() - 1);
+    if (!std::isfinite(logit_cap) || logit_cap < 0.f)
+        return fail(ATTN_ERR_INVALID_ARG, "%s: logit_cap must be finite and >= 0 (0 = off)", what);
+    const long hidden = (long)num_heads * head_dim;
+    if ((long)padded_len * hidden > kMaxElems || (long)kv_rows * hidden > kMaxElems || num_heads > 65535)
+        return fail(ATTN_ERR_INVALID_ARG, "%s: tensor too large", what);
+    ta03::BlockLocalParams p;
+    p.q = q_pad; p.k = k_padded; p.v = v_padded; p.pos = pos_proj; p.o = attn_out;
+    p.seq = seq; p.padded_len = padded_len; p.H = num_heads;
+    p.max_past = max_past; p.max_future = max_future; p.pad_left = pad_left;
+    p.cap = logit_cap; p.inv_cap = logit_cap > 0.f ? 1.0f / logit_cap : 0.f;
+    return launch_status(ta03::launch_block_local(p, reinterpret_cast<hipStream_t>(stream)), what);
+}
+
 const char* attn_last_error(void) { return g_err; }
 
 }  // extern "C"

@@ -1,0 +1,170 @@
+// Conformer block-local attention with a relative-position term, for gfx950, f32.
+//
+// The pages give the call (rullama 0.5.0, src/backend/dispatch/attention.rs,
+// block_local_attention_chained): Q already projected and scaled per dimension, K and V
+// zero padded by pad_left rows in front, a positional projection pos_proj of max_span rows,
+// queries grouped in chunks of chunk_size that attend over a context of context_size keys
+// (max_past before, max_future after), an optional logit cap, head_dim 128.  The reading
+// implemented: query i sees key position t iff i - max_past <= t <= i + max_future and
+// 0 <= t < seq; score q_i.k_t + q_i.pos_proj[t - i + max_past], capped c tanh(s / c) when
+// c > 0; softmax over the visible keys; rows without a visible key are zeros.  With the
+// consistent geometry (context = chunk + past + future, span = past + future + 1, pad_left
+// = past) the chunks only decide which rows a kernel stages, so the kernel tiles the
+// queries as suits the hardware instead.
+//
+// Work decomposition: a workgroup owns 16 consecutive query rows of one head.  Their keys
+// lie in a window of 16 + past + future rows, which is staged in LDS once (K and V) with
+// the head's pos_proj rows; a 16-lane group owns one query row (each lane 8 of its 128
+// dimensions, the query itself in registers), walks the row's span of offsets computing
+// q.(k + pos) with a 16-lane butterfly sum, then the softmax and the weighted V rows.  The
+// work is a band of at most span keys per query, a few thousand FLOP per output row: the
+// kernel is bound by moving Q, K, V and O, not by arithmetic, so it runs on the vector ALU
+// with no matrix products.
+
+#include "device_common.hpp"
+#include "launch.hpp"
+
+namespace ta03 {
+
+namespace {
+
+constexpr int kBlD = 128;                 // head_dim (the pages fix it)
+constexpr int kBlRows = 16;               // query rows per workgroup (one per 16-lane group)
+constexpr int kBlStride = kBlD + 4;       // LDS row stride in floats (shifts rows across banks)
+constexpr int kBlMaxSpan = 29;            // past + future + 1 <= 29: K, V windows and pos_proj
+                                          // rows fit 64 KB of LDS (61.8 KB at the limit)
+
+template <bool CAP>
+__global__ void __launch_bounds__(256) block_local_kernel(BlockLocalParams a) {
+    extern __shared__ __attribute__((aligned(16))) float bl_lds[];
+    const int span = a.max_past + a.max_future + 1;
+    const int nwin = kBlRows + span - 1;           // window rows of this workgroup
+    float* kw = bl_lds;                            // [nwin][stride]
+    float* vw = kw + nwin * kBlStride;             // [nwin][stride]
+    float* pw = vw + nwin * kBlStride;             // [span][stride]
+
+    const int head = blockIdx.y;
+    const int i0 = blockIdx.x * kBlRows;
+    const int w0 = i0 - a.max_past;                // position of window row 0
+    const long hid = (long)a.H * kBlD;             // floats per row of every tensor
+    const int tid = threadIdx.x;
+
+    // ---- stage the window's K and V rows (positions inside [0, seq) only) and pos_proj ----
+    for (int c = tid; c < nwin * (kBlD / 4); c += 256) {
+        const int r = c / (kBlD / 4), d4 = c % (kBlD / 4);
+        const int t = w0 + r;
+        if (t >= 0 && t < a.seq) {
+            const long g = (long)(t + a.pad_left) * hid + (long)head * kBlD + 4 * d4;
+            *reinterpret_cast<float4*>(kw + r * kBlStride + 4 * d4) = *reinterpret_cast<const float4*>(a.k + g);
+            *reinterpret_cast<float4*>(vw + r * kBlStride + 4 * d4) = *reinterpret_cast<const float4*>(a.v + g);
+        }
+    }
+    for (int c = tid; c < span * (kBlD / 4); c += 256) {
+        const int r = c / (kBlD / 4), d4 = c % (kBlD / 4);
+        *reinterpret_cast<float4*>(pw + r * kBlStride + 4 * d4) =
+            *reinterpret_cast<const float4*>(a.pos + (long)r * hid + (long)head * kBlD + 4 * d4);
+    }
+
+    // ---- this lane's query row and dimensions: row g = tid / 16, d in 4 l + {0..3}, 64 + 4 l + {0..3}
+    const int g = tid >> 4;
+    const int l = tid & 15;
+    const int qi = i0 + g;
+    const bool live = qi < a.padded_len;
+    float4 q0 = {0.f, 0.f, 0.f, 0.f}, q1 = {0.f, 0.f, 0.f, 0.f};
+    if (live) {
+        const float* qrow = a.q + (long)qi * hid + (long)head * kBlD;
+        q0 = *reinterpret_cast<const float4*>(qrow + 4 * l);
+        q1 = *reinterpret_cast<const float4*>(qrow + 64 + 4 * l);
+    }
+    __syncthreads();
+
+    // visible offsets j of this row: t = qi - past + j in [0, seq)
+    const int j_lo = max(0, a.max_past - qi);
+    const int j_hi = min(span - 1, a.seq - 1 - qi + a.max_past);
+
+    // ---- scores, held by every lane of the group (the butterfly leaves the sum everywhere) --
+    float s[kBlMaxSpan];
+    float m = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < kBlMaxSpan; ++j) {
+        s[j] = -INFINITY;
+        if (j < span && j >= j_lo && j <= j_hi) {
+            const float* kr = kw + (g + j) * kBlStride;
+            const float* pr = pw + j * kBlStride;
+            const float4 k0 = *reinterpret_cast<const float4*>(kr + 4 * l);
+            const float4 k1 = *reinterpret_cast<const float4*>(kr + 64 + 4 * l);
+            const float4 p0 = *reinterpret_cast<const float4*>(pr + 4 * l);
+            const float4 p1 = *reinterpret_cast<const float4*>(pr + 64 + 4 * l);
+            float acc = q0.x * k0.x;
+            acc = __builtin_fmaf(q0.y, k0.y, acc);
+            acc = __builtin_fmaf(q0.z, k0.z, acc);
+            acc = __builtin_fmaf(q0.w, k0.w, acc);
+            acc = __builtin_fmaf(q1.x, k1.x, acc);
+            acc = __builtin_fmaf(q1.y, k1.y, acc);
+            acc = __builtin_fmaf(q1.z, k1.z, acc);
+            acc = __builtin_fmaf(q1.w, k1.w, acc);
+            float pacc = q0.x * p0.x;
+            pacc = __builtin_fmaf(q0.y, p0.y, pacc);
+            pacc = __builtin_fmaf(q0.z, p0.z, pacc);
+            pacc = __builtin_fmaf(q0.w, p0.w, pacc);
+            pacc = __builtin_fmaf(q1.x, p1.x, pacc);
+            pacc = __builtin_fmaf(q1.y, p1.y, pacc);
+            pacc = __builtin_fmaf(q1.z, p1.z, pacc);
+            pacc = __builtin_fmaf(q1.w, p1.w, pacc);
+            float x = group_sum<16>(acc + pacc);
+            if constexpr (CAP) x = a.cap * tanhf(x * a.inv_cap);
+            s[j] = x;
+            m = fmaxf(m, x);
+        }
+    }
+
+    // ---- softmax over the visible offsets, then the weighted sum of V rows --------------
+    float lsum = 0.f;
+    float4 o0 = {0.f, 0.f, 0.f, 0.f}, o1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < kBlMaxSpan; ++j) {
+        if (j < span && j >= j_lo && j <= j_hi) {
+            const float p = __builtin_amdgcn_exp2f((s[j] - m) * kLog2e);
+            lsum += p;
+            const float* vr = vw + (g + j) * kBlStride;
+            const float4 v0 = *reinterpret_cast<const float4*>(vr + 4 * l);
+            const float4 v1 = *reinterpret_cast<const float4*>(vr + 64 + 4 * l);
+            o0.x = __builtin_fmaf(p, v0.x, o0.x);
+            o0.y = __builtin_fmaf(p, v0.y, o0.y);
+            o0.z = __builtin_fmaf(p, v0.z, o0.z);
+            o0.w = __builtin_fmaf(p, v0.w, o0.w);
+            o1.x = __builtin_fmaf(p, v1.x, o1.x);
+            o1.y = __builtin_fmaf(p, v1.y, o1.y);
+            o1.z = __builtin_fmaf(p, v1.z, o1.z);
+            o1.w = __builtin_fmaf(p, v1.w, o1.w);
+        }
+    }
+    if (live) {
+        const float inv = lsum > 0.f ? 1.0f / lsum : 0.f;
+        float* orow = a.o + (long)qi * hid + (long)head * kBlD;
+        *reinterpret_cast<float4*>(orow + 4 * l) = float4{o0.x * inv, o0.y * inv, o0.z * inv, o0.w * inv};
+        *reinterpret_cast<float4*>(orow + 64 + 4 * l) = float4{o1.x * inv, o1.y * inv, o1.z * inv, o1.w * inv};
+    }
+}
+
+}  // namespace
+
+int block_local_max_span() { return kBlMaxSpan; }
+int block_local_head_dim() { return kBlD; }
+
+size_t block_local_lds_bytes(int max_past, int max_future) {
+    const int span = max_past + max_future + 1;
+    return sizeof(float) * (size_t)kBlStride * (2 * (kBlRows + span - 1) + span);
+}
+
+hipError_t launch_block_local(const BlockLocalParams& p, hipStream_t st) {
+    const dim3 grid((p.padded_len + kBlRows - 1) / kBlRows, p.H);
+    const size_t lds = block_local_lds_bytes(p.max_past, p.max_future);
+    if (p.cap > 0.f)
+        hipLaunchKernelGGL(block_local_kernel<true>, grid, dim3(256), lds, st, p);
+    else
+        hipLaunchKernelGGL(block_local_kernel<false>, grid, dim3(256), lds, st, p);
+    return hipGetLastError();
+}
+
+}  // namespace ta03

@@ -63,6 +63,21 @@ struct FwdParams {
     const int32_t* kv_len_dev; // optional: the kv length, read on the device (kv_len is then its maximum)
 };
 
+struct BlockLocalParams {
+    const float* q;            // [padded_len][H * 128]
+    const float* k;            // [kv_rows][H * 128], row r = position r - pad_left
+    const float* v;
+    const float* pos;          // [max_past + max_future + 1][H * 128]
+    float* o;                  // [padded_len][H * 128]
+    int seq, padded_len, H;
+    int max_past, max_future, pad_left;
+    float cap, inv_cap;        // logit cap (0 = off) and its inverse
+};
+
+hipError_t launch_block_local(const BlockLocalParams& p, hipStream_t st);
+int block_local_max_span();
+int block_local_head_dim();
+
 hipError_t launch_decode(const DecodeParams& p, int head_dim, int gc, bool paged, int batch,
                          hipStream_t st);
 int decode_tokens_per_block();
