@@ -285,6 +285,62 @@ int attn_block_local(const float *q_pad, const float *k_padded, const float *v_p
                      int max_future, int pad_left, float logit_cap, void *stream);
 
 /*
+ * Tiered decode with an int8 cold tier stored contiguously ("packed", no page table), as
+ * doppler attention.js executeAttentionTieredQuant binds it (packed int8 cold K and V, K and V
+ * scale buffers, packedStride, f32 Q required, no page table).  The same computation and
+ * readings as attn_decode_tiered_q8; only the cold tier's addressing differs.
+ *
+ *   cold_k, cold_v          : int8 [num_kv_heads, cold_capacity, head_dim]; position p <
+ *                             cold_len of KV head h at row h * cold_capacity + p (the pages'
+ *                             packedStride, the row pitch of the packed tier, is fixed by this
+ *                             head-major layout: head_dim bytes per row, cold_capacity rows per
+ *                             head)
+ *   cold_k_scales,
+ *   cold_v_scales           : float32 [num_kv_heads, cold_capacity]; value = q8 * scale
+ *   Requires cold_capacity >= cold_len; other arguments and errors as attn_decode_tiered_q8
+ *   (the workspace is sized the same way).
+ */
+int attn_decode_tiered_q8_packed(const float *q, const void *hot_k, const void *hot_v,
+                                 const int8_t *cold_k, const int8_t *cold_v,
+                                 const float *cold_k_scales, const float *cold_v_scales, float *o,
+                                 int num_heads, int num_kv_heads, int head_dim,
+                                 int cold_len, int hot_len, int hot_window, int hot_start,
+                                 int cold_capacity, int sliding_window, float attn_softcap,
+                                 float scale, void *workspace, size_t workspace_bytes, void *stream);
+
+/* Cold-tier layouts of attn_decode_tiered_f16, with the codes of the pages' coldLayout. */
+typedef enum {
+    ATTN_COLD_CONTIGUOUS = 0,    /* [num_kv_heads, cold_capacity, head_dim], no page table    */
+    ATTN_COLD_PAGED = 2          /* 16-token pages [num_pages, num_kv_heads, 16, head_dim]     */
+} attn_cold_layout;
+
+/*
+ * Tiered decode with an f16 cold tier (doppler attention.js executeAttentionTiered /
+ * createTieredAttentionUniformBuffer: f16 hot and cold K/V, coldLen, hotLen, hotWindow,
+ * hotStart, coldPageTable, coldPageSize, coldLayout 2 = paged / 0 = contiguous, hotLayout
+ * 1 = ring; doppler run.js passes coldLayout = coldPageTable ? 2 : 0).  The same positions,
+ * window, cap and readings as attn_decode_tiered_q8; the cold tier holds f16 rows.
+ *
+ *   q, o           : float32 [num_heads, head_dim]
+ *   hot_k, hot_v   : float16 ring [num_kv_heads, hot_window, head_dim], as attn_decode_tiered_q8
+ *   cold_layout    : ATTN_COLD_PAGED: cold_k, cold_v float16 [num_pages, num_kv_heads, 16,
+ *                    head_dim] (head-major within a page), cold_page_table int32
+ *                    [cold_capacity / 16] mapping logical page i (positions 16 i .. 16 i + 15)
+ *                    to a physical page (out-of-range entries are clamped into [0, num_pages));
+ *                    cold_capacity must be a multiple of 16 and page_size 16.
+ *                    ATTN_COLD_CONTIGUOUS: cold_k, cold_v float16 [num_kv_heads, cold_capacity,
+ *                    head_dim]; cold_page_table must be NULL; page_size and num_pages unused.
+ *   Requires cold_len <= cold_capacity; other arguments and errors as attn_decode_tiered_q8.
+ */
+int attn_decode_tiered_f16(const float *q, const void *hot_k, const void *hot_v,
+                           const void *cold_k, const void *cold_v, const int32_t *cold_page_table,
+                           float *o, int num_heads, int num_kv_heads, int head_dim,
+                           int cold_len, int hot_len, int hot_window, int hot_start,
+                           int cold_layout, int cold_capacity, int page_size, int num_pages,
+                           int sliding_window, float attn_softcap, float scale,
+                           void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * Workspace bytes needed by attn_decode (batch = 1) and attn_decode_paged_q8 for the
  * given shape (split partials and arrival counters).  Returns 0 for invalid sizes.
  * Honours the calling thread's split override (attn_set_decode_split).

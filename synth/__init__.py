@@ -311,6 +311,71 @@ def tiered_inputs(seed_c, h, hkv, d, cold_len, hot_len, hot_window, hot_start, n
 
 
 
+def build_pages_f16(rows, seed_perm: int, n_poison: int = 16, max_pages=None):
+    """Scatter one sequence's f16 rows [L, hkv, d] into 16-token pages [n_pages, hkv, 16, d]
+    (head-major within a page) placed by a seeded permutation; page table int32 [max_pages]
+    (entries past the last page -1).  Unreferenced pages and the slots past L of a last
+    partial page hold NaN."""
+    L, hkv, d = rows.shape
+    n_live = (L + PAGE - 1) // PAGE
+    n_pages = max(1, n_live + n_poison)
+    if max_pages is None:
+        max_pages = max(1, n_live)
+    perm = fisher_yates(seed_perm, n_pages)
+    pages = np.full((n_pages, hkv, PAGE, d), np.nan, dtype=np.float16)
+    table = np.full(max_pages, -1, dtype=np.int32)
+    phys = perm[:n_live]
+    table[:n_live] = phys
+    for i, pg in enumerate(phys):
+        blk = rows[i * PAGE:(i + 1) * PAGE]
+        pages[pg, :, :blk.shape[0]] = np.transpose(blk, (1, 0, 2))
+    return pages, table
+
+
+def tiered_f16_inputs(seed_c, h, hkv, d, cold_len, hot_len, hot_window, hot_start, paged,
+                      capacity=None, n_poison=16):
+    """A tiered cache with an f16 cold tier.  The hot tier and q are those of tiered_inputs
+    (same streams); the cold tier holds f16 rows [cold_len, hkv, d] drawn N(0, 1) from the K
+    and V streams, either paged (build_pages_f16, seeded permutation) or contiguous
+    [hkv, capacity, d] with NaN in the rows past cold_len (capacity defaults to cold_len + 16)."""
+    t = tiered_inputs(seed_c, h, hkv, d, 0, hot_len, hot_window, hot_start, n_poison=1)
+    ck = normal_f16(stream_seed(seed_c, TID_K), (cold_len, hkv, d))
+    cv = normal_f16(stream_seed(seed_c, TID_V), (cold_len, hkv, d))
+    t["cold_k"], t["cold_v"] = ck, cv
+    t["cold_len"] = int(cold_len)
+    if paged:
+        t["cold_k_pages"], t["cold_page_table"] = build_pages_f16(ck, stream_seed(seed_c, TID_PERM), n_poison)
+        t["cold_v_pages"], _ = build_pages_f16(cv, stream_seed(seed_c, TID_PERM), n_poison)
+    else:
+        cap = cold_len + 16 if capacity is None else capacity
+        kk = np.full((hkv, cap, d), np.nan, np.float16)
+        vv = np.full((hkv, cap, d), np.nan, np.float16)
+        kk[:, :cold_len] = np.transpose(ck, (1, 0, 2))
+        vv[:, :cold_len] = np.transpose(cv, (1, 0, 2))
+        t["cold_k_contig"], t["cold_v_contig"] = kk, vv
+    return t
+
+
+def tiered_packed_inputs(seed_c, h, hkv, d, cold_len, hot_len, hot_window, hot_start,
+                         capacity=None):
+    """tiered_inputs with the int8 cold tier laid out contiguously instead of in pages:
+    cold K/V int8 [hkv, capacity, d] and scales float32 [hkv, capacity]; rows past cold_len
+    hold int8 -128 with scale NaN (capacity defaults to cold_len + 16)."""
+    t = tiered_inputs(seed_c, h, hkv, d, cold_len, hot_len, hot_window, hot_start, n_poison=1)
+    c = t["cold"]
+    cap = cold_len + 16 if capacity is None else capacity
+    out = {}
+    for name, qq, ss in (("k", c["k_q"][0], c["k_s"][0]), ("v", c["v_q"][0], c["v_s"][0])):
+        a = np.full((hkv, cap, d), -128, np.int8)
+        sc = np.full((hkv, cap), np.nan, np.float32)
+        a[:, :cold_len] = np.transpose(qq, (1, 0, 2))
+        sc[:, :cold_len] = ss.T
+        out[name], out[name + "_s"] = a, sc
+    t["packed_k"], t["packed_v"] = out["k"], out["v"]
+    t["packed_k_scales"], t["packed_v_scales"] = out["k_s"], out["v_s"]
+    return t
+
+
 TID_POS = 9
 
 

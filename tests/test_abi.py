@@ -293,3 +293,40 @@ def block_local(**kw):
 def test_block_local_validation(kw, code, msg):
     assert block_local(**kw) == code
     assert msg in ta.attn_last_error()
+
+
+def tiered_f16(**kw):
+    a = dict(q=P, hk=P, hv=P, ck=P, cv=P, pt=P, o=P, H=8, Hkv=2, D=128, cold=100, hot=10, R=16, hs=0,
+             layout=2, cap_rows=112, ps=16, npages=20, W=0, cap=0.0, scale=0.088, ws=P, wsb=1 << 30)
+    a.update(kw)
+    return ta.lib().attn_decode_tiered_f16(a["q"], a["hk"], a["hv"], a["ck"], a["cv"], a["pt"], a["o"], a["H"],
+                                           a["Hkv"], a["D"], a["cold"], a["hot"], a["R"], a["hs"], a["layout"],
+                                           a["cap_rows"], a["ps"], a["npages"], a["W"], a["cap"], a["scale"],
+                                           a["ws"], a["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,code,msg", [
+    (dict(layout=1), ta.ATTN_ERR_INVALID_ARG, "cold_layout 1"),
+    (dict(layout=0), ta.ATTN_ERR_INVALID_ARG, "takes no page table"),
+    (dict(layout=0, pt=None, cap_rows=99), ta.ATTN_ERR_INVALID_ARG, "cold_capacity 99 is smaller"),
+    (dict(cap_rows=100), ta.ATTN_ERR_INVALID_ARG, "multiple of 16"),
+    (dict(cap_rows=96), ta.ATTN_ERR_INVALID_ARG, "exceeds max_pages * page_size"),
+    (dict(pt=None), ta.ATTN_ERR_INVALID_ARG, "cold_page_table must not be null"),
+    (dict(ps=32), ta.ATTN_ERR_UNSUPPORTED, "page_size 32"),
+    (dict(ck=None), ta.ATTN_ERR_INVALID_ARG, "cold_k_pages must not be null"),
+    (dict(hot=20), ta.ATTN_ERR_INVALID_ARG, "hot_len 20 exceeds hot_window 16"),
+    (dict(ws=None), ta.ATTN_ERR_WORKSPACE, "workspace must not be null"),
+])
+def test_tiered_f16_validation(kw, code, msg):
+    assert tiered_f16(**kw) == code
+    assert msg in ta.attn_last_error()
+
+
+def test_tiered_q8_packed_validation():
+    L = ta.lib()
+    rc = L.attn_decode_tiered_q8_packed(P, P, P, P, P, P, P, P, 8, 2, 128, 100, 10, 16, 0, 99, 0, 0.0, 0.088,
+                                        P, 1 << 30, None)
+    assert rc == ta.ATTN_ERR_INVALID_ARG and "cold_capacity 99 is smaller than cold_len 100" in ta.attn_last_error()
+    rc = L.attn_decode_tiered_q8_packed(P, P, P, P, P, None, P, P, 8, 2, 128, 100, 10, 16, 0, 128, 0, 0.0, 0.088,
+                                        P, 1 << 30, None)
+    assert rc == ta.ATTN_ERR_INVALID_ARG and "cold_k_scales must not be null" in ta.attn_last_error()

@@ -15,7 +15,8 @@ import os
 __all__ = [
     "AttnError", "lib", "attn_prefill", "attn_prefill_device_kv_len", "attn_vision", "attn_decode",
     "attn_decode_noalloc", "attn_decode_ring", "attn_decode_paged_q8", "attn_decode_tiered_q8",
-    "attn_block_local",
+    "attn_block_local", "attn_decode_tiered_q8_packed", "attn_decode_tiered_f16",
+    "ATTN_COLD_CONTIGUOUS", "ATTN_COLD_PAGED",
     "attn_decode_workspace_bytes", "attn_set_decode_split", "attn_last_error", "decode_workspace",
     "ATTN_OK", "ATTN_ERR_INVALID_ARG", "ATTN_ERR_UNSUPPORTED", "ATTN_ERR_WORKSPACE",
     "ATTN_ERR_LAUNCH", "ATTN_F32", "ATTN_F16", "LIB_PATH",
@@ -23,6 +24,7 @@ __all__ = [
 
 ATTN_OK, ATTN_ERR_INVALID_ARG, ATTN_ERR_UNSUPPORTED, ATTN_ERR_WORKSPACE, ATTN_ERR_LAUNCH = 0, -1, -2, -3, -4
 ATTN_F32, ATTN_F16 = 0, 1
+ATTN_COLD_CONTIGUOUS, ATTN_COLD_PAGED = 0, 2
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libattn.so")
 _lib = None
@@ -53,6 +55,8 @@ def lib() -> ctypes.CDLL:
                                            f, f, vp, sz, vp]
         L.attn_decode_tiered_q8.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i,
                                             i, i, i, f, f, vp, sz, vp]
+        L.attn_decode_tiered_q8_packed.argtypes = [vp] * 8 + [i] * 9 + [f, f, vp, sz, vp]
+        L.attn_decode_tiered_f16.argtypes = [vp] * 7 + [i] * 12 + [f, f, vp, sz, vp]
         L.attn_block_local.argtypes = [vp, vp, vp, vp, vp] + [i] * 11 + [f, vp]
         L.attn_decode_workspace_bytes.argtypes = [i, i, i, i, i]
         L.attn_decode_workspace_bytes.restype = sz
@@ -60,7 +64,8 @@ def lib() -> ctypes.CDLL:
         L.attn_last_error.argtypes = []
         L.attn_last_error.restype = ctypes.c_char_p
         for name in ("attn_prefill", "attn_prefill_device_kv_len", "attn_vision", "attn_decode",
-                     "attn_decode_noalloc", "attn_decode_ring", "attn_block_local", "attn_decode_paged_q8", "attn_decode_tiered_q8",
+                     "attn_decode_noalloc", "attn_decode_ring", "attn_block_local",
+                     "attn_decode_tiered_q8_packed", "attn_decode_tiered_f16", "attn_decode_paged_q8", "attn_decode_tiered_q8",
                      "attn_set_decode_split"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
@@ -304,6 +309,66 @@ def attn_decode_tiered_q8(q, hot_k, hot_v, cold_k_pages, cold_v_pages, cold_k_sc
         int(sliding_window), float(attn_softcap), float(scale), _ptr(workspace), ws_bytes,
         _stream(q, stream)))
 
+
+
+def attn_decode_tiered_q8_packed(q, hot_k, hot_v, cold_k, cold_v, cold_k_scales, cold_v_scales, o,
+                                 workspace, *, cold_len: int, hot_len: int, hot_start: int,
+                                 scale: float, sliding_window: int = 0, attn_softcap: float = 0.0,
+                                 stream=None):
+    """As attn_decode_tiered_q8 with a contiguous int8 cold tier: cold_k, cold_v int8
+    [num_kv_heads, cold_capacity, head_dim], scales float32 [num_kv_heads, cold_capacity]."""
+    _need("attn_decode_tiered_q8_packed", q=(q, "float32"), hot_k=(hot_k, "float16"),
+          hot_v=(hot_v, "float16"), cold_k=(cold_k, "int8"), cold_v=(cold_v, "int8"),
+          cold_k_scales=(cold_k_scales, "float32"), cold_v_scales=(cold_v_scales, "float32"),
+          o=(o, "float32"), workspace=(workspace, "uint8"))
+    _need_contig(q, hot_k, hot_v, cold_k, cold_v, cold_k_scales, cold_v_scales, o)
+    H, D = q.shape
+    Hkv, R, Dk = hot_k.shape
+    Hc, C, Dc = cold_k.shape
+    if Dk != D or Dc != D or Hc != Hkv or hot_v.shape != hot_k.shape or o.shape != q.shape or \
+            cold_v.shape != cold_k.shape or cold_k_scales.shape != (Hkv, C) or \
+            cold_v_scales.shape != (Hkv, C):
+        raise ValueError("shape mismatch")
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(lib().attn_decode_tiered_q8_packed(
+        _ptr(q), _ptr(hot_k), _ptr(hot_v), _ptr(cold_k), _ptr(cold_v), _ptr(cold_k_scales),
+        _ptr(cold_v_scales), _ptr(o), H, Hkv, D, int(cold_len), int(hot_len), R, int(hot_start), C,
+        int(sliding_window), float(attn_softcap), float(scale), _ptr(workspace), ws_bytes,
+        _stream(q, stream)))
+
+
+def attn_decode_tiered_f16(q, hot_k, hot_v, cold_k, cold_v, cold_page_table, o, workspace, *,
+                           cold_len: int, hot_len: int, hot_start: int, scale: float,
+                           sliding_window: int = 0, attn_softcap: float = 0.0, stream=None):
+    """Tiered decode with an f16 cold tier.  Paged when cold_page_table is given: cold_k,
+    cold_v float16 [num_pages, num_kv_heads, 16, head_dim], page table int32 [max_pages];
+    contiguous when it is None: cold_k, cold_v float16 [num_kv_heads, cold_capacity, head_dim]."""
+    _need("attn_decode_tiered_f16", q=(q, "float32"), hot_k=(hot_k, "float16"),
+          hot_v=(hot_v, "float16"), cold_k=(cold_k, "float16"), cold_v=(cold_v, "float16"),
+          cold_page_table=(cold_page_table, "int32"), o=(o, "float32"),
+          workspace=(workspace, "uint8"))
+    _need_contig(q, hot_k, hot_v, cold_k, cold_v, o)
+    H, D = q.shape
+    Hkv, R, Dk = hot_k.shape
+    if Dk != D or hot_v.shape != hot_k.shape or o.shape != q.shape or cold_v.shape != cold_k.shape:
+        raise ValueError("shape mismatch")
+    if cold_page_table is not None:
+        _need_contig(cold_page_table)
+        P, Hc, ps, Dc = cold_k.shape
+        if Hc != Hkv or Dc != D or cold_page_table.dim() != 1:
+            raise ValueError("paged cold tier: pages [P, Hkv, 16, D], table [max_pages]")
+        layout, cap, npages = ATTN_COLD_PAGED, cold_page_table.shape[0] * ps, P
+    else:
+        Hc, C, Dc = cold_k.shape
+        if Hc != Hkv or Dc != D:
+            raise ValueError("contiguous cold tier: [Hkv, cold_capacity, D]")
+        layout, cap, ps, npages = ATTN_COLD_CONTIGUOUS, C, 0, 0
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(lib().attn_decode_tiered_f16(
+        _ptr(q), _ptr(hot_k), _ptr(hot_v), _ptr(cold_k), _ptr(cold_v), _ptr(cold_page_table),
+        _ptr(o), H, Hkv, D, int(cold_len), int(hot_len), R, int(hot_start), layout, cap, ps, npages,
+        int(sliding_window), float(attn_softcap), float(scale), _ptr(workspace), ws_bytes,
+        _stream(q, stream)))
 
 
 def attn_block_local(q_pad, k_padded, v_padded, pos_proj, attn_out, *, seq: int, chunk_size: int,

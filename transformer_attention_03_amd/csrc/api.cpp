@@ -474,13 +474,28 @@ int attn_decode_paged_q8(const float* q, const int8_t* k_pages, const int8_t* v_
                          "attn_decode_paged_q8");
 }
 
-int attn_decode_tiered_q8(const float* q, const void* hot_k, const void* hot_v, const int8_t* cold_k_pages,
-                          const int8_t* cold_v_pages, const float* cold_k_scales, const float* cold_v_scales,
-                          const int32_t* cold_page_table, float* o, int num_heads, int num_kv_heads, int head_dim,
-                          int cold_len, int hot_len, int hot_window, int hot_start, int page_size, int num_pages,
-                          int max_pages, int sliding_window, float attn_softcap, float scale, void* workspace,
-                          size_t workspace_bytes, void* stream) {
-    const char* what = "attn_decode_tiered_q8";
+}  // extern "C"
+
+namespace {
+
+// Tiered decode of one sequence (shared by the three tiered entry points): an f16 ring hot
+// tier and a cold tier that is int8 (per-row scales) or f16, paged (16-token pages through
+// cold_page_table) or contiguous per KV head (cold_stride rows).
+struct ColdTier {
+    const void* k;
+    const void* v;
+    const float* ks;              // int8 only
+    const float* vs;
+    const int32_t* page_table;    // paged only
+    bool int8, paged;
+    int page_size, num_pages, max_pages;   // paged
+    int stride;                   // contiguous: rows per KV head
+};
+
+int run_tiered(const char* what, const float* q, const void* hot_k, const void* hot_v, const ColdTier& ct,
+               float* o, int num_heads, int num_kv_heads, int head_dim, int cold_len, int hot_len, int hot_window,
+               int hot_start, int sliding_window, float attn_softcap, float scale, void* workspace,
+               size_t workspace_bytes, void* stream) {
     TRY(check_ptr(q, "q"));
     TRY(check_ptr(o, "o"));
     TRY(check_heads(num_heads, num_kv_heads, head_dim));
@@ -501,48 +516,60 @@ int attn_decode_tiered_q8(const float* q, const void* hot_k, const void* hot_v, 
             return fail(ATTN_ERR_INVALID_ARG, "%s: hot tier too large", what);
     }
     if (cold_len > 0) {
-        TRY(check_ptr(cold_k_pages, "cold_k_pages"));
-        TRY(check_ptr(cold_v_pages, "cold_v_pages"));
-        TRY(check_ptr(cold_k_scales, "cold_k_scales"));
-        TRY(check_ptr(cold_v_scales, "cold_v_scales"));
-        TRY(check_ptr(cold_page_table, "cold_page_table"));
-        if (page_size != 16)
-            return fail(ATTN_ERR_UNSUPPORTED, "%s: page_size %d is not built; requires page_size 16", what, page_size);
-        if (num_pages < 1 || max_pages < 1)
-            return fail(ATTN_ERR_INVALID_ARG, "%s: num_pages and max_pages must be >= 1", what);
-        if ((long)max_pages * page_size < cold_len)
-            return fail(ATTN_ERR_INVALID_ARG, "%s: cold_len %d exceeds max_pages * page_size = %ld", what, cold_len,
-                        (long)max_pages * page_size);
-        if ((long)num_pages * page_size * num_kv_heads * head_dim > kMaxElems)
-            return fail(ATTN_ERR_INVALID_ARG, "%s: cold tier too large", what);
+        TRY(check_ptr(ct.k, ct.paged ? "cold_k_pages" : "cold_k"));
+        TRY(check_ptr(ct.v, ct.paged ? "cold_v_pages" : "cold_v"));
+        if (ct.int8) {
+            TRY(check_ptr(ct.ks, "cold_k_scales"));
+            TRY(check_ptr(ct.vs, "cold_v_scales"));
+        }
+        if (ct.paged) {
+            TRY(check_ptr(ct.page_table, "cold_page_table"));
+            if (ct.page_size != 16)
+                return fail(ATTN_ERR_UNSUPPORTED, "%s: page_size %d is not built; requires page_size 16", what,
+                            ct.page_size);
+            if (ct.num_pages < 1 || ct.max_pages < 1)
+                return fail(ATTN_ERR_INVALID_ARG, "%s: num_pages and max_pages must be >= 1", what);
+            if ((long)ct.max_pages * ct.page_size < cold_len)
+                return fail(ATTN_ERR_INVALID_ARG, "%s: cold_len %d exceeds max_pages * page_size = %ld", what, cold_len,
+                            (long)ct.max_pages * ct.page_size);
+            if ((long)ct.num_pages * ct.page_size * num_kv_heads * head_dim > kMaxElems)
+                return fail(ATTN_ERR_INVALID_ARG, "%s: cold tier too large", what);
+        } else {
+            if (ct.stride < cold_len)
+                return fail(ATTN_ERR_INVALID_ARG, "%s: cold_capacity %d is smaller than cold_len %d", what, ct.stride,
+                            cold_len);
+            if ((long)ct.stride * num_kv_heads * head_dim > kMaxElems)
+                return fail(ATTN_ERR_INVALID_ARG, "%s: cold tier too large", what);
+        }
     }
     const int total = cold_len + hot_len;
     const int k_lo = (sliding_window > 0 && total > sliding_window) ? total - sliding_window : 0;
     const int cold_vis = cold_len > k_lo ? cold_len - k_lo : 0;
     const int hot_vis = total - (k_lo > cold_len ? k_lo : cold_len);
-    // One split size for both tiers: about one round of resident workgroups (the kernel's
-    // LDS is sized for the f16 body, the larger one), in whole rounds of 16-token blocks per
-    // wave, at most the paged page-slice limit; the thread's split override wins.  The split
-    // count must fit the workspace row that attn_decode_workspace_bytes(1, ...,
-    // cold_len + hot_len) sized.
+    // One split size per tier: about one round of resident workgroups (the kernel's LDS is
+    // sized for the larger body), in whole rounds of 16-token blocks per wave, at most the
+    // paged page-slice limit; the thread's split override wins.  The split count must fit
+    // the workspace row that attn_decode_workspace_bytes(1, ..., cold_len + hot_len) sized.
     DecodePlan plan = plan_decode(1, num_heads, num_kv_heads, head_dim, cold_vis + hot_vis, false);
     const int stride = workspace_row_splits(1, num_heads, num_kv_heads, head_dim, total);
     const int max_split = ta03::decode_max_split_tokens_paged();
-    // Split lengths in tokens, cold (tc) and hot (th): equal bytes per split, since a cold
-    // token carries 2D + 8 bytes (int8 K and V rows and their scales) and a hot one 4D (f16
-    // rows); the thread's split override sets both.
+    // Split lengths in tokens, cold (tc) and hot (th): equal bytes per split (a cold token
+    // carries 2D + 8 bytes in int8 with its scales, 4D in f16; a hot one 4D).
+    const long cold_tok_bytes = ct.int8 ? 2L * head_dim + 8 : 4L * head_dim;
     int tc = g_split_override, th = g_split_override;
     if (tc <= 0) {
         int per_cu = ta03::decode_workgroups_per_cu(head_dim, false);
-        const int per_cu_paged = ta03::decode_workgroups_per_cu(head_dim, true);
-        if (per_cu_paged < per_cu) per_cu = per_cu_paged;
+        if (ct.int8) {
+            const int per_cu_paged = ta03::decode_workgroups_per_cu(head_dim, true);
+            if (per_cu_paged < per_cu) per_cu = per_cu_paged;
+        }
         const long chunks = (long)num_kv_heads * plan.nch;
         const long n_target = (256L * per_cu + chunks - 1) / chunks;
         const int unit = ta03::decode_waves(head_dim, true) * ta03::decode_tokens_per_block();
-        const long cold_b = (long)cold_vis * (2 * head_dim + 8), hot_b = (long)hot_vis * 4 * head_dim;
+        const long cold_b = (long)cold_vis * cold_tok_bytes, hot_b = (long)hot_vis * 4 * head_dim;
         const long per_b = (cold_b + hot_b + n_target - 1) / n_target;
         auto whole_rounds = [&](long t) { return (int)((((t < 1 ? 1 : t) + unit - 1) / unit) * unit); };
-        tc = whole_rounds(per_b / (2 * head_dim + 8));
+        tc = whole_rounds(per_b / cold_tok_bytes);
         th = whole_rounds(per_b / (4 * head_dim));
     }
     if (tc > max_split) tc = max_split;
@@ -565,9 +592,9 @@ int attn_decode_tiered_q8(const float* q, const void* hot_k, const void* hot_v, 
     if ((long)num_kv_heads * plan.nch > 65535) return fail(ATTN_ERR_INVALID_ARG, "%s: grid too large", what);
     ta03::DecodeParams d{};
     d.q = q;
-    d.k = cold_k_pages; d.v = cold_v_pages;
-    d.k_scales = cold_k_scales; d.v_scales = cold_v_scales;
-    d.page_table = cold_page_table; d.o = o;
+    d.k = ct.k; d.v = ct.v;
+    d.k_scales = ct.ks; d.v_scales = ct.vs;
+    d.page_table = ct.page_table; d.o = o;
     char* ws = reinterpret_cast<char*>(workspace);
     d.part_o = reinterpret_cast<float*>(ws + wl.o_off);
     d.part_m = reinterpret_cast<float*>(ws + wl.m_off);
@@ -576,7 +603,8 @@ int attn_decode_tiered_q8(const float* q, const void* hot_k, const void* hot_v, 
     d.H = num_heads; d.Hkv = num_kv_heads;
     d.kv_len = total;
     d.ring = hot_len > 0 ? hot_window : 1;
-    d.num_pages = num_pages; d.max_pages = max_pages;
+    d.num_pages = ct.paged ? ct.num_pages : 0;
+    d.max_pages = ct.paged ? ct.max_pages : 0;
     fill_scalars(d, sliding_window, attn_softcap, scale);
     d.split_tokens = th;
     d.n_split_max = stride;
@@ -588,9 +616,60 @@ int attn_decode_tiered_q8(const float* q, const void* hot_k, const void* hot_v, 
     d.tier_cold_splits = (cold_vis + tc - 1) / tc;
     d.tier_k_lo = k_lo;
     d.tier_cold_tokens = tc;
-    return launch_status(ta03::launch_decode_tiered(d, head_dim, plan.gc, splits(),
+    d.tier_cold_stride = ct.paged ? 0 : ct.stride;
+    return launch_status(ta03::launch_decode_tiered(d, head_dim, plan.gc, splits(), ct.int8, ct.paged,
                                                     reinterpret_cast<hipStream_t>(stream)),
                          what);
+}
+
+}  // namespace
+
+extern "C" {
+
+int attn_decode_tiered_q8(const float* q, const void* hot_k, const void* hot_v, const int8_t* cold_k_pages,
+                          const int8_t* cold_v_pages, const float* cold_k_scales, const float* cold_v_scales,
+                          const int32_t* cold_page_table, float* o, int num_heads, int num_kv_heads, int head_dim,
+                          int cold_len, int hot_len, int hot_window, int hot_start, int page_size, int num_pages,
+                          int max_pages, int sliding_window, float attn_softcap, float scale, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+    ColdTier ct{cold_k_pages, cold_v_pages, cold_k_scales, cold_v_scales, cold_page_table, true, true,
+                page_size, num_pages, max_pages, 0};
+    return run_tiered("attn_decode_tiered_q8", q, hot_k, hot_v, ct, o, num_heads, num_kv_heads, head_dim, cold_len,
+                      hot_len, hot_window, hot_start, sliding_window, attn_softcap, scale, workspace, workspace_bytes,
+                      stream);
+}
+
+int attn_decode_tiered_q8_packed(const float* q, const void* hot_k, const void* hot_v, const int8_t* cold_k,
+                                 const int8_t* cold_v, const float* cold_k_scales, const float* cold_v_scales,
+                                 float* o, int num_heads, int num_kv_heads, int head_dim, int cold_len, int hot_len,
+                                 int hot_window, int hot_start, int cold_capacity, int sliding_window,
+                                 float attn_softcap, float scale, void* workspace, size_t workspace_bytes,
+                                 void* stream) {
+    ColdTier ct{cold_k, cold_v, cold_k_scales, cold_v_scales, nullptr, true, false, 0, 0, 0, cold_capacity};
+    return run_tiered("attn_decode_tiered_q8_packed", q, hot_k, hot_v, ct, o, num_heads, num_kv_heads, head_dim,
+                      cold_len, hot_len, hot_window, hot_start, sliding_window, attn_softcap, scale, workspace,
+                      workspace_bytes, stream);
+}
+
+int attn_decode_tiered_f16(const float* q, const void* hot_k, const void* hot_v, const void* cold_k,
+                           const void* cold_v, const int32_t* cold_page_table, float* o, int num_heads,
+                           int num_kv_heads, int head_dim, int cold_len, int hot_len, int hot_window, int hot_start,
+                           int cold_layout, int cold_capacity, int page_size, int num_pages, int sliding_window,
+                           float attn_softcap, float scale, void* workspace, size_t workspace_bytes, void* stream) {
+    const char* what = "attn_decode_tiered_f16";
+    if (cold_layout != ATTN_COLD_CONTIGUOUS && cold_layout != ATTN_COLD_PAGED)
+        return fail(ATTN_ERR_INVALID_ARG, "%s: cold_layout %d is neither ATTN_COLD_CONTIGUOUS (0) nor ATTN_COLD_PAGED (2)",
+                    what, cold_layout);
+    const bool paged = cold_layout == ATTN_COLD_PAGED;
+    if (paged && cold_capacity % 16 != 0)
+        return fail(ATTN_ERR_INVALID_ARG, "%s: a paged cold tier needs cold_capacity (%d) a multiple of 16", what,
+                    cold_capacity);
+    if (!paged && cold_page_table != nullptr)
+        return fail(ATTN_ERR_INVALID_ARG, "%s: a contiguous cold tier takes no page table", what);
+    ColdTier ct{cold_k, cold_v, nullptr, nullptr, cold_page_table, false, paged, page_size, num_pages,
+                paged ? cold_capacity / 16 : 0, cold_capacity};
+    return run_tiered(what, q, hot_k, hot_v, ct, o, num_heads, num_kv_heads, head_dim, cold_len, hot_len, hot_window,
+                      hot_start, sliding_window, attn_softcap, scale, workspace, workspace_bytes, stream);
 }
 
 int attn_block_local(const float* q_pad, const float* k_padded, const float* v_padded, const float* pos_proj,

@@ -163,10 +163,15 @@ struct RowCtx {
     const float* vscales;
     const int* pages;      // paged: physical pages of this split, from logical page page0
     int page0;
-    int Hkv, kvh, kv_len;
+    int Hkv, kvh;
+    int stride;            // contiguous: rows per KV head
     int ring, ring_base;   // ring: capacity R, and a multiple of R at or below the split's
                            // first token (the split spans at most R tokens)
 };
+
+// Row addressing of a cache (or tier): contiguous [Hkv][stride][D], a ring [Hkv][R][D], or
+// 16-token pages [P][Hkv][16][D] through a page table.
+constexpr int kAddrContig = 0, kAddrRing = 1, kAddrPaged = 2;
 
 // Ring slot of token t (t - ring_base lies in [0, 2R)).
 __device__ __forceinline__ int ring_slot(const RowCtx& c, int t) {
@@ -175,15 +180,15 @@ __device__ __forceinline__ int ring_slot(const RowCtx& c, int t) {
 }
 
 // Row index (token t of this KV head) in rows of D elements.
-template <bool PAGED, bool RING>
+template <int ADDR>
 __device__ __forceinline__ size_t row_index(const RowCtx& c, int t) {
-    if constexpr (PAGED) {
+    if constexpr (ADDR == kAddrPaged) {
         const int pg = c.pages[(t >> 4) - c.page0];
         return ((size_t)pg * c.Hkv + c.kvh) * 16 + (t & 15);
-    } else if constexpr (RING) {
+    } else if constexpr (ADDR == kAddrRing) {
         return (size_t)c.kvh * c.ring + ring_slot(c, t);
     } else {
-        return (size_t)c.kvh * c.kv_len + t;
+        return (size_t)c.kvh * c.stride + t;
     }
 }
 
@@ -235,25 +240,26 @@ __device__ __forceinline__ DmaLane<D, PAGED> dma_lane(int lane, uint32_t rs) {
 }
 
 // DMA the block of tokens tb .. tb+15 into a ring slot (row r of a tile = token tb + r,
-// swizzled chunks; scale areas: row r at 4r).  A full block (and,
-// paged, one whose 16 tokens share a page; ring, one that does not wrap) takes the
-// uniform-base path; otherwise every lane resolves its own row, and tokens at or past t_end
-// fetch the row of token t_end - 1.
-template <int D, bool PAGED, bool RING>
+// swizzled chunks; int8: scale areas, row r at 4r).  A full block (and, paged, one whose 16
+// tokens share a page; ring, one that does not wrap) takes the uniform-base path; otherwise
+// every lane resolves its own row, and tokens at or past t_end fetch the row of token
+// t_end - 1.  PAGED is the int8 format (with scales); ADDR the row addressing.
+template <int D, bool PAGED, int ADDR>
 __device__ __forceinline__ void dma_block(char* slot, const RowCtx& c, const DmaLane<D, PAGED>& L,
                                           int tb, int t_end, int lane) {
     using S = DecShape<D, PAGED>;
+    constexpr bool RING = ADDR == kAddrRing;
     const int slot0 = RING ? ring_slot(c, tb) : 0;
-    const bool full = tb + kTB <= t_end && (!PAGED || (tb & 15) == 0) && (!RING || slot0 + kTB <= c.ring);
+    const bool full = tb + kTB <= t_end && (ADDR != kAddrPaged || (tb & 15) == 0) && (!RING || slot0 + kTB <= c.ring);
     if (full) {
         size_t row0;
-        if constexpr (PAGED) {
+        if constexpr (ADDR == kAddrPaged) {
             const int pg = __builtin_amdgcn_readfirstlane(c.pages[(tb >> 4) - c.page0]);
             row0 = ((size_t)pg * c.Hkv + c.kvh) * 16;
         } else if constexpr (RING) {
             row0 = (size_t)c.kvh * c.ring + slot0;
         } else {
-            row0 = (size_t)c.kvh * c.kv_len + tb;
+            row0 = (size_t)c.kvh * c.stride + tb;
         }
         const char* kb = c.kbase + row0 * S::RB;
         const char* vb = c.vbase + row0 * S::RB;
@@ -274,14 +280,14 @@ __device__ __forceinline__ void dma_block(char* slot, const RowCtx& c, const Dma
         for (int i = 0; i < S::TD; ++i) {
             const int p = 1024 * i + 16 * lane;
             const int r = p / S::RB, cpos = (p % S::RB) / 16;
-            const size_t ri = row_index<PAGED, RING>(c, min(tb + r, t_end - 1));
+            const size_t ri = row_index<ADDR>(c, min(tb + r, t_end - 1));
             dma16(c.kbase + ri * S::RB + 16 * (cpos ^ ksw<S::RPL>(r)), slot + 1024 * i);
             dma16(c.vbase + ri * S::RB + 16 * (cpos ^ vsw<S::RPL>(r)), slot + S::TILE + 1024 * i);
         }
         if constexpr (PAGED) {
             if (lane < 16) {
                 // a token's scale has the index of its row
-                const size_t si = row_index<PAGED, RING>(c, min(tb + lane, t_end - 1));
+                const size_t si = row_index<ADDR>(c, min(tb + lane, t_end - 1));
                 dma4(c.kscales + si, slot + 2 * S::TILE);
                 dma4(c.vscales + si, slot + 2 * S::TILE + 256);
             }
@@ -465,14 +471,16 @@ __device__ __forceinline__ void process_block(const char* slot, int tb, int t_en
     }
 }
 
-// Where a split's K/V rows come from: the cache (or tier) pointers, and for a ring its
-// capacity and index offset (position t lives at row (t + ring_off) mod ring).
+// Where a split's K/V rows come from: the cache (or tier) pointers, for a ring its capacity
+// and index offset (position t lives at row (t + ring_off) mod ring), for a contiguous
+// cache its rows per KV head.
 struct TierSrc {
     const void* k;
     const void* v;
     const float* ks;
     const float* vs;
     int ring, ring_off;
+    int stride;
 };
 
 // 16-byte entries per query chunk in the caller's qx buffer: the f16 bodies stage the f32
@@ -484,7 +492,7 @@ constexpr int qx_entries() { return PAGED ? 64 : 128; }
 // waves, and either write the output (a single split) or publish the split's partial
 // (m, l, o) for the last-arriving workgroup.  LDS is the caller's, so that one kernel can
 // host splits of two cache layouts.
-template <int D, int GC, bool PAGED, bool CAP, bool RING>
+template <int D, int GC, bool PAGED, bool CAP, int ADDR>
 __device__ __forceinline__ void split_partial(const DecodeParams& a, const TierSrc& src, char* rings,
                                               float (*lds_m)[GC], float (*lds_l)[GC], int* lds_pages,
                                               half8_t* lds_qx, float (*lds_qs)[64], int b,
@@ -507,10 +515,11 @@ __device__ __forceinline__ void split_partial(const DecodeParams& a, const TierS
     c.page0 = t_begin >> 4;
     c.Hkv = a.Hkv;
     c.kvh = kvh;
-    c.kv_len = a.kv_len;
+    c.stride = src.stride;
+    constexpr bool RING = ADDR == kAddrRing;
     c.ring = RING ? src.ring : 0;
     c.ring_base = RING ? ((t_begin + src.ring_off) / src.ring) * src.ring - src.ring_off : 0;
-    if constexpr (PAGED) {
+    if constexpr (ADDR == kAddrPaged) {
         // the physical pages of this split, fetched once (clamped into range)
         const int32_t* ptab = a.page_table + (size_t)b * a.max_pages;
         const int np = ((t_end - 1) >> 4) - c.page0 + 1;
@@ -538,7 +547,7 @@ __device__ __forceinline__ void split_partial(const DecodeParams& a, const TierS
         }
 #pragma unroll
     for (int k = 0; k < S::RING; ++k)
-        if (k < nb) dma_block<D, PAGED, RING>(ring + k * S::SLOT, c, dl, first + k * STRIDE, t_end, lane);
+        if (k < nb) dma_block<D, PAGED, ADDR>(ring + k * S::SLOT, c, dl, first + k * STRIDE, t_end, lane);
 
     // ---- Qx: B operand of the QK product.  Column n = lane % 16 holds part n & 1 of head
     // n / 2 (hi, lo); k = d = 32 kc + 8 (lane / 16) + e, with e in the element order of the
@@ -617,7 +626,7 @@ __device__ __forceinline__ void split_partial(const DecodeParams& a, const TierS
         if (kn < nb) {
             // the slot of block k is refilled once this wave's reads of it are done
             wait_lds_reads();
-            dma_block<D, PAGED, RING>(ring + (k % S::RING) * S::SLOT, c, dl, first + kn * STRIDE, t_end, lane);
+            dma_block<D, PAGED, ADDR>(ring + (k % S::RING) * S::SLOT, c, dl, first + kn * STRIDE, t_end, lane);
         }
     }
 
@@ -873,36 +882,44 @@ __global__ void __launch_bounds__((DecShape<D, PAGED>::NT)) decode_split_kernel(
         t_end = min(L, t_begin + a.split_tokens);
     }
 
-    const TierSrc src{a.k, a.v, a.k_scales, a.v_scales, RING ? a.ring : 0, 0};
-    split_partial<D, GC, PAGED, CAP, RING>(a, src, rings, lds_m, lds_l, lds_pages, &lds_qx[0][0], lds_qs, b, split,
+    const TierSrc src{a.k, a.v, a.k_scales, a.v_scales, RING ? a.ring : 0, 0, a.kv_len};
+    constexpr int ADDR = PAGED ? kAddrPaged : (RING ? kAddrRing : kAddrContig);
+    split_partial<D, GC, PAGED, CAP, ADDR>(a, src, rings, lds_m, lds_l, lds_pages, &lds_qx[0][0], lds_qs, b, split,
                                            n_live, t_begin, t_end, kvh, h0);
     if (n_live == 1) return;
     merge_splits<D, GC, NT, merge_chunk<D, GC, PAGED>()>(a, rings, &lds_last, b, h0, n_live);
 }
 
-// Tiered decode of one sequence: positions [0, cold_len) sit in an int8 paged cold tier,
-// positions [cold_len, kv_len) in an f16 ring (the hot tier).  Workgroups [0, n_cold) take
-// splits of the cold tier with the int8 body, the rest splits of the hot tier with the f16
-// ring body; all of them publish partials of one online softmax and the last to arrive
-// merges them, exactly as for a single-layout cache.  LDS is sized for the larger body.
-template <int D, int GC, bool CAP>
+// Tiered decode of one sequence: positions [0, cold_len) sit in a cold tier, positions
+// [cold_len, kv_len) in an f16 ring (the hot tier).  The cold tier is int8 with per-row
+// scales or f16, either in 16-token pages through a page table or contiguous per KV head
+// (COLD, one of the kCold* kinds).  Workgroups [0, n_cold) take splits of the cold tier,
+// the rest splits of the hot tier with the f16 ring body; all of them publish partials of
+// one online softmax and the last to arrive merges them, exactly as for a single-layout
+// cache.  LDS is sized for the larger of the two bodies.
+constexpr int kColdI8Paged = 0, kColdI8Contig = 1, kColdF16Paged = 2, kColdF16Contig = 3;
+
+template <int D, int COLD>
 constexpr int tier_ring_bytes() {
     using SP = DecShape<D, true>;
     using SF = DecShape<D, false>;
-    return SP::NW * SP::WAVE_LDS > SF::NW * SF::WAVE_LDS ? SP::NW * SP::WAVE_LDS : SF::NW * SF::WAVE_LDS;
+    constexpr int p = SP::NW * SP::WAVE_LDS, f = SF::NW * SF::WAVE_LDS;
+    return (COLD == kColdI8Paged || COLD == kColdI8Contig) && p > f ? p : f;
 }
 
-template <int D, int GC, bool CAP>
+template <int D, int GC, int COLD, bool CAP>
 __global__ void __launch_bounds__((DecShape<D, true>::NT)) decode_tiered_kernel(DecodeParams a) {
     using SP = DecShape<D, true>;
     using SF = DecShape<D, false>;
     static_assert(SP::NT == SF::NT && SP::NW == SF::NW, "one block shape for both tiers");
+    constexpr bool COLD_I8 = COLD == kColdI8Paged || COLD == kColdI8Contig;
+    constexpr int COLD_ADDR = (COLD == kColdI8Paged || COLD == kColdF16Paged) ? kAddrPaged : kAddrContig;
     constexpr int NT = SP::NT;
-    constexpr int RB = tier_ring_bytes<D, GC, CAP>();
+    constexpr int RB = tier_ring_bytes<D, COLD>();
     __shared__ __attribute__((aligned(1024))) char rings[RB];
     __shared__ float lds_m[SP::NW][GC];
     __shared__ float lds_l[SP::NW][GC];
-    __shared__ int lds_pages[kMaxSplitTokens / 16 + 1];
+    __shared__ int lds_pages[COLD_ADDR == kAddrPaged ? kMaxSplitTokens / 16 + 1 : 1];
     __shared__ int lds_last;
     __shared__ __attribute__((aligned(1024))) half8_t lds_qx[SP::KC][qx_entries<false>()];   // both bodies
     __shared__ float lds_qs[SP::KC][64];
@@ -918,15 +935,15 @@ __global__ void __launch_bounds__((DecShape<D, true>::NT)) decode_tiered_kernel(
     if (split < a.tier_cold_splits) {
         const int t_begin = a.tier_k_lo + split * a.tier_cold_tokens;
         const int t_end = min(a.tier_cold_len, t_begin + a.tier_cold_tokens);
-        const TierSrc src{a.k, a.v, a.k_scales, a.v_scales, 0, 0};
-        split_partial<D, GC, true, CAP, false>(a, src, rings, lds_m, lds_l, lds_pages, &lds_qx[0][0], lds_qs, 0,
-                                               split, n_live, t_begin, t_end, kvh, h0);
+        const TierSrc src{a.k, a.v, a.k_scales, a.v_scales, 0, 0, a.tier_cold_stride};
+        split_partial<D, GC, COLD_I8, CAP, COLD_ADDR>(a, src, rings, lds_m, lds_l, lds_pages, &lds_qx[0][0], lds_qs,
+                                                      0, split, n_live, t_begin, t_end, kvh, h0);
     } else {
         const int t_begin = max(a.tier_k_lo, a.tier_cold_len) + (split - a.tier_cold_splits) * a.split_tokens;
         const int t_end = min(a.kv_len, t_begin + a.split_tokens);
-        const TierSrc src{a.hot_k, a.hot_v, nullptr, nullptr, a.ring, a.ring_off};
-        split_partial<D, GC, false, CAP, true>(a, src, rings, lds_m, lds_l, lds_pages, &lds_qx[0][0], lds_qs, 0,
-                                               split, n_live, t_begin, t_end, kvh, h0);
+        const TierSrc src{a.hot_k, a.hot_v, nullptr, nullptr, a.ring, a.ring_off, 0};
+        split_partial<D, GC, false, CAP, kAddrRing>(a, src, rings, lds_m, lds_l, lds_pages, &lds_qx[0][0], lds_qs, 0,
+                                                    split, n_live, t_begin, t_end, kvh, h0);
     }
     if (n_live == 1) return;
     merge_splits<D, GC, NT, CS>(a, rings, &lds_last, 0, h0, n_live);
@@ -982,33 +999,48 @@ hipError_t launch_decode(const DecodeParams& p, int head_dim, int gc, bool paged
 
 namespace {
 
-template <int D, bool CAP>
+template <int D, int COLD, bool CAP>
 hipError_t launch_tiered_c(const DecodeParams& p, int gc, dim3 grid, hipStream_t st) {
     const dim3 block(DecShape<D, true>::NT);
     switch (gc) {
-        case 1: hipLaunchKernelGGL((decode_tiered_kernel<D, 1, CAP>), grid, block, 0, st, p); break;
-        case 2: hipLaunchKernelGGL((decode_tiered_kernel<D, 2, CAP>), grid, block, 0, st, p); break;
-        case 4: hipLaunchKernelGGL((decode_tiered_kernel<D, 4, CAP>), grid, block, 0, st, p); break;
-        case 8: hipLaunchKernelGGL((decode_tiered_kernel<D, 8, CAP>), grid, block, 0, st, p); break;
+        case 1: hipLaunchKernelGGL((decode_tiered_kernel<D, 1, COLD, CAP>), grid, block, 0, st, p); break;
+        case 2: hipLaunchKernelGGL((decode_tiered_kernel<D, 2, COLD, CAP>), grid, block, 0, st, p); break;
+        case 4: hipLaunchKernelGGL((decode_tiered_kernel<D, 4, COLD, CAP>), grid, block, 0, st, p); break;
+        case 8: hipLaunchKernelGGL((decode_tiered_kernel<D, 8, COLD, CAP>), grid, block, 0, st, p); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
 }
 
+template <int D, int COLD>
+hipError_t launch_tiered_k(const DecodeParams& p, int gc, dim3 grid, hipStream_t st) {
+    return p.softcap > 0.f ? launch_tiered_c<D, COLD, true>(p, gc, grid, st)
+                           : launch_tiered_c<D, COLD, false>(p, gc, grid, st);
+}
+
 template <int D>
-hipError_t launch_tiered_d(const DecodeParams& p, int gc, dim3 grid, hipStream_t st) {
-    return p.softcap > 0.f ? launch_tiered_c<D, true>(p, gc, grid, st) : launch_tiered_c<D, false>(p, gc, grid, st);
+hipError_t launch_tiered_d(const DecodeParams& p, int gc, int cold_kind, dim3 grid, hipStream_t st) {
+    switch (cold_kind) {
+        case kColdI8Paged: return launch_tiered_k<D, kColdI8Paged>(p, gc, grid, st);
+        case kColdI8Contig: return launch_tiered_k<D, kColdI8Contig>(p, gc, grid, st);
+        case kColdF16Paged: return launch_tiered_k<D, kColdF16Paged>(p, gc, grid, st);
+        case kColdF16Contig: return launch_tiered_k<D, kColdF16Contig>(p, gc, grid, st);
+    }
+    return hipErrorInvalidValue;
 }
 
 }  // namespace
 
-hipError_t launch_decode_tiered(const DecodeParams& p, int head_dim, int gc, int n_splits, hipStream_t st) {
+hipError_t launch_decode_tiered(const DecodeParams& p, int head_dim, int gc, int n_splits, bool cold_int8,
+                                bool cold_paged, hipStream_t st) {
     const int nch = (p.H / p.Hkv) / gc;
     const dim3 grid(n_splits, p.Hkv * nch, 1);
+    const int kind = cold_int8 ? (cold_paged ? kColdI8Paged : kColdI8Contig)
+                               : (cold_paged ? kColdF16Paged : kColdF16Contig);
     switch (head_dim) {
-        case 64: return launch_tiered_d<64>(p, gc, grid, st);
-        case 128: return launch_tiered_d<128>(p, gc, grid, st);
-        case 256: return launch_tiered_d<256>(p, gc, grid, st);
+        case 64: return launch_tiered_d<64>(p, gc, kind, grid, st);
+        case 128: return launch_tiered_d<128>(p, gc, kind, grid, st);
+        case 256: return launch_tiered_d<256>(p, gc, kind, grid, st);
     }
     return hipErrorInvalidValue;
 }

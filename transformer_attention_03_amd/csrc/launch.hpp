@@ -44,6 +44,7 @@ struct DecodeParams {
     int tier_cold_splits;      // workgroups [0, tier_cold_splits) take cold splits
     int tier_k_lo;             // first visible position
     int tier_cold_tokens;      // tokens per cold split (split_tokens: per hot split)
+    int tier_cold_stride;      // contiguous cold tier: rows per KV head
 };
 
 struct FwdParams {
@@ -86,8 +87,10 @@ int decode_max_heads_per_workgroup();
 int decode_workgroups_per_cu(int head_dim, bool paged);
 int decode_max_splits();
 int decode_max_split_tokens_paged();
-// tiered decode: grid (n_splits, Hkv * head chunks)
-hipError_t launch_decode_tiered(const DecodeParams& p, int head_dim, int gc, int n_splits, hipStream_t st);
+// tiered decode: grid (n_splits, Hkv * head chunks); the cold tier is int8 (with per-row
+// scales) or f16, paged or contiguous
+hipError_t launch_decode_tiered(const DecodeParams& p, int head_dim, int gc, int n_splits, bool cold_int8,
+                                bool cold_paged, hipStream_t st);
 
 // Library-owned decode scratch of this GPU (the device of `st`, or the current device for
 // the null stream): its device address, looked up once per device.
