@@ -52,7 +52,7 @@ def parse():
     ap.add_argument("--workload", default="decode_f16",
                     choices=["decode_f16", "prefill_f32", "prefill_f16", "vision_f16",
                              "decode_paged_q8", "prefill_chunk_f16", "decode_ring_f16",
-                             "decode_tiered_q8", "block_local_f32", "all"])
+                             "decode_tiered_q8", "decode_tiered_f16", "block_local_f32", "all"])
     ap.add_argument("--repeats", type=int, default=5,
                     help="timed replays; the median is reported")
     ap.add_argument("--only-headline", action="store_true")
@@ -255,7 +255,7 @@ class Tiered(Workload):
     ring (hot tier, seeded start row), 32/8 heads, head_dim 128."""
     name = "decode_tiered_q8"
     kind = "hbm"
-    kernel = "decode_tiered_kernel<128, 4, false>"
+    kernel = "decode_tiered_kernel<128, 4, 0, false>"
 
     def __init__(self, dev, cold=28672, hot=4096, R=4096, hot_start=1234):
         import numpy as np
@@ -315,6 +315,61 @@ class Tiered(Workload):
 
     def cpu_run(self, threads):
         return self._oracle(threads)
+
+
+class TieredF16(Tiered):
+    """Tiered decode with an f16 cold tier in 16-token pages: 28672 old positions (seeded page
+    placement) plus the newest 4096 in a 4096-row f16 ring, 32/8 heads, head_dim 128."""
+    name = "decode_tiered_f16"
+    kernel = "decode_tiered_kernel<128, 4, 2, false>"
+
+    def __init__(self, dev, cold=28672, hot=4096, R=4096, hot_start=1234):
+        import numpy as np
+        import torch
+
+        import synth
+        import transformer_attention_03_amd as ta
+        self.ta, self.torch = ta, torch
+        self.cold, self.hot = cold, hot
+        t = synth.tiered_f16_inputs(synth.seed_of(6) + 1, 32, 8, 128, cold, hot, R, hot_start, True,
+                                    n_poison=64)
+        self.t = t
+        dv = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to(dev)
+        self.q, self.pt = dv(t["q"]), dv(t["cold_page_table"])
+        first = tuple(dv(x) for x in (t["ring_k"], t["ring_v"], t["cold_k_pages"], t["cold_v_pages"]))
+        self.nc = n_copies(sum(x.nbytes for x in first))
+        self.copies = [first] + [tuple(x.clone() for x in first) for _ in range(self.nc - 1)]
+        self.o = torch.empty((32, 128), dtype=torch.float32, device=dev)
+        self.ws = ta.decode_workspace(1, 32, 8, 128, cold + hot, dev)
+        self.hot_start = hot_start
+        self.desc = {"workload": "tiered single-token decode with an f16 cold tier: 28672 positions in "
+                                 "16-token f16 pages (seeded permutation) + the newest 4096 in an f16 "
+                                 "ring [8, 4096, 128], f32 q [32, 128], GQA 32/8, scale 1/sqrt(128)",
+                     "batch": 1, "num_heads": 32, "num_kv_heads": 8, "head_dim": 128,
+                     "cold_len": cold, "hot_len": hot, "hot_window": R, "hot_start": hot_start,
+                     "cold_dtype": "f16", "cold_layout": "paged", "hot_dtype": "f16", "q_dtype": "f32",
+                     "input_copies": self.nc}
+
+    def step(self, i):
+        hk, hv, kp, vp = self.copies[i % self.nc]
+        self.ta.attn_decode_tiered_f16(self.q, hk, hv, kp, vp, self.pt, self.o, self.ws,
+                                       cold_len=self.cold, hot_len=self.hot, hot_start=self.hot_start,
+                                       scale=1 / math.sqrt(128))
+
+    def units(self):
+        b = ((self.cold + self.hot) * 8 * 128 * 2 * 2 + ((self.cold + 15) // 16) * 4
+             + 2 * 32 * 128 * 4)
+        return b, "bytes"
+
+    def _oracle(self, threads):
+        import numpy as np
+
+        import oracle
+        t = self.t
+        k = np.concatenate([t["cold_k"], t["hot_k"]]).astype(np.float64)
+        v = np.concatenate([t["cold_v"], t["hot_v"]]).astype(np.float64)
+        return oracle.attention(t["q"][None, None], k[None], v[None], causal=True,
+                                scale=1 / math.sqrt(128), threads=threads)[0, 0]
 
 
 class BlockLocal(Workload):
@@ -491,7 +546,7 @@ class Forward(Workload):
 
 
 ALL = ["decode_f16", "prefill_f32", "prefill_f16", "vision_f16", "decode_paged_q8", "prefill_chunk_f16",
-       "decode_ring_f16", "decode_tiered_q8", "block_local_f32"]
+       "decode_ring_f16", "decode_tiered_q8", "decode_tiered_f16", "block_local_f32"]
 
 
 def make(name, dev):
@@ -505,6 +560,8 @@ def make(name, dev):
         return Tiered(dev)
     if name == "block_local_f32":
         return BlockLocal(dev)
+    if name == "decode_tiered_f16":
+        return TieredF16(dev)
     return Forward(dev, name)
 
 
