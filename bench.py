@@ -377,7 +377,7 @@ class BlockLocal(Workload):
     of 12 frames attending over 12 frames of past and none of future, logit cap 50, f32."""
     name = "block_local_f32"
     kind = "hbm"
-    kernel = "block_local_kernel<true>"
+    kernel = "block_local_kernel<32, true>"
 
     def __init__(self, dev, seq=3000, H=8, chunk=12, past=12, future=0, cap=50.0):
         import numpy as np
