@@ -651,6 +651,26 @@ def test_prefill_f32(dev, D, S, L, H, Hkv, causal, W, cap):
     assert maxabs(got, want) < TOL_F32
 
 
+# f32 instantiations fwd_f32_kernel<D, CAP, KG> not reached above: key groups run below 64
+# workgroups of 64 rows at head_dim 64 and 128, the 64-row blocks at and above it.
+@pytest.mark.parametrize("D,S,L,H,Hkv,causal,W,cap", [
+    (64, 100, 100, 2, 1, True, 0, 15.0),       # <64, true, true>
+    (64, 520, 600, 8, 2, True, 200, 15.0),     # <64, true, false>: 72 workgroups
+    (128, 520, 520, 8, 4, True, 0, 30.0),      # <128, true, false>
+    (128, 520, 700, 8, 2, True, 100, 0.0),     # <128, false, false> with a window
+    (256, 200, 200, 2, 1, True, 0, 0.0),       # <256, false, false>
+    (256, 130, 300, 4, 2, False, 0, 0.0),
+])
+def test_prefill_f32_every_instantiation(dev, D, S, L, H, Hkv, causal, W, cap):
+    say("prefill f32 instantiation D=%d S=%d L=%d H=%d cap=%g" % (D, S, L, H, cap))
+    q, k, v = synth.prefill_inputs(synth.seed_of(1) + 7 * S + L + D, S, L, H, Hkv, D, "f32")
+    got = run_prefill(dev, q, k, v, causal, W, cap)
+    assert np.all(np.isfinite(got))
+    want = oracle.attention(q[None], k[None], v[None], causal=causal, window=W, softcap=cap,
+                            scale=1 / math.sqrt(D))[0]
+    assert maxabs(got, want) < TOL_F32
+
+
 @pytest.fixture(scope="module")
 def c3_inputs():
     """Causal GQA prefill: 2048 tokens, 16/8 heads, head_dim 256, f16."""
