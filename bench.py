@@ -61,6 +61,9 @@ def parse():
                     help="launch every step from the host instead of replaying a HIP graph")
     ap.add_argument("--profile-steps", type=int, default=0,
                     help="only run this many steps of the selected workload(s), for profilers")
+    ap.add_argument("--floors", action="store_true",
+                    help="time the memory-system floors of the decode workloads (libattn_floors.so) "
+                         "beside the decode kernels, one JSON line")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="with --profile-steps: also run a plain elementwise copy of this many "
                          "bytes per step (calibrates the HBM byte counters)")
@@ -719,6 +722,165 @@ def cpu_baseline(wl, budget_s=10.0):
             "kind": "oracle", "sample": sample + " (median %.3f s per repeat)" % med}
 
 
+
+# ---------------------------------------------------------------------------------------------
+# memory-system floors (--floors): probes from libattn_floors.so, timed like the workloads
+# ---------------------------------------------------------------------------------------------
+
+def floors_lib():
+    import ctypes
+    path = os.path.join(ROOT, "transformer_attention_03_amd", "libattn_floors.so")
+    if not os.path.exists(path):
+        raise RuntimeError("libattn_floors.so is not built; run python -m transformer_attention_03_amd.build")
+    L = ctypes.CDLL(path)
+    vp, i, l = ctypes.c_void_p, ctypes.c_int, ctypes.c_long
+    L.floor_empty.argtypes = [i, vp]
+    L.floor_stream.argtypes = [vp, l, i, vp, vp]
+    L.floor_stream_merge.argtypes = [vp, l, i, i, vp, vp, vp, vp]
+    L.floor_gather.argtypes = [vp, vp, vp, i, i, l, vp, vp]
+    for f in (L.floor_empty, L.floor_stream, L.floor_stream_merge, L.floor_gather):
+        f.restype = i
+    return L
+
+
+class Floor(Workload):
+    kind = "floor"
+
+    def __init__(self, dev, lib):
+        import torch
+        self.torch, self.lib, self.dev = torch, lib, dev
+
+    def stream(self):
+        return self.torch.cuda.current_stream().cuda_stream
+
+    def call(self, rc):
+        if rc != 0:
+            raise RuntimeError("%s: the probe refused its arguments (%d)" % (self.name, rc))
+
+
+class FloorEmpty(Floor):
+    """Launches of `grid` workgroups of 512 threads that do nothing."""
+
+    def __init__(self, dev, lib, grid):
+        super().__init__(dev, lib)
+        self.grid, self.nbytes = grid, 0
+        self.name = "empty_%dx512" % grid
+
+    def step(self, i):
+        self.call(self.lib.floor_empty(self.grid, self.stream()))
+
+
+class FloorStream(Floor):
+    """A plain read of `nbytes` (16-byte loads, workgroup w reads the w-th of `grid` equal
+    ranges), over input copies as the workloads rotate them; with merge=(splits, groups), the
+    read is followed by one split-KV-shaped merge per group."""
+
+    def __init__(self, dev, lib, nbytes, grid=None, merge=None):
+        super().__init__(dev, lib)
+        torch = self.torch
+        self.nbytes, self.merge = nbytes, merge
+        self.grid = merge[0] * merge[1] if merge else grid
+        self.nc = n_copies(nbytes)
+        g = torch.Generator(device=dev)
+        g.manual_seed(1)
+        self.srcs = [torch.randint(0, 256, (nbytes,), dtype=torch.uint8, device=dev, generator=g)
+                     for _ in range(self.nc)]
+        self.sink = torch.zeros(self.grid * 8, dtype=torch.float32, device=dev)
+        if merge:
+            sp, gr = merge
+            self.part = torch.zeros(gr * sp * 520, dtype=torch.float32, device=dev)
+            self.tickets = torch.zeros(gr, dtype=torch.int32, device=dev)
+            self.out = torch.zeros(gr * 520, dtype=torch.float32, device=dev)
+            self.name = "stream_merge_%dx%d" % (sp, gr)
+        else:
+            self.name = "stream_%dx512" % self.grid
+
+    def step(self, i):
+        src = self.srcs[i % self.nc].data_ptr()
+        if self.merge:
+            sp, gr = self.merge
+            self.call(self.lib.floor_stream_merge(src, self.nbytes, sp, gr, self.part.data_ptr(),
+                                                  self.tickets.data_ptr(), self.out.data_ptr(), self.stream()))
+        else:
+            self.call(self.lib.floor_stream(src, self.nbytes, self.grid, self.sink.data_ptr(), self.stream()))
+
+
+class FloorGather(Floor):
+    """The paged int8 workload's K and V blocks (2 KB: 16 tokens of one KV head) read through
+    its page table with plain 16-byte loads, in the order (sequence, KV head, page); workgroup
+    w reads `per_wg` consecutive blocks of K and the matching V blocks."""
+
+    def __init__(self, dev, lib, per_wg):
+        super().__init__(dev, lib)
+        import numpy as np
+        import synth
+        torch = self.torch
+        c = synth.seed_of(5)
+        lens = synth.paged_kv_lens(c, 8, 16384, 32768)
+        d = synth.paged_inputs(c, 8, 32, 8, 128, lens, n_poison=64, max_pages=2048)
+        P, Hkv = d["k_pages"].shape[0], d["k_pages"].shape[1]
+        ids = []
+        for b in range(8):
+            n_pages = (int(lens[b]) + 15) // 16
+            phys = d["page_table"][b, :n_pages].astype(np.int64)
+            for h in range(Hkv):
+                ids.append(phys * Hkv + h)
+        ids = np.concatenate(ids).astype(np.uint32)
+        self.n, self.per_wg, self.pool = len(ids), per_wg, P * Hkv
+        self.blocks = torch.from_numpy(ids).to(dev)
+        kp = torch.from_numpy(np.ascontiguousarray(d["k_pages"])).to(dev)
+        vp = torch.from_numpy(np.ascontiguousarray(d["v_pages"])).to(dev)
+        self.nbytes = 2 * 2048 * self.n
+        self.nc = n_copies(2 * kp.numel())
+        self.copies = [(kp, vp)] + [(kp.clone(), vp.clone()) for _ in range(self.nc - 1)]
+        self.grid = (self.n + per_wg - 1) // per_wg
+        self.sink = torch.zeros(self.grid * 8, dtype=torch.float32, device=dev)
+        self.name = "gather_paged_%d_per_wg" % per_wg
+
+    def step(self, i):
+        kp, vp = self.copies[i % self.nc]
+        self.call(self.lib.floor_gather(kp.data_ptr(), vp.data_ptr(), self.blocks.data_ptr(), self.n,
+                                        self.per_wg, self.pool, self.sink.data_ptr(), self.stream()))
+
+
+def run_floors(dev, a):
+    """Times the floors with the workloads' method and prints one JSON line beside the
+    decode kernels' own times."""
+    import torch
+    lib = floors_lib()
+    kv = 2 * 8 * 4096 * 128 * 2          # the headline decode's K and V bytes
+    probes = [lambda: FloorEmpty(dev, lib, 128), lambda: FloorEmpty(dev, lib, 1024),
+              lambda: FloorStream(dev, lib, kv, grid=128), lambda: FloorStream(dev, lib, kv, grid=256),
+              lambda: FloorStream(dev, lib, kv, grid=1024),
+              lambda: FloorStream(dev, lib, kv, merge=(16, 8)),
+              lambda: FloorGather(dev, lib, 256), lambda: FloorGather(dev, lib, 128),
+              lambda: FloorGather(dev, lib, 64)]
+    rows = []
+    for mk in probes:
+        f = mk()
+        log("floor %s" % f.name)
+        ms, per = time_steps(f, a.steps, a.warmup, graph=True, repeats=a.repeats)
+        us = ms * 1e3
+        rows.append({"probe": f.name, "grid": f.grid, "bytes_per_launch": f.nbytes,
+                     "us_per_launch": round(us, 3),
+                     "TB_per_s": round(f.nbytes / (us * 1e-6) / 1e12, 3) if f.nbytes else None,
+                     "us_each_replay": [round(x * 1e3, 3) for x in per]})
+        del f
+        torch.cuda.empty_cache()
+    kernels = {}
+    for name in ("decode_f16", "decode_paged_q8"):
+        wl = make(name, dev)
+        log("kernel %s" % name)
+        ms, _ = time_steps(wl, a.steps if name == "decode_f16" else max(20, a.steps // 4), a.warmup,
+                           graph=True, repeats=a.repeats)
+        b, _u = wl.units()
+        kernels[name] = {"us_per_call": round(ms * 1e3, 3), "algorithmic_bytes": b,
+                         "TB_per_s": round(b / (ms * 1e-3) / 1e12, 3)}
+        del wl
+        torch.cuda.empty_cache()
+    print(json.dumps({"floors": rows, "kernels": kernels, "steps": a.steps, "repeats": a.repeats,
+                      "timing": "median of timed graph replays, as the workloads"}))
+
 def main():
     a = parse()
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -736,6 +898,10 @@ def main():
         print("no GPU visible", file=sys.stderr)
         sys.exit(1)
     dev = torch.device("cuda:0")
+
+    if a.floors:
+        run_floors(dev, a)
+        return
 
     if a.profile_steps:
         names = ALL if a.workload == "all" else [a.workload]

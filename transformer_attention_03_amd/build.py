@@ -2,9 +2,10 @@
 
     python -m transformer_attention_03_amd.build
 
-Compiles every source under csrc/ with hipcc for gfx950 and links them into
-transformer_attention_03_amd/libattn.so.  Packed FP32 instructions are disabled
-(-packed-fp32-ops) for all device code.
+Compiles the library's sources under csrc/ with hipcc for gfx950 and links them into
+transformer_attention_03_amd/libattn.so, and the memory-system floor probes that the
+benchmark times beside the kernels (csrc/floors.hip) into libattn_floors.so.  Packed FP32
+instructions are disabled (-packed-fp32-ops) for all device code.
 """
 from __future__ import annotations
 
@@ -22,6 +23,8 @@ LIB = os.path.join(PKG, "libattn.so")
 BUILD_DIR = os.path.join(PKG, "_build")
 
 SOURCES = ["api.cpp", "decode.hip", "fwd.hip", "block_local.hip"]
+FLOORS_SOURCE = "floors.hip"
+FLOORS_LIB = os.path.join(PKG, "libattn_floors.so")
 # per-source extra hipcc flags (none at present)
 KERNEL_FLAGS = {}
 ARCH = os.environ.get("TA03_OFFLOAD_ARCH", "gfx950")
@@ -58,18 +61,24 @@ def _compile(src: str, extra=()) -> str:
     return obj
 
 
-def build(verbose: bool = True, extra=()) -> str:
-    os.makedirs(BUILD_DIR, exist_ok=True)
-    with ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
-        objs = list(ex.map(lambda s: _compile(s, extra), SOURCES))
-    tmp = LIB + ".tmp%d" % os.getpid()
+def _link(objs, out):
+    tmp = out + ".tmp%d" % os.getpid()
     cmd = [hipcc(), "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("link failed:\n%s\n%s" % (" ".join(cmd), r.stderr[-4000:]))
-    os.replace(tmp, LIB)
+    os.replace(tmp, out)
+
+
+def build(verbose: bool = True, extra=()) -> str:
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    srcs = SOURCES + [FLOORS_SOURCE]
+    with ThreadPoolExecutor(max_workers=len(srcs)) as ex:
+        objs = list(ex.map(lambda s: _compile(s, extra), srcs))
+    _link(objs[:len(SOURCES)], LIB)
+    _link(objs[len(SOURCES):], FLOORS_LIB)
     if verbose:
-        print("built", LIB)
+        print("built", LIB, "and", FLOORS_LIB)
     return LIB
 
 
