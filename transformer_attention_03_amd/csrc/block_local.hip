@@ -14,8 +14,9 @@
 //
 // Work decomposition: a workgroup owns 32 consecutive query rows of one head (16 when the
 // span exceeds 20).  Their keys lie in a window of rows + past + future rows, which is
-// staged in LDS once (K and V) with the head's pos_proj rows; a 16-lane group owns one
-// query row (each lane 8 of its 128
+// staged in LDS once (K and V) with the head's pos_proj rows, every load issued before the
+// first LDS write; workgroups are placed so that neighbouring row blocks, whose windows
+// overlap, run on one XCD.  A 16-lane group owns one query row (each lane 8 of its 128
 // dimensions, the query itself in registers), walks the row's span of offsets computing
 // q.(k + pos) with a 16-lane butterfly sum, then the softmax and the weighted V rows.  The
 // work is a band of at most span keys per query, a few thousand FLOP per output row: the
@@ -42,6 +43,7 @@ constexpr int bl_lds_floats(int span) { return kBlStride * (2 * (ROWS + span - 1
 template <int ROWS, bool CAP>
 __global__ void __launch_bounds__(16 * ROWS) block_local_kernel(BlockLocalParams a) {
     constexpr int kBlRows = ROWS;                  // query rows per workgroup (one per 16-lane group)
+    constexpr int MAXS = ROWS == 32 ? kBlWideSpan : kBlMaxSpan;   // largest span of this shape
     constexpr int NT = 16 * ROWS;
     extern __shared__ __attribute__((aligned(16))) float bl_lds[];
     const int span = a.max_past + a.max_future + 1;
@@ -50,32 +52,19 @@ __global__ void __launch_bounds__(16 * ROWS) block_local_kernel(BlockLocalParams
     float* vw = kw + nwin * kBlStride;             // [nwin][stride]
     float* pw = vw + nwin * kBlStride;             // [span][stride]
 
-    const int head = blockIdx.y;
-    const int i0 = blockIdx.x * kBlRows;
+    // XCD-aware placement: workgroup ids are dealt to the eight XCDs in turn, so give each XCD
+    // a contiguous range of (head, row block) items; neighbouring row blocks, whose windows
+    // overlap by span - 1 rows, then share an L2
+    const int n = gridDim.x;
+    const int id = blockIdx.x;
+    const int xcd = id & 7, kk = id >> 3, q8 = n >> 3, r8 = n & 7;
+    const int item = (xcd < r8 ? xcd * (q8 + 1) : r8 * (q8 + 1) + (xcd - r8) * q8) + kk;
+    const int nrb = (a.padded_len + kBlRows - 1) / kBlRows;
+    const int head = item / nrb;
+    const int i0 = (item % nrb) * kBlRows;
     const int w0 = i0 - a.max_past;                // position of window row 0
     const long hid = (long)a.H * kBlD;             // floats per row of every tensor
     const int tid = threadIdx.x;
-
-    // ---- stage the window's K and V rows and pos_proj; rows of positions outside [0, seq)
-    // are never read from memory and hold zeros in LDS (their scores are masked, and a zero V
-    // row keeps the weighted sum finite)
-    for (int c = tid; c < nwin * (kBlD / 4); c += NT) {
-        const int r = c / (kBlD / 4), d4 = c % (kBlD / 4);
-        const int t = w0 + r;
-        float4 kv = {0.f, 0.f, 0.f, 0.f}, vv = {0.f, 0.f, 0.f, 0.f};
-        if (t >= 0 && t < a.seq) {
-            const long g = (long)(t + a.pad_left) * hid + (long)head * kBlD + 4 * d4;
-            kv = *reinterpret_cast<const float4*>(a.k + g);
-            vv = *reinterpret_cast<const float4*>(a.v + g);
-        }
-        *reinterpret_cast<float4*>(kw + r * kBlStride + 4 * d4) = kv;
-        *reinterpret_cast<float4*>(vw + r * kBlStride + 4 * d4) = vv;
-    }
-    for (int c = tid; c < span * (kBlD / 4); c += NT) {
-        const int r = c / (kBlD / 4), d4 = c % (kBlD / 4);
-        *reinterpret_cast<float4*>(pw + r * kBlStride + 4 * d4) =
-            *reinterpret_cast<const float4*>(a.pos + (long)r * hid + (long)head * kBlD + 4 * d4);
-    }
 
     // ---- this lane's query row and dimensions: row g = tid / 16, d in 4 l + {0..3}, 64 + 4 l + {0..3}
     const int g = tid >> 4;
@@ -88,6 +77,49 @@ __global__ void __launch_bounds__(16 * ROWS) block_local_kernel(BlockLocalParams
         q0 = *reinterpret_cast<const float4*>(qrow + 4 * l);
         q1 = *reinterpret_cast<const float4*>(qrow + 64 + 4 * l);
     }
+    // ---- stage the window's K and V rows and pos_proj: every load of the workgroup's share
+    // is issued before the first LDS write, so the staging costs one memory round trip; rows
+    // of positions outside [0, seq) are never read from memory and hold zeros in LDS (their
+    // scores are masked, and a zero V row keeps the weighted sum finite)
+    constexpr int KV_IT = ((kBlRows + MAXS - 1) * (kBlD / 4) + NT - 1) / NT;
+    constexpr int P_IT = (MAXS * (kBlD / 4) + NT - 1) / NT;
+    float4 kst[KV_IT], vst[KV_IT], pst[P_IT];
+#pragma unroll
+    for (int u = 0; u < KV_IT; ++u) {
+        const int c = tid + u * NT;
+        const int r = c / (kBlD / 4), d4 = c % (kBlD / 4);
+        const int t = w0 + r;
+        kst[u] = float4{0.f, 0.f, 0.f, 0.f};
+        vst[u] = kst[u];
+        if (r < nwin && t >= 0 && t < a.seq) {
+            const long gofs = (long)(t + a.pad_left) * hid + (long)head * kBlD + 4 * d4;
+            kst[u] = *reinterpret_cast<const float4*>(a.k + gofs);
+            vst[u] = *reinterpret_cast<const float4*>(a.v + gofs);
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < P_IT; ++u) {
+        const int c = tid + u * NT;
+        const int r = c / (kBlD / 4), d4 = c % (kBlD / 4);
+        pst[u] = float4{0.f, 0.f, 0.f, 0.f};
+        if (r < span) pst[u] = *reinterpret_cast<const float4*>(a.pos + (long)r * hid + (long)head * kBlD + 4 * d4);
+    }
+
+#pragma unroll
+    for (int u = 0; u < KV_IT; ++u) {
+        const int c = tid + u * NT;
+        const int r = c / (kBlD / 4), d4 = c % (kBlD / 4);
+        if (r < nwin) {
+            *reinterpret_cast<float4*>(kw + r * kBlStride + 4 * d4) = kst[u];
+            *reinterpret_cast<float4*>(vw + r * kBlStride + 4 * d4) = vst[u];
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < P_IT; ++u) {
+        const int c = tid + u * NT;
+        const int r = c / (kBlD / 4), d4 = c % (kBlD / 4);
+        if (r < span) *reinterpret_cast<float4*>(pw + r * kBlStride + 4 * d4) = pst[u];
+    }
     __syncthreads();
 
     // visible offsets j of this row: t = qi - past + j in [0, seq)
@@ -97,10 +129,10 @@ __global__ void __launch_bounds__(16 * ROWS) block_local_kernel(BlockLocalParams
     // ---- scores, held by every lane of the group (the butterfly leaves the sum everywhere);
     // every offset of the span is computed (a branch per offset would split the groups of a
     // wave) and the invisible ones are masked to -inf ----------------------------------------
-    float s[kBlMaxSpan];
+    float s[MAXS];
     float m = -INFINITY;
 #pragma unroll
-    for (int j = 0; j < kBlMaxSpan; ++j) {
+    for (int j = 0; j < MAXS; ++j) {
         s[j] = -INFINITY;
         if (j < span) {
             const float* kr = kw + (g + j) * kBlStride;
@@ -138,7 +170,7 @@ __global__ void __launch_bounds__(16 * ROWS) block_local_kernel(BlockLocalParams
     float lsum = 0.f;
     float4 o0 = {0.f, 0.f, 0.f, 0.f}, o1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int j = 0; j < kBlMaxSpan; ++j) {
+    for (int j = 0; j < MAXS; ++j) {
         if (j < span) {
             const float p = __builtin_amdgcn_exp2f((s[j] - m) * kLog2e);
             lsum += p;
@@ -170,7 +202,7 @@ int block_local_head_dim() { return kBlD; }
 
 template <int ROWS>
 hipError_t launch_rows(const BlockLocalParams& p, hipStream_t st) {
-    const dim3 grid((p.padded_len + ROWS - 1) / ROWS, p.H);
+    const dim3 grid(((p.padded_len + ROWS - 1) / ROWS) * p.H);
     const size_t lds = sizeof(float) * (size_t)bl_lds_floats<ROWS>(p.max_past + p.max_future + 1);
     if (p.cap > 0.f)
         hipLaunchKernelGGL((block_local_kernel<ROWS, true>), grid, dim3(16 * ROWS), lds, st, p);
@@ -183,6 +215,7 @@ hipError_t launch_block_local(const BlockLocalParams& p, hipStream_t st) {
     // 32 query rows per workgroup where the window fits 64 KB (half the workgroups, each
     // staging 32 + span - 1 key rows instead of 16 + span - 1 for 16 queries, and for the
     // 3000-frame, 8-head workload one round of resident workgroups: 17.8 against 22.1 us)
+    if ((long)((p.padded_len + 15) / 16) * p.H > 0x7fffffffL) return hipErrorInvalidValue;
     static_assert(sizeof(float) * bl_lds_floats<32>(kBlWideSpan) <= 65536, "wide windows fit 64 KB");
     static_assert(sizeof(float) * bl_lds_floats<16>(kBlMaxSpan) <= 65536, "windows fit 64 KB");
     if (p.max_past + p.max_future + 1 <= kBlWideSpan) return launch_rows<32>(p, st);
