@@ -8,9 +8,10 @@ A step is one call of the workload's entry point over one batch of synthetic inp
 contiguous f16 KV cache (32 query / 8 KV heads, head_dim 128, kv_len 4096); the other
 workloads (f32 causal prefill, f16 windowed+softcapped GQA prefill, f16 vision, batched
 paged int8 decode, f16 chunked prefill against a cache whose length is read on the device,
-f16 decode over a ring-buffer cache, and tiered decode over an int8 paged cold tier plus an
-f16 ring hot tier) are measured on the same JSON line under
-"workloads".
+f16 decode over a ring-buffer cache, tiered decode over an int8 or f16 cold tier, paged or
+contiguous, plus an f16 ring hot tier, and Conformer block-local attention) are measured on
+the same JSON line under "workloads".  `--floors` times the memory-system floors of the
+decode workloads (libattn_floors.so) beside the decode kernels instead.
 
 Timing: W untimed steps, then K steps between HIP events recorded on the stream the
 kernels run on, after a device synchronisation on both sides; the median of 5 such timed
@@ -52,7 +53,8 @@ def parse():
     ap.add_argument("--workload", default="decode_f16",
                     choices=["decode_f16", "prefill_f32", "prefill_f16", "vision_f16",
                              "decode_paged_q8", "prefill_chunk_f16", "decode_ring_f16",
-                             "decode_tiered_q8", "decode_tiered_f16", "block_local_f32", "all"])
+                             "decode_tiered_q8", "decode_tiered_f16", "decode_tiered_q8_packed",
+                             "decode_tiered_f16_contig", "block_local_f32", "all"])
     ap.add_argument("--repeats", type=int, default=5,
                     help="timed replays; the median is reported")
     ap.add_argument("--only-headline", action="store_true")
@@ -375,6 +377,90 @@ class TieredF16(Tiered):
                                 scale=1 / math.sqrt(128), threads=threads)[0, 0]
 
 
+class TieredPacked(Tiered):
+    """Tiered decode whose int8 cold tier is one contiguous array per KV head (no page
+    table): the same 28672 cold rows and scales as the paged int8 tier, plus the newest 4096
+    in a 4096-row f16 ring, 32/8 heads, head_dim 128."""
+    name = "decode_tiered_q8_packed"
+    kernel = "decode_tiered_kernel<128, 4, 1, false>"
+
+    def __init__(self, dev, cold=28672, hot=4096, R=4096, hot_start=1234):
+        import numpy as np
+        import torch
+
+        import synth
+        import transformer_attention_03_amd as ta
+        self.ta, self.torch = ta, torch
+        self.cold, self.hot = cold, hot
+        t = synth.tiered_packed_inputs(synth.seed_of(6), 32, 8, 128, cold, hot, R, hot_start, capacity=cold)
+        self.t = t
+        dv = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to(dev)
+        self.q = dv(t["q"])
+        first = tuple(dv(t[x]) for x in ("ring_k", "ring_v", "packed_k", "packed_v", "packed_k_scales",
+                                           "packed_v_scales"))
+        self.nc = n_copies(sum(x.nbytes for x in first))
+        self.copies = [first] + [tuple(x.clone() for x in first) for _ in range(self.nc - 1)]
+        self.o = torch.empty((32, 128), dtype=torch.float32, device=dev)
+        self.ws = ta.decode_workspace(1, 32, 8, 128, cold + hot, dev)
+        self.hot_start = hot_start
+        self.desc = {"workload": "tiered single-token decode with a packed int8 cold tier: 28672 "
+                                 "positions in int8 [8, 28672, 128] with per-token scales (no page "
+                                 "table) + the newest 4096 in an f16 ring [8, 4096, 128], f32 q "
+                                 "[32, 128], GQA 32/8, scale 1/sqrt(128)",
+                     "batch": 1, "num_heads": 32, "num_kv_heads": 8, "head_dim": 128,
+                     "cold_len": cold, "hot_len": hot, "hot_window": R, "hot_start": hot_start,
+                     "cold_dtype": "int8", "cold_layout": "contiguous", "hot_dtype": "f16",
+                     "q_dtype": "f32", "input_copies": self.nc}
+
+    def step(self, i):
+        hk, hv, kc, vc, ks, vs = self.copies[i % self.nc]
+        self.ta.attn_decode_tiered_q8_packed(self.q, hk, hv, kc, vc, ks, vs, self.o, self.ws,
+                                             cold_len=self.cold, hot_len=self.hot,
+                                             hot_start=self.hot_start, scale=1 / math.sqrt(128))
+
+    def units(self):
+        b = self.cold * 8 * (128 + 128 + 4 + 4) + self.hot * 8 * 128 * 2 * 2 + 2 * 32 * 128 * 4
+        return b, "bytes"
+
+
+class TieredF16Contig(TieredF16):
+    """Tiered decode with a contiguous f16 cold tier [8, 28672, 128] (no page table) plus the
+    newest 4096 in a 4096-row f16 ring, 32/8 heads, head_dim 128."""
+    name = "decode_tiered_f16_contig"
+    kernel = "decode_tiered_kernel<128, 4, 3, false>"
+
+    def __init__(self, dev, cold=28672, hot=4096, R=4096, hot_start=1234):
+        import numpy as np
+        import torch
+
+        import synth
+        import transformer_attention_03_amd as ta
+        self.ta, self.torch = ta, torch
+        self.cold, self.hot = cold, hot
+        t = synth.tiered_f16_inputs(synth.seed_of(6) + 1, 32, 8, 128, cold, hot, R, hot_start, False,
+                                    capacity=cold)
+        self.t = t
+        dv = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to(dev)
+        self.q, self.pt = dv(t["q"]), None
+        first = tuple(dv(t[x]) for x in ("ring_k", "ring_v", "cold_k_contig", "cold_v_contig"))
+        self.nc = n_copies(sum(x.nbytes for x in first))
+        self.copies = [first] + [tuple(x.clone() for x in first) for _ in range(self.nc - 1)]
+        self.o = torch.empty((32, 128), dtype=torch.float32, device=dev)
+        self.ws = ta.decode_workspace(1, 32, 8, 128, cold + hot, dev)
+        self.hot_start = hot_start
+        self.desc = {"workload": "tiered single-token decode with a contiguous f16 cold tier: 28672 "
+                                 "positions in f16 [8, 28672, 128] + the newest 4096 in an f16 ring "
+                                 "[8, 4096, 128], f32 q [32, 128], GQA 32/8, scale 1/sqrt(128)",
+                     "batch": 1, "num_heads": 32, "num_kv_heads": 8, "head_dim": 128,
+                     "cold_len": cold, "hot_len": hot, "hot_window": R, "hot_start": hot_start,
+                     "cold_dtype": "f16", "cold_layout": "contiguous", "hot_dtype": "f16",
+                     "q_dtype": "f32", "input_copies": self.nc}
+
+    def units(self):
+        b = (self.cold + self.hot) * 8 * 128 * 2 * 2 + 2 * 32 * 128 * 4
+        return b, "bytes"
+
+
 class BlockLocal(Workload):
     """Conformer block-local attention (audio encoder): 3000 frames, 8 heads of 128, chunks
     of 12 frames attending over 12 frames of past and none of future, logit cap 50, f32."""
@@ -549,7 +635,8 @@ class Forward(Workload):
 
 
 ALL = ["decode_f16", "prefill_f32", "prefill_f16", "vision_f16", "decode_paged_q8", "prefill_chunk_f16",
-       "decode_ring_f16", "decode_tiered_q8", "decode_tiered_f16", "block_local_f32"]
+       "decode_ring_f16", "decode_tiered_q8", "decode_tiered_f16", "decode_tiered_q8_packed",
+       "decode_tiered_f16_contig", "block_local_f32"]
 
 
 def make(name, dev):
@@ -565,6 +652,10 @@ def make(name, dev):
         return BlockLocal(dev)
     if name == "decode_tiered_f16":
         return TieredF16(dev)
+    if name == "decode_tiered_q8_packed":
+        return TieredPacked(dev)
+    if name == "decode_tiered_f16_contig":
+        return TieredF16Contig(dev)
     return Forward(dev, name)
 
 
