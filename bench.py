@@ -540,7 +540,7 @@ class Forward(Workload):
             self.S, self.H, self.Hkv, self.D, self.causal, self.W, self.cap = 2048, 16, 8, 256, True, 512, 50.0
             q, k, v = synth.prefill_inputs(synth.seed_of(3), 2048, 2048, 16, 8, 256, "f16")
             self.kind = "mfma"
-            self.kernel = "fwd_f16_kernel<256, 1, 8, 2, 64, 1, true>"
+            self.kernel = "fwd_f16_kernel<256, 1, 8, 2, 64, 1, 1>"
             self.desc = {"workload": "causal GQA prefill, f16, 2048 tokens, 16/8 heads, head_dim "
                                      "256, sliding window 512, softcap 50, scale 1/16"}
         elif name == "prefill_chunk_f16":
@@ -548,7 +548,7 @@ class Forward(Workload):
             self.L = 4096
             q, k, v = synth.prefill_inputs(synth.seed_of(3) + 61, 512, 4096, 16, 8, 128, "f16")
             self.kind = "mfma"
-            self.kernel = "fwd_f16_kernel<128, 1, 8, 2, 32, 4, false>"
+            self.kernel = "fwd_f16_kernel<128, 1, 8, 2, 32, 4, 0>"
             self.desc = {"workload": "chunked causal prefill against a cache, f16, 512 new tokens "
                                      "after 3584 cached (kv length 4096 read on the device), "
                                      "16/8 heads, head_dim 128, scale 1/sqrt(128)"}
@@ -556,7 +556,7 @@ class Forward(Workload):
             self.S, self.H, self.Hkv, self.D, self.causal, self.W, self.cap = 2304, 16, 16, 64, False, 0, 0.0
             q, k, v = synth.vision_inputs(synth.seed_of(4), 2304, 16, 64)
             self.kind = "mfma"
-            self.kernel = "fwd_f16_kernel<64, 1, 3, 2, 96, 1, false>"
+            self.kernel = "fwd_f16_kernel<64, 1, 3, 2, 96, 1, 0>"
             self.desc = {"workload": "bidirectional vision attention, f16 [16, 2304, 64] "
                                      "head-major, scale 1/8"}
         self.vision = name == "vision_f16"

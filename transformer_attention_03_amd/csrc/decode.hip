@@ -329,7 +329,7 @@ constexpr int merge_chunk() {
 
 template <int D, bool PAGED, bool CAP>
 __device__ __forceinline__ void process_block(const char* slot, int tb, int t_end, bool full,
-                                              float cap_log2, float qbias,
+                                              float cap_log2, float inv_cap, float qbias,
                                               const half8_t (&qx)[D / 32], WaveAcc<D>& A,
                                               int lane) {
     using S = DecShape<D, PAGED>;
@@ -398,7 +398,7 @@ __device__ __forceinline__ void process_block(const char* slot, int tb, int t_en
     for (int v = 0; v < 4; ++v) {
         float x = sacc[v] + dpp_f<kDppXor1>(sacc[v]);
         if constexpr (PAGED) x = __builtin_fmaf(x, 1024.f, -qbias) * ks[v];
-        if constexpr (CAP) x = tanh_via_exp(x) * cap_log2;
+        if constexpr (CAP) x = tanh_accurate(x * inv_cap) * cap_log2;
         s[v] = x;
     }
     if (!full) {
@@ -552,8 +552,10 @@ __device__ __forceinline__ void split_partial(const DecodeParams& a, const TierS
     // ---- Qx: B operand of the QK product.  Column n = lane % 16 holds part n & 1 of head
     // n / 2 (hi, lo); k = d = 32 kc + 8 (lane / 16) + e, with e in the element order of the
     // K operand (int8: 0 2 1 3 4 6 5 7).  The query is pre-multiplied so that the scores come
-    // out in log2 units (or as the tanh argument when a cap is set).
-    const float qmul = CAP ? a.scale * a.inv_softcap : a.scale_log2;
+    // out in log2 units, or, when a cap is set, as scale * q.k, which the block divides by the
+    // cap in f32 (folding 1 / c into the query as well would push it into the f16 subnormals
+    // for large caps).
+    const float qmul = CAP ? a.scale : a.scale_log2;
     const float cap_log2 = a.softcap * kLog2e;
     // Computed once per workgroup: wave w converts the d chunks kc = w, w + NW, ... and
     // every wave reads all of them back from LDS.
@@ -621,7 +623,7 @@ __device__ __forceinline__ void split_partial(const DecodeParams& a, const TierS
         else wait_vmem_at_most<0>();
         const int tb = first + k * STRIDE;
         process_block<D, PAGED, CAP>(ring + (k % S::RING) * S::SLOT, tb, t_end, tb + kTB <= t_end,
-                                     cap_log2, qbias, qx, A, lane);
+                                     cap_log2, a.inv_softcap, qbias, qx, A, lane);
         const int kn = k + S::RING;
         if (kn < nb) {
             // the slot of block k is refilled once this wave's reads of it are done

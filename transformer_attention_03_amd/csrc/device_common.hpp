@@ -31,6 +31,19 @@ __device__ __forceinline__ float tanh_via_exp(float x) {
     return 1.0f - 2.0f * fast_rcp(e + 1.0f);
 }
 
+// tanh with a small relative error for every argument: below |x| = 1/4 the odd Taylor series
+// x - x^3/3 + 2x^5/15 - 17x^7/315 (remainder under 4e-7 relative there), above it the
+// identity above, whose absolute error of a few f32 ulps of 1 is then under 1e-6 of |x|.
+// A logit cap c tanh(s / c) needs this when c is large: the identity alone errs by about
+// 1.2e-7 c in absolute terms, which for c = 1e6 is 0.1 on every score.
+__device__ __forceinline__ float tanh_accurate(float x) {
+    const float x2 = x * x;
+    float p = __builtin_fmaf(x2, -17.f / 315.f, 2.f / 15.f);
+    p = __builtin_fmaf(x2, p, -1.f / 3.f);
+    const float small = __builtin_fmaf(x * x2, p, x);
+    return __builtin_fabsf(x) < 0.25f ? small : tanh_via_exp(x);
+}
+
 // ---- cross-lane helpers (DPP inside a row of 16 lanes, ds_bpermute across rows) ------------
 
 template <int CTRL>

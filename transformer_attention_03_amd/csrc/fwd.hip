@@ -34,7 +34,10 @@ namespace {
 // tiles, one per group, so every wave walks 1 / KS of the keys.  At the end the groups'
 // online-softmax states (running max, row sum, unnormalised output) are merged through LDS
 // by log-sum-exp and the first group writes the rows.
-template <int D, int QB, int NW, int NS, int BN, int KS, bool CAP>
+// CAP: 0 no logit cap; 1 the cap through the exponential identity alone (caps up to
+// kFastCapMax, where its absolute score error of about 1.2e-7 c stays below 1e-5); 2 the cap
+// through tanh_accurate (larger caps, where that error would grow with c).
+template <int D, int QB, int NW, int NS, int BN, int KS, int CAP>
 __global__ void __launch_bounds__(64 * NW) fwd_f16_kernel(FwdParams a) {
     using S = F16Shape<D, QB, NW, NS, BN, KS>;
     static_assert(KS == 1 || (NS == 2 && QB == 1 && NW % KS == 0), "key groups: two stages, one row block per wave");
@@ -122,10 +125,12 @@ __global__ void __launch_bounds__(64 * NW) fwd_f16_kernel(FwdParams a) {
 
     const float sc2 = CAP ? 1.f : a.scale_log2;        // raw score -> log2 units
     // softcap in log2 units: t = C1 - C2 / (2^(s * K1) + 1), C1 = c log2 e, C2 = 2 c log2 e,
-    // K1 = 2 scale log2 e / c  (c tanh(scale s / c) = c - 2c / (exp(2 scale s / c) + 1))
+    // K1 = 2 scale log2 e / c  (c tanh(scale s / c) = c - 2c / (exp(2 scale s / c) + 1));
+    // for large caps t = C1 tanh(s * KX), KX = scale / c
     const float K1 = 2.f * a.scale * kLog2e * a.inv_softcap;
     const float C1 = a.softcap * kLog2e;
     const float C2 = 2.f * C1;
+    const float KX = a.scale * a.inv_softcap;
 
     // Tile-invariant parts of the fragment addresses (the swizzles depend on the row only
     // through bits that the per-block steps 16 kb, 32 c + 16 h do not change).
@@ -233,7 +238,7 @@ __global__ void __launch_bounds__(64 * NW) fwd_f16_kernel(FwdParams a) {
             half8_t pf[S::QB][S::BN / 32];
 #pragma unroll
             for (int qb = 0; qb < S::QB; ++qb) {
-                if constexpr (CAP) {
+                if constexpr (CAP == 1) {
 #pragma unroll
                     for (int kb = 0; kb < S::NKB; ++kb)
 #pragma unroll
@@ -241,6 +246,11 @@ __global__ void __launch_bounds__(64 * NW) fwd_f16_kernel(FwdParams a) {
                             const float e2 = fast_exp2(st[kb][qb][i] * K1);
                             st[kb][qb][i] = __builtin_fmaf(-C2, fast_rcp(e2 + 1.f), C1);
                         }
+                } else if constexpr (CAP == 2) {
+#pragma unroll
+                    for (int kb = 0; kb < S::NKB; ++kb)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) st[kb][qb][i] = tanh_accurate(st[kb][qb][i] * KX) * C1;
                 }
                 if (masked) {
                     // visible keys of this row form [vlo, vhi]; key - vlo <= vhi - vlo (unsigned)
@@ -612,12 +622,17 @@ bool use_small(int head_dim, int dtype, int seq_len, int H) {
     return (long)((seq_len + bm - 1) / bm) * H < kComputeUnits;
 }
 
+// Largest logit cap taken by the exponential identity alone (kernel CAP mode 1).
+constexpr float kFastCapMax = 64.f;
+
 template <int D, typename C>
 hipError_t launch_f16(const FwdParams& p, dim3 grid, hipStream_t st) {
-    if (p.softcap > 0.f)
-        hipLaunchKernelGGL((fwd_f16_kernel<D, C::QB, C::NW, C::NS, C::BN, C::KS, true>), grid, dim3(64 * C::NW), 0, st, p);
+    if (p.softcap > kFastCapMax)
+        hipLaunchKernelGGL((fwd_f16_kernel<D, C::QB, C::NW, C::NS, C::BN, C::KS, 2>), grid, dim3(64 * C::NW), 0, st, p);
+    else if (p.softcap > 0.f)
+        hipLaunchKernelGGL((fwd_f16_kernel<D, C::QB, C::NW, C::NS, C::BN, C::KS, 1>), grid, dim3(64 * C::NW), 0, st, p);
     else
-        hipLaunchKernelGGL((fwd_f16_kernel<D, C::QB, C::NW, C::NS, C::BN, C::KS, false>), grid, dim3(64 * C::NW), 0, st, p);
+        hipLaunchKernelGGL((fwd_f16_kernel<D, C::QB, C::NW, C::NS, C::BN, C::KS, 0>), grid, dim3(64 * C::NW), 0, st, p);
     return hipGetLastError();
 }
 

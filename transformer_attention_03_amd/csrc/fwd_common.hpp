@@ -79,7 +79,7 @@ __device__ __forceinline__ void work_item(const FwdParams& a, int& head, int& qb
 // code has no branch).
 template <bool CAP>
 __device__ __forceinline__ float score_transform(const FwdParams& a, float s) {
-    if constexpr (CAP) return a.softcap * tanh_via_exp(s * a.scale * a.inv_softcap) * kLog2e;
+    if constexpr (CAP) return a.softcap * tanh_accurate(s * a.scale * a.inv_softcap) * kLog2e;
     return s * a.scale_log2;
 }
 
