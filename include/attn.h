@@ -125,6 +125,10 @@ int attn_vision(const void *q, const void *k, const void *v, void *o,
  *   q, o : float32 [num_heads, head_dim]
  *   k, v : float16 [num_kv_heads, kv_len, head_dim]   (head-major cache)
  *   The query sits at position kv_len - 1 and sees keys [max(0, kv_len - W), kv_len - 1].
+ *   Device-data range: the products run on f16 matrix operands holding q * scale * log2(e)
+ *   (q * scale under a cap) split into a high and a low f16 part, so every element of that
+ *   must stay below 65504 in magnitude (|q| below about 5e5 at scale 1/sqrt(128)); this
+ *   holds for the decode and tiered entry points alike.
  *   workspace : device memory of at least attn_decode_workspace_bytes(1, num_heads,
  *               num_kv_heads, head_dim, kv_len) bytes, 256-byte aligned, ZERO-FILLED by the
  *               caller once when allocated; the kernels leave it zeroed again on completion
