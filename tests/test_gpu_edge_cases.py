@@ -6,7 +6,8 @@ tolerances:
 - a tiny logit cap (c = 1e-3: every capped score within 1e-3 of 0, near-uniform weights);
 - a huge logit cap (c = 1e6: c tanh(s / c) = s to 1e-12, so the result must equal the
   uncapped one), which tests the cap's accuracy for small tanh arguments;
-- identical keys (every score equal: exactly uniform weights).
+- identical keys (every score equal: exactly uniform weights);
+- int8 rows with zero scales (zero K scales: equal scores; zero V scales: a zero output).
 """
 import math
 
@@ -206,3 +207,35 @@ def test_equal_keys_give_the_mean_of_the_visible_values(dev):
     mean1 = v1.astype(np.float64).mean(axis=1)
     for h in range(8):
         assert maxabs(got1[h], mean1[h // 4]) < 2e-5, h
+
+
+def test_paged_zero_scales(dev):
+    """int8 rows whose scales are zero: a sequence whose K scales are all zero has equal
+    scores (uniform weights, the mean of its V rows); one whose V scales are all zero
+    returns zeros; a third sequence is untouched."""
+    lens = [700, 333, 1000]
+    say("edge paged zero scales lens=%s" % lens)
+    H, Hkv, D = 8, 2, 128
+    d = synth.paged_inputs(synth.seed_of(11) + 31, len(lens), H, Hkv, D, lens)
+    for b, key in ((0, "k"), (1, "v")):
+        n_pages = (lens[b] + 15) // 16
+        d[key + "_scales"][d["page_table"][b, :n_pages]] = 0.0
+        d[key + "_s"][b][:] = 0.0
+    t = {k: to_dev(d[k], dev) for k in ("q", "k_pages", "v_pages", "k_scales", "v_scales", "page_table",
+                                        "kv_lens")}
+    o = torch.empty((len(lens), H, D), dtype=torch.float32, device=dev)
+    ws = ta.decode_workspace(len(lens), H, Hkv, D, d["page_table"].shape[1] * 16, dev)
+    ta.attn_decode_paged_q8(t["q"], t["k_pages"], t["v_pages"], t["k_scales"], t["v_scales"], t["page_table"],
+                            t["kv_lens"], o, ws, scale=1 / math.sqrt(D))
+    torch.cuda.synchronize()
+    got = o.cpu().numpy()
+    assert np.all(np.isfinite(got))
+    assert np.all(got[1] == 0)
+    mean0 = oracle.dequant_i8(d["v_q"][0], d["v_s"][0]).mean(axis=0)       # [Hkv, D]
+    for h in range(H):
+        assert maxabs(got[0, h], mean0[h // (H // Hkv)]) < 2e-5, h
+    for b in range(len(lens)):
+        k = oracle.dequant_i8(d["k_q"][b], d["k_s"][b])[None]
+        v = oracle.dequant_i8(d["v_q"][b], d["v_s"][b])[None]
+        want = oracle.attention(d["q"][b][None, None], k, v, causal=True, scale=1 / math.sqrt(D))[0, 0]
+        assert maxabs(got[b], want) < 5e-5 * max(1.0, float(np.abs(want).max())), b
