@@ -943,7 +943,7 @@ def run_floors(dev, a):
     probes = [lambda: FloorEmpty(dev, lib, 128), lambda: FloorEmpty(dev, lib, 1024),
               lambda: FloorStream(dev, lib, kv, grid=128), lambda: FloorStream(dev, lib, kv, grid=256),
               lambda: FloorStream(dev, lib, kv, grid=1024),
-              lambda: FloorStream(dev, lib, kv, merge=(16, 8)),
+              lambda: FloorStream(dev, lib, kv, merge=(16, 8)), lambda: FloorStream(dev, lib, kv, merge=(32, 8)),
               lambda: FloorGather(dev, lib, 256), lambda: FloorGather(dev, lib, 128),
               lambda: FloorGather(dev, lib, 64)]
     rows = []
