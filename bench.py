@@ -829,7 +829,8 @@ def floors_lib():
     L.floor_stream.argtypes = [vp, l, i, vp, vp]
     L.floor_stream_merge.argtypes = [vp, l, i, i, vp, vp, vp, vp]
     L.floor_gather.argtypes = [vp, vp, vp, i, i, l, vp, vp]
-    for f in (L.floor_empty, L.floor_stream, L.floor_stream_merge, L.floor_gather):
+    L.floor_lds_read.argtypes = [i, i, i, vp, vp]
+    for f in (L.floor_empty, L.floor_stream, L.floor_stream_merge, L.floor_gather, L.floor_lds_read):
         f.restype = i
     return L
 
@@ -896,6 +897,21 @@ class FloorStream(Floor):
             self.call(self.lib.floor_stream(src, self.nbytes, self.grid, self.sink.data_ptr(), self.stream()))
 
 
+class FloorLds(Floor):
+    """LDS reads only: `grid` workgroups of `threads` threads, 4 * iters 16-byte reads per
+    lane after filling 64 KB of LDS; nbytes counts the bytes read from LDS."""
+
+    def __init__(self, dev, lib, grid, threads, iters=4000):
+        super().__init__(dev, lib)
+        self.grid, self.threads, self.iters = grid, threads, iters
+        self.nbytes = grid * threads * 16 * 4 * iters
+        self.out = self.torch.zeros(grid * threads, dtype=self.torch.int32, device=dev)
+        self.name = "lds_read_%dx%d" % (grid, threads)
+
+    def step(self, i):
+        self.call(self.lib.floor_lds_read(self.grid, self.threads, self.iters, self.out.data_ptr(), self.stream()))
+
+
 class FloorGather(Floor):
     """The paged int8 workload's K and V blocks (2 KB: 16 tokens of one KV head) read through
     its page table with plain 16-byte loads, in the order (sequence, KV head, page); workgroup
@@ -945,17 +961,21 @@ def run_floors(dev, a):
               lambda: FloorStream(dev, lib, kv, grid=1024),
               lambda: FloorStream(dev, lib, kv, merge=(16, 8)), lambda: FloorStream(dev, lib, kv, merge=(32, 8)),
               lambda: FloorGather(dev, lib, 256), lambda: FloorGather(dev, lib, 128),
-              lambda: FloorGather(dev, lib, 64)]
+              lambda: FloorGather(dev, lib, 64), lambda: FloorLds(dev, lib, 256, 512),
+              lambda: FloorLds(dev, lib, 256, 1024), lambda: FloorLds(dev, lib, 512, 512)]
     rows = []
     for mk in probes:
         f = mk()
         log("floor %s" % f.name)
         ms, per = time_steps(f, a.steps, a.warmup, graph=True, repeats=a.repeats)
         us = ms * 1e3
-        rows.append({"probe": f.name, "grid": f.grid, "bytes_per_launch": f.nbytes,
-                     "us_per_launch": round(us, 3),
-                     "TB_per_s": round(f.nbytes / (us * 1e-6) / 1e12, 3) if f.nbytes else None,
-                     "us_each_replay": [round(x * 1e3, 3) for x in per]})
+        row = {"probe": f.name, "grid": f.grid, "bytes_per_launch": f.nbytes,
+               "us_per_launch": round(us, 3),
+               "TB_per_s": round(f.nbytes / (us * 1e-6) / 1e12, 3) if f.nbytes else None,
+               "us_each_replay": [round(x * 1e3, 3) for x in per]}
+        if isinstance(f, FloorLds):     # bytes per clock per compute unit at 2.4 GHz
+            row["B_per_clk_per_CU"] = round(f.nbytes / (us * 1e-6) / 2.4e9 / 256, 1)
+        rows.append(row)
         del f
         torch.cuda.empty_cache()
     kernels = {}

@@ -20,7 +20,7 @@ def L():
 
 
 def test_exports_and_links_no_torch(L):
-    for n in ("floor_empty", "floor_stream", "floor_stream_merge", "floor_gather"):
+    for n in ("floor_empty", "floor_stream", "floor_stream_merge", "floor_gather", "floor_lds_read"):
         assert hasattr(L, n), n
     out = os.popen("ldd %s" % PATH).read()
     assert "torch" not in out and "c10" not in out
@@ -55,3 +55,10 @@ def test_gather_refuses_bad_pools(L):
     assert L.floor_gather(P, P, P, 0, 4, 100, P, None) == -1         # no blocks
     assert L.floor_gather(P + 8, P, P, 10, 4, 100, P, None) == -1    # misaligned k
     assert L.floor_gather(P, P, P, 10 ** 8, 1, 100, P, None) == -1   # grid beyond 65535
+
+
+def test_lds_read_refuses_bad_shapes(L):
+    assert L.floor_lds_read(256, 384, 10, P, None) == -1      # threads not built
+    assert L.floor_lds_read(0, 512, 10, P, None) == -1
+    assert L.floor_lds_read(256, 512, 0, P, None) == -1
+    assert L.floor_lds_read(256, 512, 10, None, None) == -1

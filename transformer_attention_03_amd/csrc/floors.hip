@@ -4,7 +4,8 @@
 // merge of the split-KV kernel's shape (device-scope partial stores, a wait for their
 // completion, an arrival counter, the last workgroup reading every partial back), and a
 // read of randomly placed 2 KB blocks through a page table (the paged int8 cache's K and V
-// blocks).  Measurement probes: they compute nothing of the attention method, and the
+// blocks), and the LDS read bandwidth that the forward kernels' fragment reads draw on.
+// Measurement probes: they compute nothing of the attention method, and the
 // attention library neither links nor calls them.  Built into libattn_floors.so.
 //
 // Every entry point validates its sizes on the host, and every kernel bounds its accesses
@@ -119,6 +120,31 @@ __global__ void __launch_bounds__(kThreads) floor_gather_kernel(const uint4* __r
     if ((threadIdx.x & 63) == 0) sink[blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6)] = (float)(a & 0xffff);
 }
 
+// LDS read bandwidth: each workgroup fills 64 KB of LDS, then every lane reads 16 bytes per
+// ds_read_b128 (consecutive lanes at consecutive 16-byte slots: no bank conflicts), four reads
+// per iteration, for iters iterations.
+template <int NT>
+__global__ void __launch_bounds__(NT) floor_lds_kernel(uint32_t* __restrict__ out, int iters) {
+    __shared__ __attribute__((aligned(16))) uint4 buf[4096];
+    for (int i = threadIdx.x; i < 4096; i += NT) buf[i] = make_uint4(i, i + 1, i + 2, i + 3);
+    __syncthreads();
+    uint4 a = make_uint4(0, 0, 0, 0), b = a, c = a, d = a;
+    const int base = threadIdx.x & 4095;
+    for (int it = 0; it < iters; ++it) {
+        const int o = (it * 256) & 4095;
+        const uint4 x0 = buf[(base + o) & 4095];
+        const uint4 x1 = buf[(base + o + 64) & 4095];
+        const uint4 x2 = buf[(base + o + 128) & 4095];
+        const uint4 x3 = buf[(base + o + 192) & 4095];
+        a.x ^= x0.x; a.y ^= x0.y; a.z ^= x0.z; a.w ^= x0.w;
+        b.x ^= x1.x; b.y ^= x1.y; b.z ^= x1.z; b.w ^= x1.w;
+        c.x ^= x2.x; c.y ^= x2.y; c.z ^= x2.z; c.w ^= x2.w;
+        d.x ^= x3.x; d.y ^= x3.y; d.z ^= x3.z; d.w ^= x3.w;
+    }
+    out[(long)blockIdx.x * NT + threadIdx.x] =
+        a.x ^ a.y ^ a.z ^ a.w ^ b.x ^ b.y ^ b.z ^ b.w ^ c.x ^ c.y ^ c.z ^ c.w ^ d.x ^ d.y ^ d.z ^ d.w;
+}
+
 int status(hipError_t e) { return e == hipSuccess ? 0 : -4; }
 
 }  // namespace
@@ -168,6 +194,22 @@ int floor_gather(const void* k, const void* v, const uint32_t* blocks, int n, in
     if (grid > 65535) return -1;
     hipLaunchKernelGGL(floor_gather_kernel, dim3((unsigned)grid), dim3(kThreads), 0, (hipStream_t)stream,
                        (const uint4*)k, (const uint4*)v, blocks, n, per_wg, (uint32_t)pool_blocks, sink);
+    return status(hipGetLastError());
+}
+
+// LDS reads of 64 * 16 bytes per wave-instruction: grid workgroups of threads (256, 512 or
+// 1024) threads, 4 * iters reads per lane.  out: grid * threads uint32.
+int floor_lds_read(int grid, int threads, int iters, uint32_t* out, void* stream) {
+    if (!out || grid < 1 || grid > 65535 || iters < 1) return -1;
+    const hipStream_t st = (hipStream_t)stream;
+    if (threads == 256)
+        hipLaunchKernelGGL(floor_lds_kernel<256>, dim3(grid), dim3(256), 0, st, out, iters);
+    else if (threads == 512)
+        hipLaunchKernelGGL(floor_lds_kernel<512>, dim3(grid), dim3(512), 0, st, out, iters);
+    else if (threads == 1024)
+        hipLaunchKernelGGL(floor_lds_kernel<1024>, dim3(grid), dim3(1024), 0, st, out, iters);
+    else
+        return -1;
     return status(hipGetLastError());
 }
 
