@@ -110,3 +110,45 @@ def test_tiered_dtypes():
         ta.attn_decode_tiered_q8(a["q"][0], hk, hk, a["kp"], a["vp"], a["ks"], a["vs"],
                                  a["pt"][0].long(), a["o"][0], a["ws"], cold_len=16, hot_len=8,
                                  hot_start=0, scale=0.125)
+
+
+def test_tiered_packed_and_f16_dtypes():
+    hk = z((2, 32, 64), "float16")
+    q, o = z((8, 64), "float32"), z((8, 64), "float32")
+    ck8, cs = z((2, 40, 64), "int8"), z((2, 40), "float32")
+    with pytest.raises(ValueError, match="cold_k must be int8"):
+        ta.attn_decode_tiered_q8_packed(q, hk, hk, ck8.float(), ck8, cs, cs, o, ws(), cold_len=16, hot_len=8,
+                                        hot_start=0, scale=0.125)
+    with pytest.raises(ValueError, match="cold_v_scales must be float32"):
+        ta.attn_decode_tiered_q8_packed(q, hk, hk, ck8, ck8, cs, cs.half(), o, ws(), cold_len=16, hot_len=8,
+                                        hot_start=0, scale=0.125)
+    with pytest.raises(ValueError, match="must be on a GPU"):
+        ta.attn_decode_tiered_q8_packed(q, hk, hk, ck8, ck8, cs, cs, o, ws(), cold_len=16, hot_len=8,
+                                        hot_start=0, scale=0.125)
+    ck16 = z((2, 40, 64), "float16")
+    with pytest.raises(ValueError, match="cold_k must be float16"):
+        ta.attn_decode_tiered_f16(q, hk, hk, ck16.float(), ck16, None, o, ws(), cold_len=16, hot_len=8,
+                                  hot_start=0, scale=0.125)
+    with pytest.raises(ValueError, match="cold_page_table must be int32"):
+        ta.attn_decode_tiered_f16(q, hk, hk, z((3, 2, 16, 64), "float16"), z((3, 2, 16, 64), "float16"),
+                                  z((3,), "int64"), o, ws(), cold_len=16, hot_len=8, hot_start=0, scale=0.125)
+    with pytest.raises(ValueError, match="must be on a GPU"):
+        ta.attn_decode_tiered_f16(q, hk, hk, ck16, ck16, None, o, ws(), cold_len=16, hot_len=8,
+                                  hot_start=0, scale=0.125)
+
+
+def test_block_local_and_noalloc_dtypes():
+    x = z((24, 2, 128), "float32")
+    kv = z((36, 2, 128), "float32")
+    pos = z((13, 2, 128), "float32")
+    with pytest.raises(ValueError, match="q_pad must be float32"):
+        ta.attn_block_local(x.half(), kv, kv, pos, x, seq=20, chunk_size=12, max_past=12, max_future=0)
+    with pytest.raises(ValueError, match="pos_proj must be float32"):
+        ta.attn_block_local(x, kv, kv, pos.half(), x, seq=20, chunk_size=12, max_past=12, max_future=0)
+    with pytest.raises(ValueError, match="must be on a GPU"):
+        ta.attn_block_local(x, kv, kv, pos, x, seq=20, chunk_size=12, max_past=12, max_future=0)
+    q, k = z((8, 64), "float32"), z((2, 32, 64), "float16")
+    with pytest.raises(ValueError, match="k must be float16"):
+        ta.attn_decode_noalloc(q, k.float(), k, q.clone(), scale=0.125)
+    with pytest.raises(ValueError, match="must be on a GPU"):
+        ta.attn_decode_noalloc(q, k, k, q.clone(), scale=0.125)
