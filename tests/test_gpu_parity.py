@@ -537,6 +537,45 @@ def test_paged_permutation_is_bit_identical(dev):
     assert maxabs(oa, paged_oracle(a)) < TOL_F16
 
 
+def test_paged_identity_table_equals_random_placement(dev):
+    """The same logical pages stored in order (sequence b's page i at physical page
+    start_b + i) and at seeded random places give bitwise identical outputs."""
+    say("paged identity table")
+    lens = [1500, 33, 4096]
+    a = synth.paged_inputs(synth.seed_of(5) + 101, 3, 32, 8, 128, lens, n_poison=8)
+    ident = dict(a)
+    n_live = [(n + 15) // 16 for n in lens]
+    P = sum(n_live)
+    kp, vp = np.full_like(a["k_pages"][:P], -128), np.full_like(a["v_pages"][:P], -128)
+    ks, vs = np.full_like(a["k_scales"][:P], np.nan), np.full_like(a["v_scales"][:P], np.nan)
+    table = np.full_like(a["page_table"], -1)
+    start = 0
+    for b, n in enumerate(n_live):
+        for i in range(n):
+            src = a["page_table"][b, i]
+            kp[start + i], vp[start + i] = a["k_pages"][src], a["v_pages"][src]
+            ks[start + i], vs[start + i] = a["k_scales"][src], a["v_scales"][src]
+            table[b, i] = start + i
+        start += n
+    ident.update(k_pages=kp, v_pages=vp, k_scales=ks, v_scales=vs, page_table=table)
+    assert np.array_equal(run_paged(dev, a).view(np.uint32), run_paged(dev, ident).view(np.uint32))
+
+
+def test_paged_int8_equals_f16_decode_on_dequantised_values(dev):
+    """Cross-entry check: the int8 paged decode of a sequence and the contiguous f16 decode
+    of the same rows dequantised (then rounded to f16) agree within the f16 tolerance."""
+    say("paged int8 vs f16 decode")
+    lens = [3000, 700]
+    d = synth.paged_inputs(synth.seed_of(5) + 103, 2, 32, 8, 128, lens)
+    got = run_paged(dev, d)
+    for b in range(2):
+        k16 = oracle.dequant_i8(d["k_q"][b], d["k_s"][b]).astype(np.float16)   # [L, Hkv, D]
+        v16 = oracle.dequant_i8(d["v_q"][b], d["v_s"][b]).astype(np.float16)
+        ref, _ = run_decode(dev, d["q"][b], np.ascontiguousarray(np.transpose(k16, (1, 0, 2))),
+                            np.ascontiguousarray(np.transpose(v16, (1, 0, 2))))
+        assert maxabs(got[b], ref) < TOL_F16, b
+
+
 def test_paged_negative_control_detects_mis_indexing(dev):
     """A wrong page-table entry must show up.  One query sees every key, so the result is
     invariant to the ORDER of its pages; the controls therefore (a) point a logical page at
