@@ -3,6 +3,7 @@ declares, and rejects invalid arguments on the host (before any HIP call) with t
 documented status codes and messages."""
 import ctypes
 import os
+import subprocess
 import re
 
 import pytest
@@ -41,9 +42,10 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_library_links_no_torch():
-    out = os.popen("ldd %s" % ta.LIB_PATH).read()
-    assert "torch" not in out and "c10" not in out
-    assert "amdhip64" in out
+    r = subprocess.run(["ldd", ta.LIB_PATH], capture_output=True, text=True, timeout=60)
+    assert r.returncode == 0, r.stderr
+    assert "torch" not in r.stdout and "c10" not in r.stdout
+    assert "amdhip64" in r.stdout, r.stdout + r.stderr
 
 
 def prefill(**kw):
