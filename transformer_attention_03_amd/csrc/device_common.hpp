@@ -72,6 +72,41 @@ __device__ __forceinline__ float group_sum(float x) {
     return x;
 }
 
+// Max over aligned groups of 16 lanes (one DPP row); every lane gets the max.
+__device__ __forceinline__ float group_max16(float x) {
+    x = fmaxf(x, dpp_f<kDppXor1>(x));
+    x = fmaxf(x, dpp_f<kDppXor2>(x));
+    x = fmaxf(x, dpp_f<kDppHalfMirror>(x));
+    return fmaxf(x, dpp_f<kDppMirror>(x));
+}
+
+// Lane n of each row of 16 lanes, to every lane of that row (DPP row_newbcast).  n must be a
+// compile-time constant after inlining and unrolling (the switch then folds to one case).
+template <int N>
+__device__ __forceinline__ float row_bcast16_c(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x150 + N, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float row_bcast16(float x, int n) {
+    switch (n & 15) {
+        case 0: return row_bcast16_c<0>(x);
+        case 1: return row_bcast16_c<1>(x);
+        case 2: return row_bcast16_c<2>(x);
+        case 3: return row_bcast16_c<3>(x);
+        case 4: return row_bcast16_c<4>(x);
+        case 5: return row_bcast16_c<5>(x);
+        case 6: return row_bcast16_c<6>(x);
+        case 7: return row_bcast16_c<7>(x);
+        case 8: return row_bcast16_c<8>(x);
+        case 9: return row_bcast16_c<9>(x);
+        case 10: return row_bcast16_c<10>(x);
+        case 11: return row_bcast16_c<11>(x);
+        case 12: return row_bcast16_c<12>(x);
+        case 13: return row_bcast16_c<13>(x);
+        case 14: return row_bcast16_c<14>(x);
+        default: return row_bcast16_c<15>(x);
+    }
+}
+
 // Integer sum over the wave (every lane gets it) and inclusive prefix sum by lane.
 __device__ __forceinline__ int wave_sum_i(int x) {
 #pragma unroll
