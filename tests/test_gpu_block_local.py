@@ -49,6 +49,10 @@ def run_case(dev, seq, chunk, past, future, H, cap, seed):
     (1000, 25, 14, 14, 3, 20.0),
     (3, 40, 2, 0, 2, 0.0),           # padding queries past seq + max_past see no key: zeros
     (4096, 12, 12, 0, 8, 50.0),
+    (300, 8, 10, 5, 2, 0.0),         # span 16: one round of 16 offsets exactly
+    (129, 6, 16, 0, 3, 5.0),         # span 17: a second round of offsets, 32-row workgroups
+    (500, 10, 12, 7, 4, 30.0),       # span 20: the widest span of 32-row workgroups
+    (7, 3, 2, 1, 2, 0.0),            # 9 padded rows: the last group's second row is past the end
 ])
 def test_block_local(dev, seq, chunk, past, future, H, cap):
     print("block-local seq=%d chunk=%d past=%d future=%d H=%d cap=%g" % (seq, chunk, past, future, H, cap),
