@@ -33,7 +33,10 @@ namespace ta03 {
 namespace {
 
 constexpr int kBlD = 128;                 // head_dim (the pages fix it)
-constexpr int kBlStride = kBlD + 4;       // LDS row stride in floats (shifts rows across banks)
+constexpr int kBlStride = kBlD;           // LDS row stride in floats: unpadded rows read without bank
+                                          // conflicts here (a group reads a contiguous 256-byte half
+                                          // row; the groups of a wave, rows two apart); a 4-float pad
+                                          // or a per-group chunk swizzle cost a third of the LDS cycles
 constexpr int kBlMaxSpan = 29;            // past + future + 1 <= 29: the K and V windows of 16
                                           // queries and the pos_proj rows fit 64 KB of LDS
 constexpr int kBlWideSpan = 20;           // spans up to 20 run 32 queries per workgroup
