@@ -52,6 +52,9 @@ constexpr int kTB = 16;                  // tokens per block: one MFMA tile
 constexpr int kLdsBudget = 136 * 1024;   // ring bytes per workgroup
 constexpr int kMaxSplits = 256;          // split partials merged per (sequence, head)
 constexpr int kMaxSplitTokens = 4096;    // paged: tokens per workgroup (page slice in LDS)
+constexpr int kMergePad = 4;             // floats after each head's row of the wave-merge buffer:
+                                         // a wave's writer lanes store the rows of its heads at
+                                         // once, and unpadded rows would put them in the same banks
 
 template <int D, bool PAGED>
 struct DecShape {
@@ -504,7 +507,7 @@ __device__ __forceinline__ void split_partial(const DecodeParams& a, const TierS
     constexpr int QXN = qx_entries<PAGED>();
     const int lane = threadIdx.x & 63;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    float(*lds_o)[GC][D] = reinterpret_cast<float(*)[GC][D]>(rings);                    // [NW][GC][D]
+    float(*lds_o)[GC][D + kMergePad] = reinterpret_cast<float(*)[GC][D + kMergePad]>(rings);   // [NW][GC][D + pad]
 
     RowCtx c;
     c.kbase = reinterpret_cast<const char*>(src.k);
@@ -794,7 +797,7 @@ __global__ void __launch_bounds__((DecShape<D, PAGED>::NT)) decode_split_kernel(
     __shared__ int lds_last;
     __shared__ __attribute__((aligned(1024))) half8_t lds_qx[S::KC][qx_entries<PAGED>()];
     __shared__ float lds_qs[S::KC][64];
-    static_assert(sizeof(float) * NW * GC * D <= NW * S::WAVE_LDS, "merge buffer fits in the rings");
+    static_assert(sizeof(float) * NW * GC * (D + kMergePad) <= NW * S::WAVE_LDS, "merge buffer fits in the rings");
 
     const int lane = threadIdx.x & 63;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -925,7 +928,7 @@ __global__ void __launch_bounds__((DecShape<D, true>::NT)) decode_tiered_kernel(
     __shared__ int lds_last;
     __shared__ __attribute__((aligned(1024))) half8_t lds_qx[SP::KC][qx_entries<false>()];   // both bodies
     __shared__ float lds_qs[SP::KC][64];
-    static_assert(sizeof(float) * SP::NW * GC * D <= RB, "merge buffer fits in the rings");
+    static_assert(sizeof(float) * SP::NW * GC * (D + kMergePad) <= RB, "merge buffer fits in the rings");
     constexpr int CS = (RB / 4) / (GC * (D + 2)) > kMaxSplits ? kMaxSplits : (RB / 4) / (GC * (D + 2));
 
     const int G = a.H / a.Hkv;
