@@ -8,7 +8,10 @@ synthetic generators' as everywhere else.
 - paged int8 decode whose page pool holds 140,000 pages (K and V pools 2.29 GB each), the
   live pages of two sequences scattered over it by the seeded permutation, the rest poison;
 - a 64-token prefill chunk at the end of a 1,200,000-position f16 cache (K and V 2.46 GB;
-  positions from 1,048,576 on lie past 2^31 bytes).
+  positions from 1,048,576 on lie past 2^31 bytes);
+- Conformer block-local attention over 540,000 frames of 8 heads (q, K, V and the output
+  2.21 GB each, f32; frames from 524,288 on lie past 2^31 bytes), checked on slices of 120
+  frames that the oracle takes as sequences of their own.
 """
 import math
 
@@ -124,3 +127,33 @@ def test_prefill_chunk_beyond_2gib(dev):
             want = oracle.attention(q[None, :, h:h + 1], kk, vv, causal=True,
                                     scale=1 / math.sqrt(D))[0, :, 0]
             assert maxabs(got[:, h], want) < TOL_F16, h
+
+
+def test_block_local_beyond_2gib(dev):
+    seq, chunk, past, future, H, cap = 540000, 12, 12, 0, 8, 50.0
+    say("max size: block-local seq=%d chunk=%d past=%d future=%d H=%d" % (seq, chunk, past, future, H))
+    d = synth.block_local_inputs(synth.seed_of(10) + 3, seq, chunk, past, future, H)
+    q, k, v, pos = d["q"], d["k"], d["v"], d["pos"]
+    assert q.nbytes > (1 << 31) and k.nbytes > (1 << 31)
+    qd, kd, vd = (torch.from_numpy(x).to(dev) for x in (q, k, v))
+    od = torch.empty_like(qd)
+    ta.attn_block_local(qd, kd, vd, torch.from_numpy(pos).to(dev), od, seq=seq, chunk_size=chunk,
+                        max_past=past, max_future=future, logit_cap=cap)
+    torch.cuda.synchronize()
+    got = od.cpu().numpy()
+    del qd, kd, vd, od
+    release()
+    assert np.all(np.isfinite(got))
+    # Frames [f0, f0 + n) as a sequence of their own (f0 and n multiples of the chunk): a row
+    # whose key window lies inside the slice has the same output as in the full call.
+    n = 120
+    row_bytes = H * 128 * 4
+    for f0 in (0, 264000, 524280, 529992, d["padded_len"] - n):
+        assert f0 % chunk == 0
+        want = oracle.block_local(q[f0:f0 + n], k[f0:f0 + n + past + future], v[f0:f0 + n + past + future],
+                                  pos, seq=min(n, seq - f0), chunk_size=chunk, max_past=past,
+                                  max_future=future, logit_cap=cap)
+        lo = 0 if f0 == 0 else past + future
+        assert maxabs(got[f0 + lo:f0 + n], want[lo:]) < 1e-4, f0
+        if f0 >= 524280:
+            assert (f0 + n) * row_bytes > (1 << 31)
