@@ -63,8 +63,12 @@ __global__ void __launch_bounds__(64 * NW) fwd_f16_kernel(FwdParams a) {
     const char* kg_ptr = reinterpret_cast<const char*>(reinterpret_cast<const _Float16*>(a.k) + (long)kvh * a.k_head);
     const char* vg = reinterpret_cast<const char*>(reinterpret_cast<const _Float16*>(a.v) + (long)kvh * a.k_head);
 
-    DmaLane<D, QB, NW, NS, BN> dl;
-    dma_lane_init(dl, a, w, lane);
+    // The tiles of key group kg are loaded by that group's NW / KS waves alone, so a wave
+    // forms the address of one tile per iteration instead of KS (scalar arithmetic that all
+    // waves of a compute unit otherwise share one scalar unit for).
+    constexpr int NWT = NW / KS;
+    DmaLane<D, QB, NWT, NS, BN> dl;
+    dma_lane_init(dl, a, w % NWT, lane);
 
     // Tiles are visited from a starting point that depends on the query block, so that the
     // workgroups of one head do not all fetch the same tile at the same moment (each would
@@ -77,11 +81,9 @@ __global__ void __launch_bounds__(64 * NW) fwd_f16_kernel(FwdParams a) {
     // kt0 + i KS + j, j < KS, one per key group)
 #pragma unroll
     for (int st0 = 0; st0 < NS - 1; ++st0)
-#pragma unroll
-        for (int j = 0; j < KS; ++j)
-            if (tr.kt0 + st0 * KS + j < tr.kt1)
-                f16_dma_tile<D, QB, NW, NS, BN>(a, kg_ptr, vg, dl, tile_key(tr.kt0 + st0 * KS + j), w, lane,
-                                                k_lds[st0][j], v_lds[st0][j]);
+        if (tr.kt0 + st0 * KS + kg < tr.kt1)
+            f16_dma_tile<D, QB, NWT, NS, BN>(a, kg_ptr, vg, dl, tile_key(tr.kt0 + st0 * KS + kg), w % NWT, lane,
+                                             k_lds[st0][kg], v_lds[st0][kg]);
 
     // ---- Q fragments (B operand of S^T = K Q^T) --------------------------------------------
     half8_t qf[S::QB][S::DC];
@@ -182,11 +184,9 @@ __global__ void __launch_bounds__(64 * NW) fwd_f16_kernel(FwdParams a) {
         {
             const int nxt = it + NS - 1;
             const int sn = (stage + NS - 1) % NS;
-#pragma unroll
-            for (int j = 0; j < KS; ++j)
-                if (tr.kt0 + nxt * KS + j < tr.kt1)
-                    f16_dma_tile<D, QB, NW, NS, BN>(a, kg_ptr, vg, dl, tile_key(tr.kt0 + nxt * KS + j), w, lane,
-                                                    k_lds[sn][j], v_lds[sn][j]);
+            if (tr.kt0 + nxt * KS + kg < tr.kt1)
+                f16_dma_tile<D, QB, NWT, NS, BN>(a, kg_ptr, vg, dl, tile_key(tr.kt0 + nxt * KS + kg), w % NWT, lane,
+                                                 k_lds[sn][kg], v_lds[sn][kg]);
         }
         const int kt = tr.kt0 + it * KS + kg;
         if ((KS == 1 || kt < tr.kt1) && wave_sees(tile_key(kt))) {
