@@ -830,7 +830,9 @@ def floors_lib():
     L.floor_stream_merge.argtypes = [vp, l, i, i, vp, vp, vp, vp]
     L.floor_gather.argtypes = [vp, vp, vp, i, i, l, vp, vp]
     L.floor_lds_read.argtypes = [i, i, i, vp, vp]
-    for f in (L.floor_empty, L.floor_stream, L.floor_stream_merge, L.floor_gather, L.floor_lds_read):
+    L.floor_lds_read64.argtypes = [i, i, i, vp, vp]
+    for f in (L.floor_empty, L.floor_stream, L.floor_stream_merge, L.floor_gather, L.floor_lds_read,
+              L.floor_lds_read64):
         f.restype = i
     return L
 
@@ -912,6 +914,21 @@ class FloorLds(Floor):
         self.call(self.lib.floor_lds_read(self.grid, self.threads, self.iters, self.out.data_ptr(), self.stream()))
 
 
+class FloorLds64(Floor):
+    """LDS reads of 8 bytes per lane, plain or transposing (the V^T operand reads of the
+    forward kernels): `grid` workgroups of 512 threads, 4 * iters reads per lane."""
+
+    def __init__(self, dev, lib, grid, tr, iters=4000):
+        super().__init__(dev, lib)
+        self.grid, self.tr, self.iters, self.threads = grid, tr, iters, 512
+        self.nbytes = grid * 512 * 8 * 4 * iters
+        self.out = self.torch.zeros(grid * 512, dtype=self.torch.int32, device=dev)
+        self.name = "lds_read%s_b64_%dx512" % ("_tr16" if tr else "", grid)
+
+    def step(self, i):
+        self.call(self.lib.floor_lds_read64(self.grid, self.tr, self.iters, self.out.data_ptr(), self.stream()))
+
+
 class FloorGather(Floor):
     """The paged int8 workload's K and V blocks (2 KB: 16 tokens of one KV head) read through
     its page table with plain 16-byte loads, in the order (sequence, KV head, page); workgroup
@@ -962,7 +979,8 @@ def run_floors(dev, a):
               lambda: FloorStream(dev, lib, kv, merge=(16, 8)), lambda: FloorStream(dev, lib, kv, merge=(32, 8)),
               lambda: FloorGather(dev, lib, 256), lambda: FloorGather(dev, lib, 128),
               lambda: FloorGather(dev, lib, 64), lambda: FloorLds(dev, lib, 256, 512),
-              lambda: FloorLds(dev, lib, 256, 1024), lambda: FloorLds(dev, lib, 512, 512)]
+              lambda: FloorLds(dev, lib, 256, 1024), lambda: FloorLds(dev, lib, 512, 512),
+              lambda: FloorLds64(dev, lib, 256, 0), lambda: FloorLds64(dev, lib, 256, 1)]
     rows = []
     for mk in probes:
         f = mk()
@@ -973,7 +991,7 @@ def run_floors(dev, a):
                "us_per_launch": round(us, 3),
                "TB_per_s": round(f.nbytes / (us * 1e-6) / 1e12, 3) if f.nbytes else None,
                "us_each_replay": [round(x * 1e3, 3) for x in per]}
-        if isinstance(f, FloorLds):     # bytes per clock per compute unit at 2.4 GHz
+        if isinstance(f, (FloorLds, FloorLds64)):     # bytes per clock per compute unit at 2.4 GHz
             row["B_per_clk_per_CU"] = round(f.nbytes / (us * 1e-6) / 2.4e9 / 256, 1)
         rows.append(row)
         del f

@@ -20,7 +20,8 @@ def L():
 
 
 def test_exports_and_links_no_torch(L):
-    for n in ("floor_empty", "floor_stream", "floor_stream_merge", "floor_gather", "floor_lds_read"):
+    for n in ("floor_empty", "floor_stream", "floor_stream_merge", "floor_gather", "floor_lds_read",
+              "floor_lds_read64"):
         assert hasattr(L, n), n
     out = os.popen("ldd %s" % PATH).read()
     assert "torch" not in out and "c10" not in out
@@ -62,3 +63,10 @@ def test_lds_read_refuses_bad_shapes(L):
     assert L.floor_lds_read(0, 512, 10, P, None) == -1
     assert L.floor_lds_read(256, 512, 0, P, None) == -1
     assert L.floor_lds_read(256, 512, 10, None, None) == -1
+
+
+def test_lds_read64_refuses_bad_modes(L):
+    assert L.floor_lds_read64(256, 2, 10, P, None) == -1      # neither plain nor transposing
+    assert L.floor_lds_read64(0, 0, 10, P, None) == -1
+    assert L.floor_lds_read64(256, 1, 0, P, None) == -1
+    assert L.floor_lds_read64(256, 0, 10, None, None) == -1

@@ -145,6 +145,42 @@ __global__ void __launch_bounds__(NT) floor_lds_kernel(uint32_t* __restrict__ ou
         a.x ^ a.y ^ a.z ^ a.w ^ b.x ^ b.y ^ b.z ^ b.w ^ c.x ^ c.y ^ c.z ^ c.w ^ d.x ^ d.y ^ d.z ^ d.w;
 }
 
+// LDS reads of 8 bytes per lane (the width of the transposing reads that feed the V^T operand
+// of the forward kernels' P.V products): TR 0 plain ds_read_b64, TR 1 ds_read_b64_tr_b16.
+// Lane l reads the 8 bytes at 8 l of a 512-byte span (no bank conflicts for the plain read),
+// four spans per iteration; 512 threads.
+template <int TR>
+__global__ void __launch_bounds__(512) floor_lds64_kernel(uint32_t* __restrict__ out, int iters) {
+    typedef short s4_t __attribute__((ext_vector_type(4)));
+    __shared__ __attribute__((aligned(16))) uint4 buf[4096];
+    for (int i = threadIdx.x; i < 4096; i += 512) buf[i] = make_uint4(i, i + 1, i + 2, i + 3);
+    __syncthreads();
+    const char* base = reinterpret_cast<const char*>(buf);
+    const int lane = threadIdx.x & 63;
+    const int wofs = (threadIdx.x >> 6) * 512;
+    uint32_t a = 0, b = 0, c = 0, d = 0;
+    for (int it = 0; it < iters; ++it) {
+        const int o = (it * 2048 + wofs) & 65535;
+        uint2 x[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const char* addr = base + ((o + 512 * u) & 65535) + 8 * lane;
+            if constexpr (TR == 1) {
+                const s4_t w = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (__attribute__((address_space(3))) s4_t*)(uint32_t)(uintptr_t)addr);
+                x[u] = __builtin_bit_cast(uint2, w);
+            } else {
+                x[u] = *reinterpret_cast<const uint2*>(addr);
+            }
+        }
+        a ^= x[0].x ^ x[0].y;
+        b ^= x[1].x ^ x[1].y;
+        c ^= x[2].x ^ x[2].y;
+        d ^= x[3].x ^ x[3].y;
+    }
+    out[(long)blockIdx.x * 512 + threadIdx.x] = a ^ b ^ c ^ d;
+}
+
 int status(hipError_t e) { return e == hipSuccess ? 0 : -4; }
 
 }  // namespace
@@ -194,6 +230,18 @@ int floor_gather(const void* k, const void* v, const uint32_t* blocks, int n, in
     if (grid > 65535) return -1;
     hipLaunchKernelGGL(floor_gather_kernel, dim3((unsigned)grid), dim3(kThreads), 0, (hipStream_t)stream,
                        (const uint4*)k, (const uint4*)v, blocks, n, per_wg, (uint32_t)pool_blocks, sink);
+    return status(hipGetLastError());
+}
+
+// LDS reads of 64 * 8 bytes per wave-instruction, plain (tr 0) or transposing (tr 1): grid
+// workgroups of 512 threads, 4 * iters reads per lane.  out: grid * 512 uint32.
+int floor_lds_read64(int grid, int tr, int iters, uint32_t* out, void* stream) {
+    if (!out || grid < 1 || grid > 65535 || iters < 1 || (tr != 0 && tr != 1)) return -1;
+    const hipStream_t st = (hipStream_t)stream;
+    if (tr == 1)
+        hipLaunchKernelGGL(floor_lds64_kernel<1>, dim3(grid), dim3(512), 0, st, out, iters);
+    else
+        hipLaunchKernelGGL(floor_lds64_kernel<0>, dim3(grid), dim3(512), 0, st, out, iters);
     return status(hipGetLastError());
 }
 
