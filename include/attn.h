@@ -346,8 +346,11 @@ int attn_decode_tiered_f16(const float *q, const void *hot_k, const void *hot_v,
 
 /*
  * Workspace bytes needed by attn_decode (batch = 1) and attn_decode_paged_q8 for the
- * given shape (split partials and arrival counters).  Returns 0 for invalid sizes.
- * Honours the calling thread's split override (attn_set_decode_split).
+ * given shape (split partials and arrival counters).  Returns 0 for invalid sizes,
+ * including shapes whose query (batch * num_heads * head_dim) or cache (max_kv_len *
+ * num_kv_heads * head_dim) would exceed 2^40 elements, which the decode entry points refuse
+ * with ATTN_ERR_INVALID_ARG.  Honours the calling thread's split override
+ * (attn_set_decode_split).
  */
 size_t attn_decode_workspace_bytes(int batch, int num_heads, int num_kv_heads, int head_dim,
                                    int max_kv_len);

@@ -178,6 +178,7 @@ def paged(**kw):
     (dict(ws=None), ta.ATTN_ERR_WORKSPACE, "workspace"),
     (dict(wsb=1000), ta.ATTN_ERR_WORKSPACE, "smaller than"),
     (dict(cap=-2.0), ta.ATTN_ERR_INVALID_ARG, "attn_softcap"),
+    (dict(B=1 << 20, H=1 << 20, Hkv=1), ta.ATTN_ERR_INVALID_ARG, "query rows"),   # q of 2^47 floats
 ])
 def test_paged_validation(kw, code, msg):
     assert paged(**kw) == code
@@ -227,6 +228,23 @@ def test_workspace_bytes():
     assert ta.attn_decode_workspace_bytes(8, 32, 8, 128, 32768) > n
     assert ta.attn_decode_workspace_bytes(1, 30, 8, 128, 4096) == 0
     assert ta.attn_decode_workspace_bytes(1, 32, 8, 100, 4096) == 0
+
+
+@pytest.mark.parametrize("args", [
+    (2 ** 31 - 1, 2 ** 31 - 1, 1, 128, 2 ** 31 - 1),     # q of ~2^69 floats
+    (1 << 20, 1 << 20, 1, 256, 1 << 20),
+    (1, 8, 8, 128, 2 ** 31 - 1),                          # K of 2^41 elements
+])
+def test_workspace_bytes_refuses_shapes_no_buffer_can_hold(args):
+    """Shapes whose q (batch x heads x head_dim) or K would exceed 2^40 elements are refused
+    (0), so the size arithmetic never wraps to a small, allocatable number."""
+    assert ta.attn_decode_workspace_bytes(*args) == 0
+
+
+def test_workspace_bytes_grows_without_wrapping():
+    """Large but representable shapes give sizes that grow with the shape."""
+    sizes = [ta.attn_decode_workspace_bytes(b, 4096, 1, 128, 1 << 20) for b in (1, 64, 4096)]
+    assert all(n > 0 for n in sizes) and sizes[0] < sizes[1] < sizes[2]
 
 
 def test_split_override_sizes_workspace():

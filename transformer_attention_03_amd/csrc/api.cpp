@@ -69,6 +69,15 @@ int check_scalars(int sliding_window, float attn_softcap, float scale) {
 
 constexpr long kMaxElems = 1L << 40;
 
+// q and o hold rows * num_heads * head_dim elements; the split workspace is sized from the
+// same product, so capping it keeps every size computation far from overflow.
+int check_query_rows(long rows, int num_heads, int head_dim, const char* what) {
+    if (rows * num_heads * head_dim > kMaxElems)
+        return fail(ATTN_ERR_INVALID_ARG, "%s: %ld query rows of %d heads x %d is too large", what, rows,
+                    num_heads, head_dim);
+    return ATTN_OK;
+}
+
 // ---- decode split plan ----------------------------------------------------------------------
 
 struct DecodePlan {
@@ -322,6 +331,8 @@ size_t attn_decode_workspace_bytes(int batch, int num_heads, int num_kv_heads, i
     if (batch < 1 || num_heads < 1 || num_kv_heads < 1 || num_heads % num_kv_heads != 0 ||
         max_kv_len < 1 || (head_dim != 64 && head_dim != 128 && head_dim != 256))
         return 0;
+    if ((long)batch * num_heads * head_dim > kMaxElems || (long)max_kv_len * num_kv_heads * head_dim > kMaxElems)
+        return 0;
     return workspace_bytes_for(batch, num_heads, num_kv_heads, head_dim, max_kv_len);
 }
 
@@ -345,6 +356,7 @@ int attn_decode(const float* q, const void* k, const void* v, float* o, int num_
     TRY(check_scalars(sliding_window, attn_softcap, scale));
     if ((long)kv_len * num_kv_heads * head_dim > kMaxElems)
         return fail(ATTN_ERR_INVALID_ARG, "attn_decode: tensor too large");
+    TRY(check_query_rows(1, num_heads, head_dim, "attn_decode"));
     const int eff = (sliding_window > 0 && sliding_window < kv_len) ? sliding_window : kv_len;
     return run_decode_contiguous(q, k, v, o, num_heads, num_kv_heads, head_dim, kv_len, 0, eff,
                                  sliding_window, attn_softcap, scale, workspace, workspace_bytes,
@@ -363,6 +375,7 @@ int attn_decode_noalloc(const float* q, const void* k, const void* v, float* o, 
     if (kv_len < 1) return fail(ATTN_ERR_INVALID_ARG, "%s: invalid kv_len %d (must be >= 1)", what, kv_len);
     TRY(check_scalars(sliding_window, attn_softcap, scale));
     if ((long)kv_len * num_kv_heads * head_dim > kMaxElems) return fail(ATTN_ERR_INVALID_ARG, "%s: tensor too large", what);
+    TRY(check_query_rows(1, num_heads, head_dim, what));
     const int eff = (sliding_window > 0 && sliding_window < kv_len) ? sliding_window : kv_len;
     // the scratch needed by this call's plan (host arithmetic only, before any HIP call)
     const DecodePlan plan = plan_decode(1, num_heads, num_kv_heads, head_dim, eff, false);
@@ -398,6 +411,7 @@ int attn_decode_ring(const float* q, const void* k, const void* v, float* o, int
                     sliding_window, ring_len);
     if ((long)ring_len * num_kv_heads * head_dim > kMaxElems)
         return fail(ATTN_ERR_INVALID_ARG, "attn_decode_ring: tensor too large");
+    TRY(check_query_rows(1, num_heads, head_dim, "attn_decode_ring"));
     // visible keys: the newest E = (W > 0 ? W : ring_len) tokens
     const int span = sliding_window > 0 ? sliding_window : ring_len;
     const int eff = total_len < span ? total_len : span;
@@ -429,6 +443,7 @@ int attn_decode_paged_q8(const float* q, const int8_t* k_pages, const int8_t* v_
     TRY(check_scalars(sliding_window, attn_softcap, scale));
     if ((long)num_pages * page_size * num_kv_heads * head_dim > kMaxElems)
         return fail(ATTN_ERR_INVALID_ARG, "attn_decode_paged_q8: cache too large");
+    TRY(check_query_rows(batch, num_heads, head_dim, "attn_decode_paged_q8"));
     if ((long)max_pages_per_seq * page_size >
         (long)ta03::decode_max_splits() * ta03::decode_max_split_tokens_paged())
         return fail(ATTN_ERR_UNSUPPORTED,
@@ -504,6 +519,7 @@ int run_tiered(const char* what, const float* q, const void* hot_k, const void* 
         return fail(ATTN_ERR_INVALID_ARG, "%s: cold_len (%d) and hot_len (%d) must be >= 0", what, cold_len, hot_len);
     if ((long)cold_len + hot_len < 1 || (long)cold_len + hot_len > 0x7fffffffL - 16)
         return fail(ATTN_ERR_INVALID_ARG, "%s: cold_len + hot_len must be in [1, 2^31 - 17]", what);
+    TRY(check_query_rows(1, num_heads, head_dim, what));
     if (hot_len > 0) {
         TRY(check_ptr(hot_k, "hot_k"));
         TRY(check_ptr(hot_v, "hot_v"));
