@@ -196,3 +196,84 @@ def test_random_block_local(dev, i, cfg):
     got = o.cpu().numpy()
     assert np.all(np.isfinite(got))
     assert maxabs(got, want) < TOL_F32
+
+
+def ring_cases():
+    rng = np.random.default_rng(20260106)
+    out = []
+    for _ in range(N_CASES):
+        H, Hkv = heads(rng)
+        D = int(rng.choice([64, 128, 256]))
+        R = int(rng.integers(1, 2000))
+        total = int(rng.integers(1, 3 * R + 2))
+        W = 0 if rng.random() < 0.5 else int(rng.integers(1, R + 1))
+        out.append((H, Hkv, D, R, total, W, cap(rng)))
+    return out
+
+
+@pytest.mark.parametrize("i,cfg", list(enumerate(ring_cases())))
+def test_random_ring(dev, i, cfg):
+    H, Hkv, D, R, total, W, c = cfg
+    say("random ring %d: H=%d Hkv=%d D=%d R=%d total=%d W=%d cap=%g" % (i, H, Hkv, D, R, total, W, c))
+    q, k, v = synth.decode_inputs(synth.seed_of(25) + i, H, Hkv, D, total)
+    span = W if W > 0 else R
+    lo = max(0, total - span)
+
+    def ring(x):
+        r = np.full((Hkv, R, D), np.nan, dtype=x.dtype)     # rows of hidden positions stay NaN
+        for t in range(lo, total):
+            r[:, t % R] = x[:, t]
+        return r
+
+    qd, kd, vd = to_dev(q, dev), to_dev(ring(k), dev), to_dev(ring(v), dev)
+    od = torch.empty((H, D), dtype=torch.float32, device=dev)
+    ws = ta.decode_workspace(1, H, Hkv, D, R, dev)
+    ta.attn_decode_ring(qd, kd, vd, od, ws, total_len=total, scale=1 / math.sqrt(D), sliding_window=W,
+                        attn_softcap=c)
+    torch.cuda.synchronize()
+    got = od.cpu().numpy()
+    kk, vv = (np.transpose(x[:, lo:total], (1, 0, 2))[None] for x in (k, v))
+    want = oracle.attention(q[None, None], kk, vv, causal=True, softcap=c, scale=1 / math.sqrt(D))[0, 0]
+    assert np.all(np.isfinite(got))
+    assert maxabs(got, want) < TOL_F16
+
+
+def tiered_cases():
+    rng = np.random.default_rng(20260107)
+    out = []
+    for _ in range(N_CASES):
+        H, Hkv = heads(rng)
+        D = int(rng.choice([64, 128, 256]))
+        cold = int(rng.integers(0, 3000))
+        R = int(rng.integers(16, 1500))
+        hot = int(rng.integers(0 if cold > 0 else 1, R + 1))
+        hs = int(rng.integers(0, R))
+        W = 0 if rng.random() < 0.6 else int(rng.integers(1, cold + hot + 1))
+        out.append((H, Hkv, D, cold, hot, R, hs, W, cap(rng)))
+    return out
+
+
+@pytest.mark.parametrize("i,cfg", list(enumerate(tiered_cases())))
+def test_random_tiered_q8(dev, i, cfg):
+    H, Hkv, D, cold, hot, R, hs, W, c = cfg
+    say("random tiered q8 %d: H=%d Hkv=%d D=%d cold=%d hot=%d R=%d hs=%d W=%d cap=%g" % (i, H, Hkv, D, cold, hot,
+                                                                                         R, hs, W, c))
+    t = synth.tiered_inputs(synth.seed_of(26) + i, H, Hkv, D, cold, hot, R, hs, n_poison=5)
+    ct = t["cold"]
+    d = {n: to_dev(x, dev) for n, x in (("q", t["q"]), ("hk", t["ring_k"]), ("hv", t["ring_v"]),
+                                         ("kp", ct["k_pages"]), ("vp", ct["v_pages"]), ("ks", ct["k_scales"]),
+                                         ("vs", ct["v_scales"]), ("pt", ct["page_table"][0]))}
+    o = torch.empty((H, D), dtype=torch.float32, device=dev)
+    ws = ta.decode_workspace(1, H, Hkv, D, cold + hot, dev)
+    ta.attn_decode_tiered_q8(d["q"], d["hk"], d["hv"], d["kp"], d["vp"], d["ks"], d["vs"], d["pt"], o, ws,
+                             cold_len=cold, hot_len=hot, hot_start=hs, scale=1 / math.sqrt(D), sliding_window=W,
+                             attn_softcap=c)
+    torch.cuda.synchronize()
+    assert int(ws[-256:].sum().item()) == 0
+    got = o.cpu().numpy()
+    k = np.concatenate([oracle.dequant_i8(ct["k_q"][0], ct["k_s"][0]), t["hot_k"].astype(np.float64)])
+    v = np.concatenate([oracle.dequant_i8(ct["v_q"][0], ct["v_s"][0]), t["hot_v"].astype(np.float64)])
+    want = oracle.attention(t["q"][None, None], k[None], v[None], causal=True, window=W, softcap=c,
+                            scale=1 / math.sqrt(D))[0, 0]
+    assert np.all(np.isfinite(got))
+    assert maxabs(got, want) < TOL_F16
