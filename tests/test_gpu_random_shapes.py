@@ -277,3 +277,42 @@ def test_random_tiered_q8(dev, i, cfg):
                             scale=1 / math.sqrt(D))[0, 0]
     assert np.all(np.isfinite(got))
     assert maxabs(got, want) < TOL_F16
+
+
+def odd_group_cases():
+    """Query heads per KV head outside the powers of two (3, 5, 6, 7, 12, 16): the decode
+    kernels then run several head chunks per KV head, and the forward maps heads to KV heads
+    by integer division."""
+    rng = np.random.default_rng(20260108)
+    out = []
+    for i in range(20):
+        hkv = int(rng.choice([1, 2, 4]))
+        H = hkv * int(rng.choice([3, 5, 6, 7, 12, 16]))
+        D = int(rng.choice([64, 128, 256]))
+        fam = ["prefill", "decode", "paged", "ring", "tiered"][i % 5]
+        if fam == "prefill":
+            S = int(rng.integers(1, 200))
+            L = S + int(rng.integers(0, 100))
+            out.append((fam, (H, hkv, D, S, L, True, window(rng, L), cap(rng), "f16")))
+        elif fam == "decode":
+            L = int(rng.integers(1, 3000))
+            out.append((fam, (H, hkv, D, L, window(rng, L), cap(rng))))
+        elif fam == "paged":
+            lens = [int(x) for x in rng.integers(1, 2000, size=int(rng.integers(1, 4)))]
+            out.append((fam, (H, hkv, D, lens, window(rng, max(lens)), cap(rng))))
+        elif fam == "ring":
+            R = int(rng.integers(1, 1500))
+            out.append((fam, (H, hkv, D, R, int(rng.integers(1, 3 * R + 2)), 0, cap(rng))))
+        else:
+            cold, R = int(rng.integers(0, 2000)), int(rng.integers(16, 800))
+            hot = int(rng.integers(0 if cold > 0 else 1, R + 1))
+            out.append((fam, (H, hkv, D, cold, hot, R, int(rng.integers(0, R)), 0, cap(rng))))
+    return out
+
+
+@pytest.mark.parametrize("i,case", list(enumerate(odd_group_cases())))
+def test_random_odd_groups(dev, i, case):
+    fam, cfg = case
+    run = {"prefill": test_random_prefill, "decode": test_random_decode, "paged": test_random_paged,
+           "ring": test_random_ring, "tiered": test_random_tiered_q8}[fam]
+    run(dev, 100 + i, cfg)
