@@ -718,20 +718,27 @@ __device__ __forceinline__ void merge_splits(const DecodeParams& a, char* rings,
     if (!*lds_last) return;
 
     // The split partials (device-scope data) are pulled into LDS by DMA, CS splits at a
-    // time, and folded per (head, d) pair into a running maximum, weighted sum and
-    // normaliser.  Compact loops: this code runs once per (sequence, head chunk), on a
-    // compute unit that has not executed it before.
+    // time.  Per chunk, one wave per head takes the chunk's maximum and each split's weight
+    // 2^(m_s - M) once (a lane per split), and folds the normaliser; then every thread folds
+    // its (head, d) pairs with those weights.  Compact loops: this code runs once per
+    // (sequence, head chunk), on a compute unit that has not executed it before.
     float* lds_po = reinterpret_cast<float*>(rings);          // [GC][CS][D]
-    float* lds_pm = lds_po + GC * CS * D;                      // [GC][CS]
+    float* lds_pm = lds_po + GC * CS * D;                      // [GC][CS]: m, then the weights
     float* lds_pl = lds_pm + GC * CS;                          // [GC][CS]
+    __shared__ float lds_f[GC];                                // rescale of the running sums
+    __shared__ float lds_L[GC];                                // final normalisers
+    constexpr int NWV = NT / 64;
+    constexpr int GPW = (GC + NWV - 1) / NWV;                  // heads per wave
     constexpr int PER = (GC * D + NT - 1) / NT;                // (head, d) pairs per thread
-    float M[PER], Lsum[PER], acc[PER];
+    float Mh[GPW], Lh[GPW];                                    // wave-uniform, head w + NWV j
 #pragma unroll
-    for (int r = 0; r < PER; ++r) {
-        M[r] = -INFINITY;
-        Lsum[r] = 0.f;
-        acc[r] = 0.f;
+    for (int j = 0; j < GPW; ++j) {
+        Mh[j] = -INFINITY;
+        Lh[j] = 0.f;
     }
+    float acc[PER];
+#pragma unroll
+    for (int r = 0; r < PER; ++r) acc[r] = 0.f;
     for (int s0 = 0; s0 < n_live; s0 += CS) {
         const int cs = min(CS, n_live - s0);
         // outputs: head g's cs * D floats are contiguous in the workspace and in LDS
@@ -755,30 +762,47 @@ __device__ __forceinline__ void merge_splits(const DecodeParams& a, char* rings,
         __syncthreads();
         // LDS now holds outputs at [g][s][d] with stride cs * D per head, and m, l at [g][s]
 #pragma unroll
+        for (int j = 0; j < GPW; ++j) {
+            const int g = w + NWV * j;
+            if (g < GC) {
+                float mx = -INFINITY;
+                for (int s = lane; s < cs; s += 64) mx = fmaxf(mx, lds_pm[g * cs + s]);
+                const float mc = fmaxf(Mh[j], rows_max(group_max16(mx)));
+                float ls = 0.f;
+                for (int s = lane; s < cs; s += 64) {
+                    const float ms = lds_pm[g * cs + s];
+                    const float wgt = (ms == -INFINITY) ? 0.f : fast_exp2(ms - mc);
+                    ls = __builtin_fmaf(wgt, lds_pl[g * cs + s], ls);
+                    lds_pm[g * cs + s] = wgt;
+                }
+                const float f = (Mh[j] == -INFINITY) ? 0.f : fast_exp2(Mh[j] - mc);
+                Lh[j] = __builtin_fmaf(Lh[j], f, rows_sum(group_sum<16>(ls)));
+                Mh[j] = mc;
+                if (lane == 0) {
+                    lds_f[g] = f;
+                    lds_L[g] = Lh[j];
+                }
+            }
+        }
+        __syncthreads();
+#pragma unroll
         for (int r = 0; r < PER; ++r) {
             const int i = min(threadIdx.x + r * NT, GC * D - 1);
             const int g = i / D, d = i % D;
-            float mc = M[r];
-            for (int s = 0; s < cs; ++s) mc = fmaxf(mc, lds_pm[g * cs + s]);
-            const float f = (M[r] == -INFINITY) ? 0.f : fast_exp2(M[r] - mc);
-            float o = acc[r] * f, l = Lsum[r] * f;
+            float o = acc[r] * lds_f[g];
 #pragma unroll 4
-            for (int s = 0; s < cs; ++s) {
-                const float ms = lds_pm[g * cs + s];
-                const float wgt = (ms == -INFINITY) ? 0.f : fast_exp2(ms - mc);
-                o = __builtin_fmaf(wgt, lds_po[(g * cs + s) * D + d], o);
-                l = __builtin_fmaf(wgt, lds_pl[g * cs + s], l);
-            }
-            M[r] = mc;
+            for (int s = 0; s < cs; ++s) o = __builtin_fmaf(lds_pm[g * cs + s], lds_po[(g * cs + s) * D + d], o);
             acc[r] = o;
-            Lsum[r] = l;
         }
         __syncthreads();
     }
 #pragma unroll
     for (int r = 0; r < PER; ++r) {
         const int i = threadIdx.x + r * NT;
-        if (i < GC * D) a.o[(part_base + i / D) * D + (i % D)] = Lsum[r] != 0.f ? acc[r] / Lsum[r] : 0.f;
+        if (i < GC * D) {
+            const float L = lds_L[i / D];
+            a.o[(part_base + i / D) * D + (i % D)] = L != 0.f ? acc[r] / L : 0.f;
+        }
     }
 }
 
