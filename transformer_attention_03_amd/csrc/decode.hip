@@ -665,20 +665,23 @@ __device__ __forceinline__ void split_partial(const DecodeParams& a, const TierS
     __syncthreads();
 
     // ---- merge the waves; finish or publish the split partial ---------------------------
+    // A wave's 64 (head, d) pairs share one head (D is a multiple of 64): lane ww < NW takes
+    // the weight 2^(m_ww - M) of wave ww's partial once, and the fold reads the weights
+    // from those lanes.
+    static_assert(D % 64 == 0 && NW <= 16, "one head per wave in the wave merge");
     const size_t part_base = (size_t)b * a.H + h0;   // + g, then * n_split_max
     for (int i = threadIdx.x; i < GC * D; i += NT) {
-        const int g = i / D, d = i % D;
-        float M = -INFINITY;
+        const int g = __builtin_amdgcn_readfirstlane(i / D), d = i % D;
+        const float mw = lane < NW ? lds_m[lane][g] : -INFINITY;
+        const float Mx = group_max<NW>(mw);
+        const float f = (mw == -INFINITY) ? 0.f : fast_exp2(mw - Mx);
+        const float lsx = group_sum<NW>(lane < NW ? f * lds_l[lane][g] : 0.f);
+        float os = 0.f;
 #pragma unroll
-        for (int ww = 0; ww < NW; ++ww) M = fmaxf(M, lds_m[ww][g]);
-        float os = 0.f, ls = 0.f;
-#pragma unroll
-        for (int ww = 0; ww < NW; ++ww) {
-            const float mw = lds_m[ww][g];
-            const float f = (mw == -INFINITY) ? 0.f : fast_exp2(mw - M);
-            os += f * lds_o[ww][g][d];
-            ls += f * lds_l[ww][g];
-        }
+        for (int ww = 0; ww < NW; ++ww)
+            os = __builtin_fmaf(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(f), ww)), lds_o[ww][g][d], os);
+        const float M = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(Mx), 0));
+        const float ls = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lsx), 0));
         if (n_live == 1) {
             a.o[(part_base + g) * D + d] = ls != 0.f ? os / ls : 0.f;
         } else {

@@ -72,6 +72,16 @@ __device__ __forceinline__ float group_sum(float x) {
     return x;
 }
 
+// Max over aligned groups of N lanes (N in 1,2,4,8,16); every lane gets the max.
+template <int N>
+__device__ __forceinline__ float group_max(float x) {
+    if constexpr (N >= 2) x = fmaxf(x, dpp_f<kDppXor1>(x));
+    if constexpr (N >= 4) x = fmaxf(x, dpp_f<kDppXor2>(x));
+    if constexpr (N >= 8) x = fmaxf(x, dpp_f<kDppHalfMirror>(x));
+    if constexpr (N >= 16) x = fmaxf(x, dpp_f<kDppMirror>(x));
+    return x;
+}
+
 // Max over aligned groups of 16 lanes (one DPP row); every lane gets the max.
 __device__ __forceinline__ float group_max16(float x) {
     x = fmaxf(x, dpp_f<kDppXor1>(x));
