@@ -44,8 +44,10 @@ def test_library_exports_every_declared_symbol():
 def test_library_links_no_torch():
     r = subprocess.run(["ldd", ta.LIB_PATH], capture_output=True, text=True, timeout=60)
     assert r.returncode == 0, r.stderr
-    assert "torch" not in r.stdout and "c10" not in r.stdout
-    assert "amdhip64" in r.stdout, r.stdout + r.stderr
+    # library names only: the hexadecimal load addresses can hold any digit string
+    names = [ln.split()[0] for ln in r.stdout.splitlines() if ln.strip()]
+    assert not any("torch" in n or "c10" in n for n in names), names
+    assert any("amdhip64" in n for n in names), r.stdout + r.stderr
 
 
 def prefill(**kw):

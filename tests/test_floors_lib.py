@@ -24,7 +24,9 @@ def test_exports_and_links_no_torch(L):
               "floor_lds_read64"):
         assert hasattr(L, n), n
     out = os.popen("ldd %s" % PATH).read()
-    assert "torch" not in out and "c10" not in out
+    # library names only: the hexadecimal load addresses can hold any digit string
+    names = [ln.split()[0] for ln in out.splitlines() if ln.strip()]
+    assert names and not any("torch" in n or "c10" in n for n in names), names
 
 
 @pytest.mark.parametrize("args", [
