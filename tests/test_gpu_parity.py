@@ -295,6 +295,24 @@ def test_paged_q8_relative_accuracy(dev, lens, H, Hkv, D, vf):
     assert maxabs(got, want) < 5e-5 * np.abs(want).max()
 
 
+@pytest.mark.parametrize("D", [64, 128, 256])
+@pytest.mark.parametrize("group", [1, 2, 4, 8])
+def test_decode_merge_in_passes(dev, D, group):
+    """16-token splits over 4096 tokens: 256 partials per (sequence, head chunk).  The last
+    workgroup folds them through LDS a number of splits at a time that shrinks with the
+    heads per workgroup and head_dim (down to 15 at 8 heads of 256), so most of these
+    cases take several passes, each with its own maximum and rescale."""
+    say("decode merge in passes D=%d group=%d" % (D, group))
+    Hkv = 2
+    q, k, v = synth.decode_inputs(synth.seed_of(2) + 500 + D + group, Hkv * group, Hkv, D, 4096)
+    try:
+        ta.attn_set_decode_split(16)
+        got, _ = run_decode(dev, q, k, v)
+    finally:
+        ta.attn_set_decode_split(0)
+    assert maxabs(got, decode_oracle(q, k, v)) < TOL_F16
+
+
 def test_paged_q8_error_does_not_grow_with_split_length(dev):
     """int8 V enters the products with a bias of 1.125 per weight, which leaves the
     accumulators block by block: a 4096-token split (32 blocks per wave) keeps the accuracy
