@@ -744,22 +744,24 @@ __device__ __forceinline__ void merge_splits(const DecodeParams& a, char* rings,
     for (int r = 0; r < PER; ++r) acc[r] = 0.f;
     for (int s0 = 0; s0 < n_live; s0 += CS) {
         const int cs = min(CS, n_live - s0);
-        // outputs: head g's cs * D floats are contiguous in the workspace and in LDS
-        const int n16 = GC * cs * D / 4;                       // 16-byte pieces
-        for (int c0 = w * 64; c0 < n16; c0 += NT) {
-            const int c = c0 + lane;
-            const int g = c / (cs * D / 4), off = c % (cs * D / 4);
-            if (c < n16)
-                dma16_coherent(a.part_o + ((part_base + g) * a.n_split_max + s0) * D + 4 * off,
-                               lds_po + 4 * c0);
+        // outputs: head g's cs * D floats are contiguous in the workspace and in LDS (a loop
+        // per head keeps run-time divisions out of the addresses)
+        const int npg = cs * (D / 4);                          // 16-byte pieces per head
+#pragma unroll
+        for (int g = 0; g < GC; ++g) {
+            const float* src = a.part_o + ((part_base + g) * a.n_split_max + s0) * D;
+            float* dst = lds_po + g * cs * D;
+            for (int c0 = w * 64; c0 < npg; c0 += NT)
+                if (c0 + lane < npg) dma16_coherent(src + 4 * (c0 + lane), dst + 4 * c0);
         }
-        for (int c0 = w * 64; c0 < GC * cs; c0 += NT) {
-            const int c = c0 + lane;
-            const int g = c / cs, s = c % cs;
-            if (c < GC * cs) {
-                dma4_coherent(a.part_m + (part_base + g) * a.n_split_max + s0 + s, lds_pm + c0);
-                dma4_coherent(a.part_l + (part_base + g) * a.n_split_max + s0 + s, lds_pl + c0);
-            }
+        // m and l: a wave per head, a lane per split
+        for (int g = w; g < GC; g += NWV) {
+            const size_t row = (part_base + g) * a.n_split_max + s0;
+            for (int c0 = 0; c0 < cs; c0 += 64)
+                if (c0 + lane < cs) {
+                    dma4_coherent(a.part_m + row + c0 + lane, lds_pm + g * cs + c0);
+                    dma4_coherent(a.part_l + row + c0 + lane, lds_pl + g * cs + c0);
+                }
         }
         wait_vmem_at_most<0>();
         __syncthreads();
