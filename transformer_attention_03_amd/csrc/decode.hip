@@ -830,10 +830,10 @@ __global__ void __launch_bounds__((DecShape<D, PAGED>::NT)) decode_split_kernel(
 
     const int lane = threadIdx.x & 63;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int G = a.H / a.Hkv;
-    const int nch = G / GC;
-    const int kvh = blockIdx.y / nch;
-    const int h0 = kvh * G + (blockIdx.y % nch) * GC;
+    const int G = a.group;
+    const int nch = a.nch;
+    const int kvh = nch == 1 ? (int)blockIdx.y : (int)blockIdx.y / nch;   // no division for one chunk
+    const int h0 = kvh * G + ((int)blockIdx.y - kvh * nch) * GC;
 
     // ---- key range of this sequence, and of this split --------------------------------
     int b, split, n_live, t_begin, t_end, L;
@@ -910,8 +910,7 @@ __global__ void __launch_bounds__((DecShape<D, PAGED>::NT)) decode_split_kernel(
         b = blockIdx.z;
         L = a.kv_len;
         const int k_lo = (a.window > 0 && L > a.window) ? L - a.window : 0;
-        n_live = (L - k_lo + a.split_tokens - 1) / a.split_tokens;
-        if (split >= n_live) return;
+        n_live = gridDim.x;                       // the host's split count for this length
         t_begin = k_lo + split * a.split_tokens;
         t_end = min(L, t_begin + a.split_tokens);
     }
@@ -960,10 +959,10 @@ __global__ void __launch_bounds__((DecShape<D, true>::NT)) decode_tiered_kernel(
     static_assert(sizeof(float) * SP::NW * GC * (D + kMergePad) <= RB, "merge buffer fits in the rings");
     constexpr int CS = (RB / 4) / (GC * (D + 2)) > kMaxSplits ? kMaxSplits : (RB / 4) / (GC * (D + 2));
 
-    const int G = a.H / a.Hkv;
-    const int nch = G / GC;
-    const int kvh = blockIdx.y / nch;
-    const int h0 = kvh * G + (blockIdx.y % nch) * GC;
+    const int G = a.group;
+    const int nch = a.nch;
+    const int kvh = nch == 1 ? (int)blockIdx.y : (int)blockIdx.y / nch;   // no division for one chunk
+    const int h0 = kvh * G + ((int)blockIdx.y - kvh * nch) * GC;
     const int n_live = gridDim.x;
     const int split = blockIdx.x;
     if (split < a.tier_cold_splits) {

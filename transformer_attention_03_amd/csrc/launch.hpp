@@ -24,6 +24,7 @@ struct DecodeParams {
     float* part_l;             // [B][H][n_split_max]
     uint32_t* tickets;         // [B][Hkv * head_chunks], zero between calls
     int H, Hkv;
+    int group, nch;            // query heads per KV head; head chunks (workgroups) per KV head
     int kv_len;                // contiguous cache length (unused when paged); ring: tokens so far
     int ring;                  // ring cache capacity in tokens (token t at row t mod ring); 0 = none
     int num_pages, max_pages;
