@@ -241,6 +241,7 @@ int run_decode_contiguous(const float* q, const void* k, const void* v, float* o
     d.tickets = reinterpret_cast<uint32_t*>(ws + wl.t_off);
     d.H = num_heads; d.Hkv = num_kv_heads; d.kv_len = kv_len; d.ring = ring;
     d.group = num_heads / num_kv_heads; d.nch = plan.nch;
+    d.nch_inv = ((1ull << 32) + plan.nch - 1) / plan.nch;
     d.num_pages = 0; d.max_pages = 0;
     fill_scalars(d, window, attn_softcap, scale);
     d.split_tokens = plan.split_tokens;
@@ -480,6 +481,7 @@ int attn_decode_paged_q8(const float* q, const int8_t* k_pages, const int8_t* v_
     d.tickets = reinterpret_cast<uint32_t*>(ws + wl.t_off);
     d.H = num_heads; d.Hkv = num_kv_heads; d.kv_len = 0;
     d.group = num_heads / num_kv_heads; d.nch = plan.nch;
+    d.nch_inv = ((1ull << 32) + plan.nch - 1) / plan.nch;
     d.num_pages = num_pages; d.max_pages = max_pages_per_seq;
     fill_scalars(d, sliding_window, attn_softcap, scale);
     d.split_tokens = plan.split_tokens;
@@ -620,6 +622,7 @@ int run_tiered(const char* what, const float* q, const void* hot_k, const void* 
     d.tickets = reinterpret_cast<uint32_t*>(ws + wl.t_off);
     d.H = num_heads; d.Hkv = num_kv_heads;
     d.group = num_heads / num_kv_heads; d.nch = plan.nch;
+    d.nch_inv = ((1ull << 32) + plan.nch - 1) / plan.nch;
     d.kv_len = total;
     d.ring = hot_len > 0 ? hot_window : 1;
     d.num_pages = ct.paged ? ct.num_pages : 0;

@@ -832,7 +832,7 @@ __global__ void __launch_bounds__((DecShape<D, PAGED>::NT)) decode_split_kernel(
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int G = a.group;
     const int nch = a.nch;
-    const int kvh = nch == 1 ? (int)blockIdx.y : (int)blockIdx.y / nch;   // no division for one chunk
+    const int kvh = (int)(((unsigned long long)blockIdx.y * a.nch_inv) >> 32);   // blockIdx.y / nch
     const int h0 = kvh * G + ((int)blockIdx.y - kvh * nch) * GC;
 
     // ---- key range of this sequence, and of this split --------------------------------
@@ -961,7 +961,7 @@ __global__ void __launch_bounds__((DecShape<D, true>::NT)) decode_tiered_kernel(
 
     const int G = a.group;
     const int nch = a.nch;
-    const int kvh = nch == 1 ? (int)blockIdx.y : (int)blockIdx.y / nch;   // no division for one chunk
+    const int kvh = (int)(((unsigned long long)blockIdx.y * a.nch_inv) >> 32);   // blockIdx.y / nch
     const int h0 = kvh * G + ((int)blockIdx.y - kvh * nch) * GC;
     const int n_live = gridDim.x;
     const int split = blockIdx.x;

@@ -25,6 +25,7 @@ struct DecodeParams {
     uint32_t* tickets;         // [B][Hkv * head_chunks], zero between calls
     int H, Hkv;
     int group, nch;            // query heads per KV head; head chunks (workgroups) per KV head
+    unsigned long long nch_inv; // ceil(2^32 / nch): y / nch = (y * nch_inv) >> 32 for y < 2^16
     int kv_len;                // contiguous cache length (unused when paged); ring: tokens so far
     int ring;                  // ring cache capacity in tokens (token t at row t mod ring); 0 = none
     int num_pages, max_pages;
