@@ -729,7 +729,7 @@ __device__ __forceinline__ void merge_splits(const DecodeParams& a, char* rings,
     float* lds_pm = lds_po + GC * CS * D;                      // [GC][CS]: m, then the weights
     float* lds_pl = lds_pm + GC * CS;                          // [GC][CS]
     __shared__ float lds_f[GC];                                // rescale of the running sums
-    __shared__ float lds_L[GC];                                // final normalisers
+    __shared__ float lds_L[GC];                                // 1 / final normaliser (0 if none)
     constexpr int NWV = NT / 64;
     constexpr int GPW = (GC + NWV - 1) / NWV;                  // heads per wave
     constexpr int PER = (GC * D + NT - 1) / NT;                // (head, d) pairs per thread
@@ -785,7 +785,7 @@ __device__ __forceinline__ void merge_splits(const DecodeParams& a, char* rings,
                 Mh[j] = mc;
                 if (lane == 0) {
                     lds_f[g] = f;
-                    lds_L[g] = Lh[j];
+                    lds_L[g] = Lh[j] != 0.f ? 1.f / Lh[j] : 0.f;
                 }
             }
         }
@@ -799,15 +799,12 @@ __device__ __forceinline__ void merge_splits(const DecodeParams& a, char* rings,
             for (int s = 0; s < cs; ++s) o = __builtin_fmaf(lds_pm[g * cs + s], lds_po[(g * cs + s) * D + d], o);
             acc[r] = o;
         }
-        __syncthreads();
+        if (s0 + CS < n_live) __syncthreads();                 // the next chunk reuses the buffers
     }
 #pragma unroll
     for (int r = 0; r < PER; ++r) {
         const int i = threadIdx.x + r * NT;
-        if (i < GC * D) {
-            const float L = lds_L[i / D];
-            a.o[(part_base + i / D) * D + (i % D)] = L != 0.f ? acc[r] / L : 0.f;
-        }
+        if (i < GC * D) a.o[(part_base + i / D) * D + (i % D)] = acc[r] * lds_L[i / D];
     }
 }
 
